@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent-KV attention hot path on one MI355X.
+
+One step = one chunk of one layer in the streaming rollout at the Wan2.1-1.3B
+geometry (VideoMLA paper, section 4.1 and appendix D.1): `steps_per_chunk`
+frozen-cache vmla_attend calls (the 4-step student sampler, appendix D.5)
+followed by one vmla_compress_append that writes the chunk into the
+21-frame ring and evicts the oldest frames.  The window is full (32,760 cached
+keys + 4,680 chunk keys) for every timed step.  Inputs are seeded synthetic
+tensors already resident in HBM; weights are random N(0,1)/sqrt(fan_in).
+
+Prints one JSON line.  `value` = query tokens attended per second.
+`roofline` describes the dominant kernel (latent attention) timed live with
+HIP events recorded by the library around it; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (for fp32 workloads)
+PEAK_HBM_GBS = 8000.0
+METRIC = "query tokens/s and MFMA TFLOP/s (% peak) per layer, Wan-1.3B latent attn"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "latent_attn_wan_layer_pmc.json")
+ATTN_SOURCE = os.path.join(ROOT, "mla_latent_kv_vmla_amd", "csrc", "attention.hip")
+
+
+def attention_flops(g, n_frames: int) -> float:
+    """Algorithmic FLOPs of one latent-attention launch: per (query row, key)
+    2*(d_c+d_r) for the score and 2*d_c for the value sum."""
+    rows = g.batch * g.n_q * g.n_heads
+    return rows * g.n_k(n_frames) * (2.0 * (g.d_c + g.d_rope) + 2.0 * g.d_c)
+
+
+def attend_call_flops(g, n_frames: int) -> float:
+    """All algorithmic FLOPs of one vmla_attend call (projections + attention)."""
+    M = g.batch * g.n_q
+    d, nh = g.hidden, g.n_heads
+    gemm = 2.0 * M * (d * (g.d_c + g.d_rope) + d * g.d_q + g.d_q * nh * g.head_dim
+                      + nh * g.d_nope * g.d_c + nh * g.d_c * g.d_v + nh * g.d_v * d)
+    return gemm + attention_flops(g, n_frames)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime first)
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        t = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return t.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def traffic_from_counters():
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        s = json.load(open(PMC_SUMMARY))
+        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        if s.get("attention_source_sha256") == sha:
+            return s.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(g, w, hist, n, x, sample_tokens: int):
+    """The oracle as it stands (float64 numpy) on a contiguous sample of query
+    tokens of the same call; returns query tokens/s of the sample."""
+    import numpy as np
+    from oracle import mla
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    q = np.arange(sample_tokens)
+    t0 = time.perf_counter()
+    mla.attend(g, w, hist, n, x, query_tokens=q)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "query tokens/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": (f"{sample_tokens} of {g.n_q} query tokens (all {g.n_heads} heads) of one attend call "
+                       f"against the full {g.n_k(n)} keys, float64 numpy; {dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan1.3b-layer")
+    ap.add_argument("--steps-per-chunk", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1560)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after timing, run plain device copies of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the latent-attention path on a single MI355X "
+              "(see the sharding paragraph of the design notes); --gpus above 1 is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mla_latent_kv_vmla_amd import vmla, workloads as wl
+
+    g = wl.GEOMETRIES[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = vmla.torch_dtype(g)
+    w = wl.latent_weights(g, mode="literal")
+    layer = vmla.LatentAttention(g, {k: torch.from_numpy(v) for k, v in w.as_dict().items()})
+    hist = {}
+    for k in range(g.prefill_chunks):
+        xk = wl.hidden_states(g, chunk=k)
+        layer.append(torch.from_numpy(xk).to(dev, dt))
+        for i in range(g.chunk_frames):
+            hist[k * g.chunk_frames + i] = xk[0].reshape(g.chunk_frames, g.tokens_per_frame, g.hidden)[i]
+    n_prefill = layer.state()[0]
+    xs_np = [wl.hidden_states(g, chunk=g.prefill_chunks, step=s) for s in range(args.steps_per_chunk)]
+    xs = [torch.from_numpy(a).to(dev, dt) for a in xs_np]
+    out = torch.empty_like(xs[0])
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    ev = HipEvents()
+    n_att = (args.warmup + args.steps) * args.steps_per_chunk
+    ev_pairs = [(ev.create(), ev.create()) for _ in range(n_att)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.warmup + args.steps)]
+
+    def step(i):
+        for s in range(args.steps_per_chunk):
+            a, b = ev_pairs[i * args.steps_per_chunk + s]
+            vmla.vmla_attend_profiled(layer.ctx, xs[s], out, a, b, sh)
+        vmla.vmla_compress_append(layer.ctx, xs[-1], sh)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    region0.record(stream)
+    for i in range(args.warmup, args.warmup + args.steps):
+        step_ev[i][0].record(stream)
+        step(i)
+        step_ev[i][1].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_region = region0.elapsed_time(region1)
+    ms_per_step = ms_region / args.steps
+
+    attn_ms = [ev.elapsed_ms(a, b) for a, b in ev_pairs[args.warmup * args.steps_per_chunk:]]
+    attn_avg = float(np.mean(attn_ms))
+    n_frames = min(layer.state()[0], g.window_frames)  # window full for every timed step
+    flops_attn = attention_flops(g, n_frames)
+    achieved = flops_attn / (attn_avg * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if g.dtype == wl.F32 else PEAK_BF16_TFLOPS
+    tokens_per_step = g.batch * g.n_q * args.steps_per_chunk
+    value = tokens_per_step / (ms_per_step * 1e-3)
+    call_flops = attend_call_flops(g, n_frames)
+
+    if args.calibrate_copy_mb > 0:
+        nbytes = args.calibrate_copy_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if g.dtype == wl.F32 else "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(fan_in) weights and hidden states)",
+        "config": {"workload": g.name, "batch": g.batch, "query_tokens_per_call": g.n_q,
+                   "keys_per_call": g.n_k(n_frames), "heads": g.n_heads, "d_c": g.d_c, "d_rope": g.d_rope,
+                   "window_frames": g.window_frames, "chunk_frames": g.chunk_frames,
+                   "attends_per_step": args.steps_per_chunk, "appends_per_step": 1},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic_from_counters(),
+                     "kernel": "latent_attn_kernel (+ split combine)",
+                     "flops_per_launch": flops_attn, "avg_launch_ms": attn_avg},
+        "attend_call_tflops": call_flops * args.steps_per_chunk / (ms_per_step * 1e-3) / 1e12,
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(g, w, hist, n_prefill, xs_np[0][0], args.cpu_sample_tokens)
+    for a, b in ev_pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    layer.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

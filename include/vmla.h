@@ -1,0 +1,173 @@
+/*
+ * vmla.h -- C ABI of libvmla.so: latent-KV chunk attention for streaming video
+ * diffusion on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is the self-attention layer of VideoMLA ("VideoMLA:
+ * Low-Rank Latent KV Cache for Minute-Scale Autoregressive Video Diffusion",
+ * sections 3.1-3.3 and appendices C.1, D.1, D.4): every cached token keeps one
+ * head-shared content latent c (d_c scalars) and one head-shared decoupled
+ * 3D-RoPE key k_r (d_rope scalars) in a sliding window of latent frames, and a
+ * chunk of query frames attends to that window plus itself.  Queries are
+ * absorbed into latent space through W_UK and outputs are lifted through W_UV
+ * (the Multi-Head Latent Attention rearrangement the paper builds on), so the
+ * per-head keys and values are never materialised.
+ *
+ * Conventions shared by every entry point
+ *   - All device memory (weights, cache, workspace, x, out) is owned by the
+ *     caller.  The library borrows the pointers; it never allocates, frees or
+ *     copies device memory on the host's behalf.  Weights, cache and workspace
+ *     must stay valid, unmoved and (for weights) unchanged for the life of a ctx.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Element type of all tensors is the config's dtype (bf16 or f32), row-major.
+ *     Weights use the torch.nn.Linear layout [out_features, in_features].
+ *   - Calls enqueue work on the given HIP stream and return without waiting.
+ *     All argument checks happen before anything is enqueued; on a non-zero
+ *     status nothing was enqueued and the ctx is unchanged.  Launch failures are
+ *     reported as VMLA_ERR_HIP (from hipGetLastError after the launch).
+ *   - A ctx is not thread-safe; all calls on one ctx must be issued in one stream
+ *     order.  No exception crosses the ABI.
+ */
+#ifndef VMLA_H
+#define VMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VMLA_API __attribute__((visibility("default")))
+
+/* status codes */
+enum {
+  VMLA_OK = 0,
+  VMLA_ERR_NULL = 1,        /* a required pointer argument is NULL */
+  VMLA_ERR_CONFIG = 2,      /* config fields out of range or inconsistent */
+  VMLA_ERR_UNSUPPORTED = 3, /* valid config, but no kernel built for (dtype, d_c, d_rope) */
+  VMLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  VMLA_ERR_STATE = 5,       /* call not valid in the ctx's current state */
+  VMLA_ERR_ARG = 6,         /* another argument out of range */
+  VMLA_ERR_HIP = 7          /* the HIP runtime reported an error for a launch */
+};
+
+enum { VMLA_DTYPE_BF16 = 0, VMLA_DTYPE_F32 = 1 };
+
+/*
+ * Layer geometry.  Names follow the paper's notation (section 3; section 4.1
+ * gives the Wan-1.3B values: hidden 1536, 12 heads, d_nope 96 + d_rope 32,
+ * d_c 192, d_q 768; appendix D.1: 30x52 grid, 3-frame chunks, 21-frame window).
+ *   head dim d_h = d_nope + d_rope; softmax scale 1/sqrt(d_h).
+ *   rope_pairs_t/h/w: complex pairs of the decoupled key per axis, in the
+ *     order t, h, w; 2*(t+h+w) must equal d_rope (section 3.2, 4.1).
+ *   tokens per frame T = grid_h*grid_w; token s sits at row s/grid_w,
+ *     column s%grid_w.  Chunk = chunk_frames frames = C*T query tokens.
+ *   batch: independent streams advanced in lockstep (one frame counter).
+ *   attn_workgroups: persistent attention workgroups (0 = 256, one per MI355X
+ *     compute unit); it sizes part of the workspace.
+ * Constraints (else VMLA_ERR_CONFIG): all sizes > 0;
+ *   1 <= chunk_frames <= window_frames; d_nope, d_rope, d_c, d_v, d_q and hidden
+ *   multiples of 8; rope_theta > 0.
+ * Built kernels (else VMLA_ERR_UNSUPPORTED): (dtype, d_c, d_rope) in
+ *   {(f32, 24, 8), (bf16, 24, 8), (bf16, 96, 32), (bf16, 192, 32), (bf16, 448, 32)}.
+ */
+typedef struct vmla_config {
+  int32_t batch;
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t d_nope;
+  int32_t d_rope;
+  int32_t d_v;
+  int32_t d_c;
+  int32_t d_q;
+  int32_t rope_pairs_t, rope_pairs_h, rope_pairs_w;
+  float rope_theta;
+  int32_t grid_h, grid_w;
+  int32_t window_frames;
+  int32_t chunk_frames;
+  int32_t dtype;
+  int32_t attn_workgroups;
+} vmla_config;
+
+/*
+ * Device pointers to one layer's weights (Linear layout, config dtype).
+ *   w_dkv [d_c, hidden]       content latent c = W_DKV x          (section 3.1)
+ *   w_kr  [d_rope, hidden]    decoupled key k^ = W_KR x, rotated by 3D-RoPE (3.2)
+ *   w_dq  [d_q, hidden]       query latent c^Q = W_DQ x            (section 4.1)
+ *   w_uq  [n_heads*(d_nope+d_rope), d_q]  per head [q_nope ; q_rope]
+ *   w_uk  [n_heads, d_nope, d_c]  per-head content-key lift k_nope = W_UK^h c (3.3)
+ *   w_uv  [n_heads, d_v, d_c]     per-head value lift v = W_UV^h c           (3.3)
+ *   w_o   [hidden, n_heads*d_v]   output projection
+ */
+typedef struct vmla_weights {
+  const void *w_dkv, *w_kr, *w_dq, *w_uq, *w_uk, *w_uv, *w_o;
+} vmla_weights;
+
+typedef struct vmla_ctx vmla_ctx; /* opaque; holds host-side metadata only */
+
+/* Bytes of the ring cache: batch * window_frames * T * (d_c + d_rope) elements.
+ * Row (slot*T + s) of stream b holds [c (d_c) | k_r rotated (d_rope)] of token s
+ * of the frame in that slot; frame f lives in slot f % window_frames.
+ * Returns 0 for an invalid config. */
+VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg);
+
+/* Bytes of scratch device memory a ctx needs (chunk latents, absorbed queries,
+ * latent outputs, partial softmax states).  Returns 0 for an invalid config. */
+VMLA_API size_t vmla_workspace_bytes(const vmla_config* cfg);
+
+/* Create a ctx over caller-owned memory.  cache: vmla_cache_bytes(cfg) bytes;
+ * its contents are not read until frames are appended (unused slots may hold
+ * anything).  workspace: vmla_workspace_bytes(cfg) bytes.  rope_freqs: host
+ * array of d_rope/2 floats giving omega per complex pair (axis order t, h, w),
+ * copied at create; NULL selects theta^(-2i/(2p_a)), i = 0..p_a-1, per axis.
+ * Makes no HIP call.  On success *out is a new ctx with 0 frames appended. */
+VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* cache,
+                         void* workspace, const float* rope_freqs, vmla_ctx** out);
+
+/* Append one chunk: x is [batch, chunk_frames*T, hidden].  Computes
+ * [c | RoPE(k^)] for frames n..n+C-1 (n = frames appended so far; the temporal
+ * coordinate is the absolute frame index) and writes them into ring slots
+ * (n+i) % window_frames, evicting the frames that held them (oldest first,
+ * appendix D.4).  Then n += C on the host. */
+VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stream);
+
+/* Attend one chunk: x is [batch, C*T, hidden], out is [batch, C*T, hidden].
+ * Every query token of frames n..n+C-1 attends, in every head, to all cached
+ * frames [max(0, n-W), n) and all tokens of the chunk itself (chunk-causal,
+ * appendix D.4), followed by W_UV and W_O.  Leaves the cache and n unchanged:
+ * the frozen-cache denoising steps of a rollout call this repeatedly, then
+ * append the final step's x. */
+VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream);
+
+/* Same as vmla_attend, and additionally records attn_start on the stream right
+ * before the latent-attention kernels and attn_stop right after them, so a caller
+ * can time the dominant kernels of the call with hipEventElapsedTime.  Both
+ * events must be created by the caller (hipEventCreate); NULL -> VMLA_ERR_NULL. */
+VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEvent_t attn_start,
+                                  hipEvent_t attn_stop, hipStream_t stream);
+
+/* Test hook: compute the cache rows [c | RoPE(k^)] of x ([batch, C*T, hidden])
+ * as frames frame0..frame0+C-1 into latents_out ([batch, C*T, d_c+d_rope]),
+ * without touching the cache or n.  frame0 >= 0 else VMLA_ERR_ARG. */
+VMLA_API int vmla_compress(vmla_ctx* ctx, const void* x, int64_t frame0, void* latents_out,
+                           hipStream_t stream);
+
+/* Host metadata: frames appended n, first valid frame max(0, n-W), and the
+ * number of valid frames min(n, W).  Any output pointer may be NULL. */
+VMLA_API int vmla_cache_state(const vmla_ctx* ctx, int64_t* frames_appended,
+                              int64_t* first_valid_frame, int32_t* n_valid_frames);
+
+/* Forget all appended frames (n = 0).  Cache bytes are left as they are. */
+VMLA_API int vmla_reset(vmla_ctx* ctx);
+
+/* Free a ctx (host memory only).  NULL is ignored. */
+VMLA_API void vmla_destroy(vmla_ctx* ctx);
+
+/* Static description of a status code. */
+VMLA_API const char* vmla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VMLA_H */

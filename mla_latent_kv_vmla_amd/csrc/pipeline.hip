@@ -1,0 +1,227 @@
+// Launch sequences of the two library calls and the GEMM epilogues they use.
+//
+//   compress (VideoMLA paper, sections 3.1-3.2): one GEMM x . [W_DKV; W_KR]^T whose
+//     epilogue rotates the decoupled key channels by 3D-RoPE, rounds to the
+//     storage type and scatters each token's row to its ring slot
+//     ((frame % W) * T + s) or to a linear buffer.
+//   attend: compress the chunk into staging; c^Q = W_DQ x; q = W_UQ c^Q with the
+//     rotary channels turned and scaled straight into the absorbed query;
+//     absorbed query q~_h = W_UK^h^T q_nope_h (per-head GEMM on MFMA);
+//     latent attention (attention.hip); o_h = W_UV^h o~_h; out = W_O o.
+#include "gemm.h"
+#include "plan.h"
+
+namespace vmla {
+
+static Rope make_rope(const Plan& p) {
+  Rope r;
+  r.pairs_t = p.pairs_t;
+  r.pairs_h = p.pairs_h;
+  r.grid_w = p.grid_w;
+  r.tokens_per_frame = p.Tpf;
+  for (int i = 0; i < kMaxRopePairs; ++i) r.freq[i] = p.freq[i];
+  return r;
+}
+
+// Y[m][n] -> y[z*yz + m*ldy + n]
+template <typename T> struct EpiStore {
+  T* y;
+  long ldy, yz;
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    store4(y + (long)z * yz + (long)m * ldy + n, v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Latent cache rows: features [0, dc) are c, [dc, dc+dr) the decoupled key,
+// rotated with the token's (frame, row, column).  Token m is chunk token
+// m % Nq of stream m / Nq, frame frame0 + t / T.
+template <typename T> struct EpiLatent {
+  T* dst;
+  long bstride;   // elements per stream in dst
+  int64_t frame0;
+  int Nq, W, dc, D;
+  int ring;
+  Rope rope;
+  __device__ void operator()(int, int m, int n, const float* v) const {
+    const int b = m / Nq, t = m % Nq;
+    const int64_t frame = frame0 + t / rope.tokens_per_frame;
+    const int s = t % rope.tokens_per_frame;
+    const long row = ring ? (long)(frame % W) * rope.tokens_per_frame + s : (long)t;
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    if (n >= dc) {
+      const int pair = (n - dc) >> 1;
+      rope.rotate2(pair, frame, s, a0, a1);
+      rope.rotate2(pair + 1, frame, s, a2, a3);
+    }
+    store4(dst + b * bstride + row * D + n, a0, a1, a2, a3);
+  }
+};
+
+// q = W_UQ c^Q, per head [q_nope (d_nope) ; q_rope (dr)].  q_nope goes to its
+// own buffer; q_rope is rotated, scaled by qscale and written into the rotary
+// part of the absorbed query row.
+template <typename T> struct EpiQuery {
+  T* qnope;  // [M][nh][d_nope]
+  T* qt;     // [M][nh][D]
+  int Nq, nh, d_nope, dh, dc, D;
+  float qscale;
+  Rope rope;
+  __device__ void operator()(int, int m, int n, const float* v) const {
+    const int h = n / dh, j = n % dh;
+    if (j < d_nope) {
+      store4(qnope + ((long)m * nh + h) * d_nope + j, v[0], v[1], v[2], v[3]);
+      return;
+    }
+    const int t = m % Nq;
+    const int64_t frame = frame0 + t / rope.tokens_per_frame;
+    const int s = t % rope.tokens_per_frame;
+    const int pair = (j - d_nope) >> 1;
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    rope.rotate2(pair, frame, s, a0, a1);
+    rope.rotate2(pair + 1, frame, s, a2, a3);
+    store4(qt + ((long)m * nh + h) * D + dc + (j - d_nope), a0 * qscale, a1 * qscale, a2 * qscale,
+           a3 * qscale);
+  }
+  int64_t frame0;
+};
+
+// Absorbed content query: q~[m][h][n] = qscale * (q_nope_h W_UK^h)[n]
+template <typename T> struct EpiAbsorb {
+  T* qt;
+  int nh, D;
+  float qscale;
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    store4(qt + ((long)m * nh + z) * D + n, v[0] * qscale, v[1] * qscale, v[2] * qscale, v[3] * qscale);
+  }
+};
+
+template <typename T, bool W_KN, class Epi>
+static void gemm(const GemmOps<T>& op, int Z, const Epi& epi, hipStream_t s) {
+  // Narrow outputs use 64-feature tiles to waste less of the last tile.
+  if (op.N <= 96 || (op.N % 128 != 0 && op.N % 64 == 0 && op.N < 512)) {
+    dim3 grid((op.N + 63) / 64, (op.M + 127) / 128, Z);
+    gemm_kernel<T, 64, 128, W_KN, Epi><<<grid, 256, 0, s>>>(op, epi);
+  } else {
+    dim3 grid((op.N + 127) / 128, (op.M + 127) / 128, Z);
+    gemm_kernel<T, 128, 128, W_KN, Epi><<<grid, 256, 0, s>>>(op, epi);
+  }
+}
+
+template <typename T>
+static GemmOps<T> ops(const void* w, long ldw, long wz, const void* x, long ldx, long xz, int N, int M, int K) {
+  GemmOps<T> o;
+  o.w = o.w2 = static_cast<const T*>(w);
+  o.ldw = ldw;
+  o.wz = wz;
+  o.x = static_cast<const T*>(x);
+  o.ldx = ldx;
+  o.xz = xz;
+  o.N = N;
+  o.M = M;
+  o.K = K;
+  o.n_split = N;
+  return o;
+}
+
+template <typename T>
+static void compress_t(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring, hipStream_t s) {
+  const int M = p.B * p.Nq;
+  GemmOps<T> op = ops<T>(p.w_dkv, p.d, 0, x, p.d, 0, p.D, M, p.d);
+  op.w2 = static_cast<const T*>(p.w_kr);
+  op.n_split = p.dc;
+  EpiLatent<T> e;
+  e.dst = static_cast<T*>(dst);
+  e.bstride = ring ? (long)p.W * p.Tpf * p.D : (long)p.Nq * p.D;
+  e.frame0 = frame0;
+  e.Nq = p.Nq;
+  e.W = p.W;
+  e.dc = p.dc;
+  e.D = p.D;
+  e.ring = ring ? 1 : 0;
+  e.rope = make_rope(p);
+  gemm<T, false>(op, 1, e, s);
+}
+
+template <typename T>
+static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s, hipEvent_t ev0,
+                           hipEvent_t ev1) {
+  const int M = p.B * p.Nq;
+  compress_t<T>(p, x, n, p.stage, false, s);
+  {  // c^Q = W_DQ x
+    EpiStore<T> e{static_cast<T*>(p.cq), p.dq, 0};
+    gemm<T, false>(ops<T>(p.w_dq, p.d, 0, x, p.d, 0, p.dq, M, p.d), 1, e, s);
+  }
+  {  // q = W_UQ c^Q -> q_nope, rotated/scaled q_rope into the absorbed query
+    EpiQuery<T> e;
+    e.qnope = static_cast<T*>(p.qnope);
+    e.qt = static_cast<T*>(p.qt);
+    e.Nq = p.Nq;
+    e.nh = p.nh;
+    e.d_nope = p.d_nope;
+    e.dh = p.dh;
+    e.dc = p.dc;
+    e.D = p.D;
+    e.qscale = p.qscale;
+    e.rope = make_rope(p);
+    e.frame0 = n;
+    gemm<T, false>(ops<T>(p.w_uq, p.dq, 0, p.cq, p.dq, 0, p.nh * p.dh, M, p.dq), 1, e, s);
+  }
+  if (p.d_nope > 0) {  // q~_h = W_UK^h^T q_nope_h for every head (z = head)
+    EpiAbsorb<T> e{static_cast<T*>(p.qt), p.nh, p.D, p.qscale};
+    gemm<T, true>(ops<T>(p.w_uk, p.dc, (long)p.d_nope * p.dc, p.qnope, (long)p.nh * p.d_nope, p.d_nope,
+                         p.dc, M, p.d_nope),
+                  p.nh, e, s);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  {
+    AttnCall a;
+    a.dtype = p.dtype;
+    a.dc = p.dc;
+    a.dr = p.dr;
+    a.qt = p.qt;
+    a.cache = p.cache;
+    a.stage = p.stage;
+    a.out = p.olat;
+    a.part_o = p.part_o;
+    a.part_ml = p.part_ml;
+    a.cache_bstride = (long)p.W * p.Tpf * p.D;
+    a.stage_bstride = (long)p.Nq * p.D;
+    a.B = p.B;
+    a.R = p.Nq * p.nh;
+    a.n_ring = (int)((n < p.W ? n : p.W) * p.Tpf);
+    a.n_stage = p.Nq;
+    a.G = p.G;
+    if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+    err = run_latent_attention(a, s);
+    if (err != hipSuccess) return err;
+    if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
+  }
+  {  // o_h = W_UV^h o~_h (z = head)
+    EpiStore<T> e{static_cast<T*>(p.o), (long)p.nh * p.dv, p.dv};
+    gemm<T, false>(ops<T>(p.w_uv, p.dc, (long)p.dv * p.dc, p.olat, (long)p.nh * p.dc, p.dc, p.dv, M, p.dc),
+                   p.nh, e, s);
+  }
+  {  // out = W_O o
+    EpiStore<T> e{static_cast<T*>(out), p.d, 0};
+    gemm<T, false>(ops<T>(p.w_o, (long)p.nh * p.dv, 0, p.o, (long)p.nh * p.dv, 0, p.d, M, p.nh * p.dv), 1, e,
+                   s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_compress(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring, hipStream_t s) {
+  if (p.dtype == DType::F32)
+    compress_t<float>(p, x, frame0, dst, ring, s);
+  else
+    compress_t<bf16>(p, x, frame0, dst, ring, s);
+  return hipGetLastError();
+}
+
+hipError_t run_attend(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s, hipEvent_t ev0,
+                      hipEvent_t ev1) {
+  if (p.dtype == DType::F32) return attend_t<float>(p, n, x, out, s, ev0, ev1);
+  return attend_t<bf16>(p, n, x, out, s, ev0, ev1);
+}
+
+}  // namespace vmla

@@ -1,0 +1,73 @@
+// Internal interface between the host runtime (vmla_host.cpp) and the kernel
+// pipelines (pipeline.hip, attention.hip).  Host-only types; no HIP kernels.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vmla {
+
+enum class DType : int { BF16 = 0, F32 = 1 };
+
+// Rows per attention workgroup used to size the partial-state workspace
+// (the largest row block any built attention kernel uses).
+constexpr int kAttnMaxRows = 256;
+constexpr int kMaxRopePairs = 64;
+
+// Everything one layer call needs: geometry, borrowed device pointers and the
+// workspace carve-up.  Filled by the host runtime; read by the pipelines.
+struct Plan {
+  DType dtype;
+  int B, d, nh, d_nope, dr, dv, dc, dq, D, dh;  // D = dc + dr, dh = d_nope + dr
+  int Tpf, grid_w, W, C, Nq;                    // tokens/frame, window and chunk frames
+  int pairs_t, pairs_h, pairs_w;
+  float freq[kMaxRopePairs];
+  float qscale;  // log2(e) / sqrt(dh): softmax scale folded into the absorbed query
+  int G;         // persistent attention workgroups
+  const void *w_dkv, *w_kr, *w_dq, *w_uq, *w_uk, *w_uv, *w_o;
+  void* cache;   // [B][W*Tpf][D]
+  // workspace regions
+  void *stage;   // [B][Nq][D]            chunk latents (rotated)
+  void *cq;      // [B][Nq][dq]           query latent
+  void *qnope;   // [B][Nq][nh][d_nope]   content part of the per-head query
+  void *qt;      // [B][Nq][nh][D]        absorbed query [W_UK^T q_nope | q_rope] * qscale
+  void *olat;    // [B][Nq][nh][dc]       attention output in latent space
+  void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV
+  float *part_o; // [2G][kAttnMaxRows][dc] unnormalised partial outputs
+  float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
+};
+
+struct WorkspaceLayout {
+  size_t stage, cq, qnope, qt, olat, o, part_o, part_ml, total;
+};
+
+WorkspaceLayout workspace_layout(const Plan& p);
+
+// Kernel pipelines.  Each returns hipSuccess or the first launch error.
+// compress: rows [c | RoPE(k^)] of x for frames frame0.. into dst; ring != 0
+// writes row (frame % W)*Tpf + s of each stream's cache, else row t of dst.
+hipError_t run_compress(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring,
+                        hipStream_t s);
+// attend: full chunk attention against the ring holding n frames.
+hipError_t run_attend(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s,
+                      hipEvent_t attn_start = nullptr, hipEvent_t attn_stop = nullptr);
+
+// Latent attention kernels (attention.hip): keys = n_ring cache rows followed by
+// the chunk's staged rows.  Returns hipErrorInvalidValue for an unbuilt shape.
+struct AttnCall {
+  DType dtype;
+  int dc, dr;
+  const void* qt;
+  const void* cache;
+  const void* stage;
+  void* out;
+  float* part_o;
+  float* part_ml;
+  long cache_bstride, stage_bstride;  // elements
+  int B, R, n_ring, n_stage;
+  int G;
+};
+hipError_t run_latent_attention(const AttnCall& a, hipStream_t s);
+bool latent_attention_supported(DType dt, int dc, int dr);
+
+}  // namespace vmla

@@ -1,0 +1,259 @@
+// Host runtime of libvmla.so: config validation, ring-buffer metadata,
+// workspace carve-up and the C ABI declared in include/vmla.h.  Every check
+// runs before anything is enqueued; only run_compress / run_attend touch HIP.
+#include "../../include/vmla.h"
+
+#include <math.h>
+#include <new>
+#include <string.h>
+
+#include "plan.h"
+
+using vmla::DType;
+using vmla::Plan;
+
+struct vmla_ctx {
+  vmla_config cfg;
+  vmla_weights w;
+  void* cache;
+  void* workspace;
+  float freq[vmla::kMaxRopePairs];
+  int64_t n;  // frames appended (lockstep over the batch)
+};
+
+namespace {
+
+constexpr int kDefaultWorkgroups = 256;  // MI355X compute units
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_config(const vmla_config* c) {
+  if (!c) return VMLA_ERR_NULL;
+  if (c->batch <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->d_nope <= 0 || c->d_rope <= 0 ||
+      c->d_v <= 0 || c->d_c <= 0 || c->d_q <= 0 || c->grid_h <= 0 || c->grid_w <= 0 ||
+      c->window_frames <= 0 || c->chunk_frames <= 0 || c->attn_workgroups < 0)
+    return VMLA_ERR_CONFIG;
+  if (c->chunk_frames > c->window_frames) return VMLA_ERR_CONFIG;
+  if (c->rope_pairs_t < 0 || c->rope_pairs_h < 0 || c->rope_pairs_w < 0 ||
+      2 * (c->rope_pairs_t + c->rope_pairs_h + c->rope_pairs_w) != c->d_rope ||
+      c->d_rope / 2 > vmla::kMaxRopePairs)
+    return VMLA_ERR_CONFIG;
+  if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return VMLA_ERR_CONFIG;
+  if (c->d_nope % 8 || c->d_rope % 8 || c->d_c % 8 || c->d_v % 8 || c->d_q % 8 || c->hidden % 8)
+    return VMLA_ERR_CONFIG;
+  if (c->dtype != VMLA_DTYPE_BF16 && c->dtype != VMLA_DTYPE_F32) return VMLA_ERR_CONFIG;
+  // sizes must fit the 32-bit row counters the kernels use
+  const long long T = (long long)c->grid_h * c->grid_w;
+  const long long rows = T * c->window_frames + T * c->chunk_frames;
+  if (rows * c->n_heads > (1LL << 30) || (long long)c->batch * T * c->chunk_frames > (1LL << 30))
+    return VMLA_ERR_CONFIG;
+  if (!vmla::latent_attention_supported(static_cast<DType>(c->dtype), c->d_c, c->d_rope))
+    return VMLA_ERR_UNSUPPORTED;
+  return VMLA_OK;
+}
+
+size_t elem_bytes(const vmla_config* c) { return c->dtype == VMLA_DTYPE_F32 ? 4 : 2; }
+
+// Geometry-only part of a plan (no pointers).
+Plan geometry(const vmla_config* c) {
+  Plan p;
+  memset(&p, 0, sizeof(p));
+  p.dtype = static_cast<DType>(c->dtype);
+  p.B = c->batch;
+  p.d = c->hidden;
+  p.nh = c->n_heads;
+  p.d_nope = c->d_nope;
+  p.dr = c->d_rope;
+  p.dv = c->d_v;
+  p.dc = c->d_c;
+  p.dq = c->d_q;
+  p.D = c->d_c + c->d_rope;
+  p.dh = c->d_nope + c->d_rope;
+  p.Tpf = c->grid_h * c->grid_w;
+  p.grid_w = c->grid_w;
+  p.W = c->window_frames;
+  p.C = c->chunk_frames;
+  p.Nq = c->chunk_frames * p.Tpf;
+  p.pairs_t = c->rope_pairs_t;
+  p.pairs_h = c->rope_pairs_h;
+  p.pairs_w = c->rope_pairs_w;
+  p.qscale = (float)(1.4426950408889634 / sqrt((double)p.dh));
+  p.G = c->attn_workgroups > 0 ? c->attn_workgroups : kDefaultWorkgroups;
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace vmla {
+WorkspaceLayout workspace_layout(const Plan& p) {
+  const size_t es = p.dtype == DType::F32 ? 4 : 2;
+  const size_t M = (size_t)p.B * p.Nq;
+  WorkspaceLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.stage = take(M * p.D * es);
+  L.cq = take(M * p.dq * es);
+  L.qnope = take(M * p.nh * (size_t)p.d_nope * es);
+  L.qt = take(M * p.nh * (size_t)p.D * es);
+  L.olat = take(M * p.nh * (size_t)p.dc * es);
+  L.o = take(M * p.nh * (size_t)p.dv * es);
+  L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * sizeof(float));
+  L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
+  L.total = off;
+  return L;
+}
+}  // namespace vmla
+
+extern "C" {
+
+VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg) {
+  if (check_config(cfg) != VMLA_OK) return 0;
+  return (size_t)cfg->batch * cfg->window_frames * cfg->grid_h * cfg->grid_w *
+         (size_t)(cfg->d_c + cfg->d_rope) * elem_bytes(cfg);
+}
+
+VMLA_API size_t vmla_workspace_bytes(const vmla_config* cfg) {
+  if (check_config(cfg) != VMLA_OK) return 0;
+  return vmla::workspace_layout(geometry(cfg)).total;
+}
+
+VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* cache, void* workspace,
+                         const float* rope_freqs, vmla_ctx** out) {
+  if (!out) return VMLA_ERR_NULL;
+  *out = nullptr;
+  int st = check_config(cfg);
+  if (st != VMLA_OK) return st;
+  if (!w || !cache || !workspace) return VMLA_ERR_NULL;
+  const void* ptrs[] = {w->w_dkv, w->w_kr, w->w_dq, w->w_uq, w->w_uk, w->w_uv, w->w_o};
+  for (const void* q : ptrs)
+    if (!q) return VMLA_ERR_NULL;
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return VMLA_ERR_ALIGN;
+  if (!aligned16(cache) || !aligned16(workspace)) return VMLA_ERR_ALIGN;
+  const int npairs = cfg->d_rope / 2;
+  if (rope_freqs)
+    for (int i = 0; i < npairs; ++i)
+      if (!isfinite(rope_freqs[i])) return VMLA_ERR_ARG;
+
+  vmla_ctx* c = new (std::nothrow) vmla_ctx;
+  if (!c) return VMLA_ERR_STATE;
+  memset(c, 0, sizeof(*c));
+  c->cfg = *cfg;
+  c->w = *w;
+  c->cache = cache;
+  c->workspace = workspace;
+  c->n = 0;
+  if (rope_freqs) {
+    for (int i = 0; i < npairs; ++i) c->freq[i] = rope_freqs[i];
+  } else {
+    // omega_i = theta^(-2i / (2 p_a)) for i = 0..p_a-1 on each axis (t, h, w)
+    const int pa[3] = {cfg->rope_pairs_t, cfg->rope_pairs_h, cfg->rope_pairs_w};
+    int k = 0;
+    for (int a = 0; a < 3; ++a)
+      for (int i = 0; i < pa[a]; ++i)
+        c->freq[k++] = (float)pow((double)cfg->rope_theta, -2.0 * i / (2.0 * pa[a]));
+  }
+  *out = c;
+  return VMLA_OK;
+}
+
+static Plan make_plan(const vmla_ctx* c) {
+  Plan p = geometry(&c->cfg);
+  for (int i = 0; i < vmla::kMaxRopePairs; ++i) p.freq[i] = c->freq[i];
+  p.w_dkv = c->w.w_dkv;
+  p.w_kr = c->w.w_kr;
+  p.w_dq = c->w.w_dq;
+  p.w_uq = c->w.w_uq;
+  p.w_uk = c->w.w_uk;
+  p.w_uv = c->w.w_uv;
+  p.w_o = c->w.w_o;
+  p.cache = c->cache;
+  const vmla::WorkspaceLayout L = vmla::workspace_layout(p);
+  char* ws = static_cast<char*>(c->workspace);
+  p.stage = ws + L.stage;
+  p.cq = ws + L.cq;
+  p.qnope = ws + L.qnope;
+  p.qt = ws + L.qt;
+  p.olat = ws + L.olat;
+  p.o = ws + L.o;
+  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  return p;
+}
+
+VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stream) {
+  if (!ctx || !x) return VMLA_ERR_NULL;
+  if (!aligned16(x)) return VMLA_ERR_ALIGN;
+  if (ctx->n > INT64_MAX / 2) return VMLA_ERR_STATE;
+  Plan p = make_plan(ctx);
+  if (vmla::run_compress(p, x, ctx->n, ctx->cache, true, stream) != hipSuccess) return VMLA_ERR_HIP;
+  ctx->n += ctx->cfg.chunk_frames;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream) {
+  if (!ctx || !x || !out) return VMLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  Plan p = make_plan(ctx);
+  if (vmla::run_attend(p, ctx->n, x, out, stream) != hipSuccess) return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEvent_t attn_start,
+                                  hipEvent_t attn_stop, hipStream_t stream) {
+  if (!ctx || !x || !out || !attn_start || !attn_stop) return VMLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  Plan p = make_plan(ctx);
+  if (vmla::run_attend(p, ctx->n, x, out, stream, attn_start, attn_stop) != hipSuccess) return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_compress(vmla_ctx* ctx, const void* x, int64_t frame0, void* latents_out,
+                           hipStream_t stream) {
+  if (!ctx || !x || !latents_out) return VMLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(latents_out)) return VMLA_ERR_ALIGN;
+  if (frame0 < 0 || frame0 > INT64_MAX / 2) return VMLA_ERR_ARG;
+  Plan p = make_plan(ctx);
+  if (vmla::run_compress(p, x, frame0, latents_out, false, stream) != hipSuccess) return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_cache_state(const vmla_ctx* ctx, int64_t* frames_appended, int64_t* first_valid_frame,
+                              int32_t* n_valid_frames) {
+  if (!ctx) return VMLA_ERR_NULL;
+  const int64_t W = ctx->cfg.window_frames;
+  if (frames_appended) *frames_appended = ctx->n;
+  if (first_valid_frame) *first_valid_frame = ctx->n > W ? ctx->n - W : 0;
+  if (n_valid_frames) *n_valid_frames = (int32_t)(ctx->n < W ? ctx->n : W);
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_reset(vmla_ctx* ctx) {
+  if (!ctx) return VMLA_ERR_NULL;
+  ctx->n = 0;
+  return VMLA_OK;
+}
+
+VMLA_API void vmla_destroy(vmla_ctx* ctx) { delete ctx; }
+
+VMLA_API const char* vmla_status_string(int status) {
+  switch (status) {
+    case VMLA_OK: return "ok";
+    case VMLA_ERR_NULL: return "required pointer is NULL";
+    case VMLA_ERR_CONFIG: return "invalid configuration";
+    case VMLA_ERR_UNSUPPORTED: return "no kernel built for this (dtype, d_c, d_rope)";
+    case VMLA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case VMLA_ERR_STATE: return "call not valid in the current state";
+    case VMLA_ERR_ARG: return "argument out of range";
+    case VMLA_ERR_HIP: return "HIP runtime error on launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

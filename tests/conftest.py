@@ -26,3 +26,11 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_sessionstart(session):
+    """Tests load what is built; build only when no library exists yet."""
+    lib = os.path.join(ROOT, "mla_latent_kv_vmla_amd", "libvmla.so")
+    if not os.path.exists(lib):
+        from mla_latent_kv_vmla_amd.build import build
+        build()

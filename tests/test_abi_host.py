@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports every
+symbol include/vmla.h declares, and rejects bad arguments before any HIP call.
+No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_vmla_amd import vmla, workloads as wl
+
+HEADERS = [os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", f)
+           for f in sorted(os.listdir(os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")))
+           if f.endswith(".h")]
+
+FAKE = 0x7F0000000000  # 16-byte aligned address that is never dereferenced
+
+
+def declared_symbols():
+    out = []
+    for h in HEADERS:
+        out += re.findall(r"VMLA_API\s+[\w\s\*]*?\b(vmla_\w+)\s*\(", open(h).read())
+    return out
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    L = ctypes.CDLL(vmla.LIB_PATH)
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared but not exported"
+
+
+def test_status_strings_and_codes():
+    assert vmla.STATUS["VMLA_OK"] == 0
+    assert len(set(vmla.STATUS.values())) == len(vmla.STATUS)
+    for name, code in vmla.STATUS.items():
+        assert vmla.vmla_status_string(code) not in ("", "unknown status")
+    assert vmla.vmla_status_string(999) == "unknown status"
+
+
+def _cfg(g=wl.WAN_LAYER, **kw):
+    c = vmla.config_from_geometry(g)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_cache_and_workspace_bytes():
+    g = wl.WAN_LAYER
+    assert vmla.vmla_cache_bytes(_cfg(g)) == 1 * 21 * 1560 * 224 * 2  # 14.68 MB, bf16 rows of 224
+    t = wl.TINY
+    assert vmla.vmla_cache_bytes(_cfg(t)) == 2 * 16 * 32 * 4
+    ws = vmla.vmla_workspace_bytes(_cfg(g))
+    nq = 4680
+    lower = nq * (224 + 768 + 12 * 96 + 12 * 224 + 12 * 192 + 1536) * 2
+    assert ws >= lower
+    b4 = wl.STRESS[192]
+    assert vmla.vmla_cache_bytes(_cfg(b4)) == 4 * 42 * 1560 * 224 * 2
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, "VMLA_ERR_CONFIG"), ("hidden", 12, "VMLA_ERR_CONFIG"), ("d_nope", 0, "VMLA_ERR_CONFIG"),
+    ("chunk_frames", 22, "VMLA_ERR_CONFIG"), ("rope_pairs_t", 5, "VMLA_ERR_CONFIG"),
+    ("rope_theta", 0.0, "VMLA_ERR_CONFIG"), ("dtype", 7, "VMLA_ERR_CONFIG"), ("grid_w", 0, "VMLA_ERR_CONFIG"),
+    ("attn_workgroups", -1, "VMLA_ERR_CONFIG"),
+    ("d_c", 200, "VMLA_ERR_UNSUPPORTED"), ("dtype", vmla.VMLA_DTYPE_F32, "VMLA_ERR_UNSUPPORTED"),
+])
+def test_invalid_configs_rejected(field, value, code):
+    c = _cfg(**{field: value})
+    assert vmla.vmla_cache_bytes(c) == 0 and vmla.vmla_workspace_bytes(c) == 0
+    with pytest.raises(vmla.VmlaError) as e:
+        vmla.vmla_create(c, _fake_weights(), FAKE, FAKE)
+    assert e.value.code == vmla.STATUS[code]
+
+
+def _fake_weights(**override):
+    d = {n: FAKE + 256 * i for i, n in enumerate(vmla.LatentAttention.WEIGHT_NAMES)}
+    d.update(override)
+    return vmla.vmla_weights(**d)
+
+
+def test_create_rejects_null_and_misaligned():
+    c = _cfg()
+    for n in vmla.LatentAttention.WEIGHT_NAMES:
+        with pytest.raises(vmla.VmlaError) as e:
+            vmla.vmla_create(c, _fake_weights(**{n: 0}), FAKE, FAKE)
+        assert e.value.code == vmla.STATUS["VMLA_ERR_NULL"]
+        with pytest.raises(vmla.VmlaError) as e:
+            vmla.vmla_create(c, _fake_weights(**{n: FAKE + 8}), FAKE, FAKE)
+        assert e.value.code == vmla.STATUS["VMLA_ERR_ALIGN"]
+    for cache, ws, code in [(0, FAKE, "VMLA_ERR_NULL"), (FAKE, 0, "VMLA_ERR_NULL"),
+                            (FAKE + 4, FAKE, "VMLA_ERR_ALIGN"), (FAKE, FAKE + 2, "VMLA_ERR_ALIGN")]:
+        with pytest.raises(vmla.VmlaError) as e:
+            vmla.vmla_create(c, _fake_weights(), cache, ws)
+        assert e.value.code == vmla.STATUS[code]
+    with pytest.raises(vmla.VmlaError) as e:
+        vmla.vmla_create(c, _fake_weights(), FAKE, FAKE, rope_freqs=[float("nan")] * 16)
+    assert e.value.code == vmla.STATUS["VMLA_ERR_ARG"]
+
+
+def test_calls_reject_bad_arguments_before_launch():
+    ctx = vmla.vmla_create(_cfg(), _fake_weights(), FAKE, FAKE)
+    try:
+        bad = [
+            (lambda: vmla.vmla_attend(ctx, 0, FAKE, 0), "VMLA_ERR_NULL"),
+            (lambda: vmla.vmla_attend(ctx, FAKE, 0, 0), "VMLA_ERR_NULL"),
+            (lambda: vmla.vmla_attend(ctx, FAKE + 2, FAKE, 0), "VMLA_ERR_ALIGN"),
+            (lambda: vmla.vmla_compress_append(ctx, 0, 0), "VMLA_ERR_NULL"),
+            (lambda: vmla.vmla_compress_append(ctx, FAKE + 8, 0), "VMLA_ERR_ALIGN"),
+            (lambda: vmla.vmla_compress(ctx, FAKE, -1, FAKE, 0), "VMLA_ERR_ARG"),
+            (lambda: vmla.vmla_compress(ctx, FAKE, 0, 0, 0), "VMLA_ERR_NULL"),
+        ]
+        for f, code in bad:
+            with pytest.raises(vmla.VmlaError) as e:
+                f()
+            assert e.value.code == vmla.STATUS[code]
+        # a rejected append leaves the frame counter alone
+        assert vmla.vmla_cache_state(ctx) == (0, 0, 0)
+        vmla.vmla_reset(ctx)
+        assert vmla.vmla_cache_state(ctx) == (0, 0, 0)
+    finally:
+        vmla.vmla_destroy(ctx)
+    vmla.vmla_destroy(None)  # NULL is ignored
+
+
+def test_null_ctx_rejected():
+    L = vmla.lib()
+    assert L.vmla_reset(None) == vmla.STATUS["VMLA_ERR_NULL"]
+    assert L.vmla_cache_state(None, None, None, None) == vmla.STATUS["VMLA_ERR_NULL"]
+    assert L.vmla_attend(None, FAKE, FAKE, None) == vmla.STATUS["VMLA_ERR_NULL"]

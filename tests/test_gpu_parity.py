@@ -1,0 +1,132 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Cases span several attention row blocks and key tiles with ragged tails, partial
+and wrapped windows, fp32 and bf16 storage, three input scalings, batched
+streams, every stream-K split shape, and the full Wan-1.3B layer (sampled query
+tokens) in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+from gpu_harness import Rollout, assert_parity, to_dev, to_np
+from mla_latent_kv_vmla_amd import workloads as wl
+from oracle import mla, ring
+
+pytestmark = pytest.mark.gpu
+
+TINY_BF16 = wl.TINY.replace(name="tiny-bf16", dtype=wl.BF16)
+SMALL = wl.WAN_SMALL_GRID
+
+
+def _print_case(*a):
+    print("case:", *a, flush=True)
+
+
+@pytest.mark.parametrize("g", [wl.TINY, TINY_BF16, SMALL, wl.WAN_LAYER], ids=lambda g: g.name)
+def test_compress_rows_match_oracle(g):
+    _print_case("compress", g.name)
+    r = Rollout(g, mode="unit")
+    x = r.x(chunk=5)
+    frame0 = 13
+    got = to_np(r.dev.compress(to_dev(x, g), frame0))
+    for b in range(g.batch):
+        ref = mla.chunk_latents(g, r.w, x[b], frame0)
+        scale = np.abs(ref).max()
+        if g.dtype == wl.F32:
+            tol = 1e-5 * np.abs(ref) + 1e-6 * scale
+        else:  # one bf16 rounding of an fp32-accumulated value
+            tol = 2.0 ** -8 * np.abs(ref) + 1e-5 * scale
+        bad = np.abs(got[b] - ref) > tol
+        assert not bad.any(), f"{bad.sum()} latent entries off; worst {np.abs(got[b] - ref).max():.3e}"
+
+
+@pytest.mark.parametrize("g", [wl.TINY, SMALL.replace(window_frames=5, chunk_frames=2),
+                               SMALL.replace(window_frames=4, chunk_frames=4)],
+                         ids=["tiny-W2C1", "W5C2", "W4C4"])
+def test_ring_append_bit_exact(g):
+    """Append writes each frame's rows into slot f % W, byte-identical to the rows
+    the compress hook produces for that frame, and leaves every other slot alone."""
+    import torch
+    _print_case("ring", g.name, g.window_frames, g.chunk_frames)
+    r = Rollout(g, mode="unit", cache_fill=-5.0)
+    canary = r.dev.cache.clone()
+    model = ring.RingModel(g.window_frames, g.tokens_per_frame)
+    T = g.tokens_per_frame
+    rows_of_frame = {}
+    for k in range(9):
+        x = r.x(chunk=k)
+        xd = to_dev(x, g)
+        expect = r.dev.compress(xd, model.n)  # [B, C*T, D]
+        for i in range(g.chunk_frames):
+            rows_of_frame[model.n + i] = expect[:, i * T:(i + 1) * T].clone()
+        r.dev.append(xd)
+        model.append(g.chunk_frames)
+        torch.cuda.synchronize()
+        n, first, nvalid = r.dev.state()
+        assert (n, first, nvalid) == (model.n, model.valid_frames().start, len(model.valid_frames()))
+        occupied = model.slot_map()
+        for slot in range(g.window_frames):
+            got = r.dev.cache[:, slot * T:(slot + 1) * T]
+            want = rows_of_frame[occupied[slot]] if slot in occupied else canary[:, slot * T:(slot + 1) * T]
+            assert torch.equal(got.view(torch.int16 if got.dtype == torch.bfloat16 else torch.int32),
+                               want.view(torch.int16 if want.dtype == torch.bfloat16 else torch.int32)), \
+                f"slot {slot} after append {k}"
+
+
+def _rollout_parity(g, modes, n_chunks, attn_workgroups=0, query_tokens=None):
+    for mode in modes:
+        r = Rollout(g, mode=mode, attn_workgroups=attn_workgroups, cache_fill=float("nan"))
+        for k in range(n_chunks):
+            x = r.x(chunk=100 + k)
+            _print_case("attend", g.name, mode, "n=", r.n, "G=", attn_workgroups)
+            got = r.attend(x)
+            for b in range(g.batch):
+                ref = r.oracle(x, b, query_tokens)
+                gb = got[b] if query_tokens is None else got[b][query_tokens]
+                assert_parity(gb, ref, f"{g.name} {mode} n={r.n} b={b}")
+            r.append(r.x(chunk=k))
+
+
+@pytest.mark.parametrize("g", [wl.TINY, TINY_BF16], ids=lambda g: g.name)
+def test_attend_tiny_all_window_states(g):
+    # W=2, C=1: empty window, partial window, full, then wrapped several times
+    _rollout_parity(g, ["literal", "unit", "sharp"], n_chunks=6)
+
+
+@pytest.mark.parametrize("mode", ["literal", "unit", "sharp"])
+def test_attend_wan_widths_small_grid(mode):
+    # 180 queries x 12 heads = 2160 rows (8.4 row blocks of 256); 180..480 keys (ragged tiles)
+    _rollout_parity(SMALL, [mode], n_chunks=4)
+
+
+@pytest.mark.parametrize("G", [1, 3, 7, 64, 100000])
+def test_attend_stream_k_splits(G):
+    """Every way of cutting (row block, key tile) work across workgroups gives the
+    same answer: one workgroup for everything, uneven cuts, one tile each."""
+    _rollout_parity(SMALL, ["sharp"], n_chunks=3, attn_workgroups=G)
+
+
+@pytest.mark.parametrize("dc", [96, 192, 448])
+def test_attend_batched_streams_latent_widths(dc):
+    g = wl.STRESS[dc].replace(grid_h=6, grid_w=10, window_frames=7)
+    _rollout_parity(g, ["sharp"], n_chunks=4)
+
+
+def test_attend_wan_layer_full_size_sampled():
+    """The benchmark's workload: 21 cached frames (32,760 keys) + 3-frame chunk
+    (4,680 queries x 12 heads), default launch configuration."""
+    g = wl.WAN_LAYER
+    for mode in ["literal", "sharp"]:
+        _print_case("wan-full", mode)
+        r = Rollout(g, mode=mode, cache_fill=float("nan"))
+        for k in range(g.prefill_chunks):
+            r.append(r.x(chunk=k))
+        assert r.n == 21
+        x = r.x(chunk=g.prefill_chunks)
+        got = r.attend(x)
+        assert np.all(np.isfinite(got))
+        q = np.unique(np.concatenate([np.arange(8), np.arange(g.n_q - 8, g.n_q),
+                                      np.random.default_rng(0).choice(g.n_q, 32, replace=False)]))
+        ref = r.oracle(x, 0, q)
+        ma, mr = assert_parity(got[0][q], ref, f"wan-full {mode}")
+        print(f"wan-full {mode}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
