@@ -17,6 +17,13 @@
 // the score product and transposed [f][key] (latent part only) for the value
 // product; both are written from one set of global loads.
 //
+// With bf16 storage the value product runs on fp16 operands: the transposed
+// latent tile is converted bf16 -> fp16 while it is staged (exact for
+// magnitudes in fp16's normal range, below 65504) and P is rounded to fp16.
+// When the softmax is nearly flat every probability sits just below 1, where
+// bf16's spacing (2^-8) exceeds the spread of the probabilities themselves;
+// fp16's spacing there is 2^-11, at the same MFMA rate.
+//
 // Scheduling is stream-K over (stream, row block, key tile): workgroup w owns
 // iterations [w*I/G, (w+1)*I/G).  A row block finished by one workgroup is
 // written directly; a row block split across workgroups leaves unnormalised
@@ -24,6 +31,8 @@
 // with the usual log-sum-exp rule.  Scores are in log2 units (log2(e) is
 // folded into the query), and the running maximum is only moved when a tile
 // exceeds it by more than 2^8, which keeps rescaling of the accumulator rare.
+#include <type_traits>
+
 #include "device_common.h"
 #include "plan.h"
 
@@ -54,6 +63,7 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
   constexpr int NT = NW * 64;
   constexpr int KS = D + VEC;       // row-major key tile stride (+16 B)
   constexpr int CS = KTILE + 4;     // transposed latent tile stride
+  using VT = typename std::conditional<sizeof(T) == 2, f16, float>::type;  // value-product operand
   constexpr int KS_EL = KTILE * KS;
   constexpr int BUF_EL = KS_EL + DCP * CS;
   constexpr int NKS = D / (2 * KPL);
@@ -76,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
   if constexpr (DCP > DC) {  // padded channels of the transposed tile stay finite
     for (int i = tid; i < 2 * (DCP - DC) * CS; i += NT) {
       const int buf = i / ((DCP - DC) * CS), r = i % ((DCP - DC) * CS);
-      lds[buf * BUF_EL + KS_EL + DC * CS + r] = T(0.f);
+      reinterpret_cast<VT*>(lds + buf * BUF_EL + KS_EL)[DC * CS + r] = VT(0.f);
     }
   }
 
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
 
   auto store_tile = [&](int buf) {
     T* Ks = lds + buf * BUF_EL;
-    T* Ct = Ks + KS_EL;
+    VT* Ct = reinterpret_cast<VT*>(Ks + KS_EL);
 #pragma unroll
     for (int i = 0; i < CB_PER; ++i) {
       const int v = tid + i * NT;
@@ -127,19 +137,16 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
         // transpose the 4 keys x VEC channels block into C^T rows
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          T* dst = &Ct[(c * VEC + e) * CS + 4 * kg];
+          VT* dst = &Ct[(c * VEC + e) * CS + 4 * kg];
           if constexpr (sizeof(T) == 2) {
             const int dw = e >> 1;
-            uint32_t k0 = creg[i][0][dw], k1 = creg[i][1][dw], k2 = creg[i][2][dw], k3 = creg[i][3][dw];
-            uint32_t lo, hi;
-            if (e & 1) {
-              lo = (k0 >> 16) | (k1 & 0xFFFF0000u);
-              hi = (k2 >> 16) | (k3 & 0xFFFF0000u);
-            } else {
-              lo = (k0 & 0xFFFFu) | (k1 << 16);
-              hi = (k2 & 0xFFFFu) | (k3 << 16);
-            }
-            *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+            auto widen = [&](uint32_t word) {
+              return (e & 1) ? __uint_as_float(word & 0xFFFF0000u) : __uint_as_float(word << 16);
+            };
+            f16x4 h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = (f16)widen(creg[i][j][dw]);
+            *reinterpret_cast<f16x4*>(dst) = h;
           } else {
             *reinterpret_cast<u32x4*>(dst) = u32x4{creg[i][0][e], creg[i][1][e], creg[i][2][e], creg[i][3][e]};
           }
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
       if (kt + 1 < kt1) load_tile(b, kt + 1);
       if (wave_active) {
         const T* Ks = lds + buf * BUF_EL;
-        const T* Ct = Ks + KS_EL;
+        const VT* Ct = reinterpret_cast<const VT*>(Ks + KS_EL);
         const int kbase = kt * KTILE;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -230,26 +237,26 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
           l_run += lsum;
           // O^T += C^T[f][keys] * P^T[keys][rows]
           if constexpr (sizeof(T) == 2) {
-            bf16x8 pf[2];
+            f16x8 pf[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-              for (int j = 0; j < 8; ++j) pf[u][j] = (bf16)s[8 * u + j];
+              for (int j = 0; j < 8; ++j) pf[u][j] = (f16)s[8 * u + j];
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb) {
-              const T* crow = &Ct[(32 * fb + l32) * CS + 32 * kb + 4 * h32];
+              const VT* crow = &Ct[(32 * fb + l32) * CS + 32 * kb + 4 * h32];
 #pragma unroll
               for (int u = 0; u < 2; ++u) {
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(crow + 16 * u);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(crow + 16 * u + 8);
-                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[fb] = Mfma<bf16>::mma(a, pf[u], o[fb]);
+                const f16x4 lo = *reinterpret_cast<const f16x4*>(crow + 16 * u);
+                const f16x4 hi = *reinterpret_cast<const f16x4*>(crow + 16 * u + 8);
+                const f16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[u], o[fb], 0, 0, 0);
               }
             }
           } else {
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb) {
-              const T* crow = &Ct[(32 * fb + l32) * CS + 32 * kb + 4 * h32];
+              const VT* crow = &Ct[(32 * fb + l32) * CS + 32 * kb + 4 * h32];
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
                 const f32x4 run = *reinterpret_cast<const f32x4*>(crow + 8 * g);
@@ -302,6 +309,9 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
 }
 
 // Merge the partial states of every row block that was split across workgroups.
+// Workgroups w0..w1 hold the pieces of row block `unit`; every piece is its
+// workgroup's first (slot 2w) except possibly w0's, which is its second
+// (slot 2w0+1) when w0 started inside an earlier row block.
 template <typename T, int DC, int ROWS>
 __global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
   const long unit = blockIdx.x;
@@ -313,20 +323,23 @@ __global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
   long w1 = (i1 - 1) * p.G / I;
   while (w1 + 1 < p.G && start(w1 + 1) <= i1 - 1) ++w1;
   if (w0 == w1) return;  // one workgroup finished this row block and wrote it
+  const long slot0 = 2 * w0 + (start(w0) < i0 ? 1 : 0);
+  const int npieces = (int)(w1 - w0 + 1);
   const int b = (int)(unit / p.RB), rb = (int)(unit % p.RB);
-  for (int task = threadIdx.x; task < ROWS * (DC / 4); task += 256) {
-    const int r = task / (DC / 4), f = (task % (DC / 4)) * 4;
+  constexpr int Q = DC / 4;  // float4 columns per row
+  for (int task = threadIdx.x; task < ROWS * Q; task += 256) {
+    const int r = task / Q, f = (task % Q) * 4;
     const int row = rb * ROWS + r;
     if (row >= p.R) continue;
     float M = -__builtin_huge_valf();
-    for (long w = w0; w <= w1; ++w) {
-      const long sr = (2 * w + (start(w) < i0 ? 1 : 0)) * kAttnMaxRows + r;
+    for (int k = 0; k < npieces; ++k) {
+      const long sr = (k == 0 ? slot0 : 2 * (w0 + k)) * kAttnMaxRows + r;
       M = fmaxf(M, p.part_ml[sr * 2]);
     }
     float L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (long w = w0; w <= w1; ++w) {
-      const long sr = (2 * w + (start(w) < i0 ? 1 : 0)) * kAttnMaxRows + r;
+    for (int k = 0; k < npieces; ++k) {
+      const long sr = (k == 0 ? slot0 : 2 * (w0 + k)) * kAttnMaxRows + r;
       const float sc = __builtin_amdgcn_exp2f(p.part_ml[sr * 2] - M);
       L += p.part_ml[sr * 2 + 1] * sc;
       acc += sc * *reinterpret_cast<const f32x4*>(p.part_o + sr * DC + f);

@@ -8,7 +8,7 @@ tokens) in the launch configuration the benchmark times.
 import numpy as np
 import pytest
 
-from gpu_harness import Rollout, assert_parity, to_dev, to_np
+from gpu_harness import Rollout, to_dev, to_np
 from mla_latent_kv_vmla_amd import workloads as wl
 from oracle import mla, ring
 
@@ -81,9 +81,9 @@ def _rollout_parity(g, modes, n_chunks, attn_workgroups=0, query_tokens=None):
             _print_case("attend", g.name, mode, "n=", r.n, "G=", attn_workgroups)
             got = r.attend(x)
             for b in range(g.batch):
-                ref = r.oracle(x, b, query_tokens)
                 gb = got[b] if query_tokens is None else got[b][query_tokens]
-                assert_parity(gb, ref, f"{g.name} {mode} n={r.n} b={b}")
+                ma, mr = r.check(gb, x, b, query_tokens, f"{g.name} {mode} n={r.n} b={b}")
+                print(f"  b={b}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
             r.append(r.x(chunk=k))
 
 
@@ -127,6 +127,5 @@ def test_attend_wan_layer_full_size_sampled():
         assert np.all(np.isfinite(got))
         q = np.unique(np.concatenate([np.arange(8), np.arange(g.n_q - 8, g.n_q),
                                       np.random.default_rng(0).choice(g.n_q, 32, replace=False)]))
-        ref = r.oracle(x, 0, q)
-        ma, mr = assert_parity(got[0][q], ref, f"wan-full {mode}")
+        ma, mr = r.check(got[0][q], x, 0, q, f"wan-full {mode}")
         print(f"wan-full {mode}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
