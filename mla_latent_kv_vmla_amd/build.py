@@ -27,6 +27,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
 
 SOURCES = ["vmla_host.cpp", "pipeline.hip", "attention.hip"]
 
+# Per-source code generation options.  The attention kernels hold a 32*NB x DC
+# fp32 accumulator plus the absorbed query per wave; with MFMA results in the
+# VGPR form the register allocator keeps them in registers (AGPRs absorb the
+# overflow) instead of spilling to scratch memory.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
@@ -37,7 +43,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -5,31 +5,41 @@
 // (VideoMLA paper, appendix D.4: chunk-causal, the whole chunk and the whole
 // window are visible).  With the per-head key and value lifts absorbed
 // (score = q~ . [c | k_r], output = sum p * c, lifted by W_UV afterwards), all
-// 12 heads share one [c | k_r] key tile and one c value tile, so each tile is
+// heads share one [c | k_r] key tile and one c value tile, so each tile is
 // staged in LDS once per workgroup and reused by all of its query rows.
 //
-// Layout of the work (one workgroup = NW waves, 32 query rows per wave):
-//   S^T[key][row]  = K_tile[key][:] . Qt[row][:]      (32x32x16 bf16 MFMA, keys as MFMA rows)
+// Work layout (one workgroup = NW waves, 32*NB query rows per wave):
+//   S^T[key][row]  = K_tile[key][:] . Qt[row][:]      (32x32x16 MFMA, keys as MFMA rows)
 //   O^T[f][row]   += C^T[f][key] * P^T[key][row]     (the S^T accumulator is already
 //                                                      the B operand of this product)
 // so softmax statistics live per lane (one query row per lane pair) and P never
-// leaves registers.  The key tile is kept twice in LDS: row-major [key][D] for
-// the score product and transposed [f][key] (latent part only) for the value
-// product; both are written from one set of global loads.
+// leaves registers.
 //
-// With bf16 storage the value product runs on fp16 operands: the transposed
-// latent tile is converted bf16 -> fp16 while it is staged (exact for
-// magnitudes in fp16's normal range, below 65504) and P is rounded to fp16.
-// When the softmax is nearly flat every probability sits just below 1, where
-// bf16's spacing (2^-8) exceeds the spread of the probabilities themselves;
-// fp16's spacing there is 2^-11, at the same MFMA rate.
+// Staging.  A key tile lives in LDS twice: row-major [key][D] (storage type) for
+// the score product, and transposed [channel][key] for the value product.  The
+// row-major copy is loaded straight from the cache / chunk rows with LDS-DMA
+// loads (global_load_lds_dwordx4: lane L's 16 bytes land at M0 + 16 L), and the
+// transposed copy is an image that a pre-pass kernel builds once per call in the
+// workspace, already in LDS layout, so staging needs no registers and no VALU.
+// LDS layouts (per stage; two stages in two distinct arrays):
+//   Ks  [KTILE][D + 16 B]: 16-B chunk q of row r lives at chunk q ^ ((r >> 4) & 3)
+//   C^T [DCP][KTILE + 16 B]: within every 16-key group the key index has bits 2
+//       and 3 swapped, so the 8 keys a lane feeds to one value MFMA are one
+//       contiguous 16-B read.  Both layouts read without bank conflicts.
+//
+// Numerics.  With bf16 storage the value product runs on fp16 operands: the
+// transposed image holds the latents converted bf16 -> fp16 (exact for
+// magnitudes in fp16's normal range, below 65504) and P is rounded to fp16.  When
+// the softmax is nearly flat every probability sits just below 1, where bf16's
+// spacing (2^-8) exceeds the spread of the probabilities themselves; fp16's
+// spacing there is 2^-11, at the same MFMA rate.
 //
 // Scheduling is stream-K over (stream, row block, key tile): workgroup w owns
 // iterations [w*I/G, (w+1)*I/G).  A row block finished by one workgroup is
 // written directly; a row block split across workgroups leaves unnormalised
 // partial states (at most two per workgroup) that the combine kernel merges
 // with the usual log-sum-exp rule.  Scores are in log2 units (log2(e) is
-// folded into the query), and the running maximum is only moved when a tile
+// folded into the query), and the running maximum is only moved when a block
 // exceeds it by more than 2^8, which keeps rescaling of the accumulator rare.
 #include <type_traits>
 
@@ -45,6 +55,7 @@ template <typename T> struct AttnArgs {
   T* out;          // [B][R][DC]
   float* part_o;   // [2G][kAttnMaxRows][DC]
   float* part_ml;  // [2G][kAttnMaxRows][2]
+  void* vtiles;    // [B][KT] value-tile images
   long cbs, sbs;
   int R, n_ring, n_keys, RB, KT, B, G;
 };
@@ -53,112 +64,133 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
 
-template <typename T, int DC, int DR, int KTILE, int NW>
-__global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
-  using MF = Mfma<T>;
-  constexpr int KPL = MF::KPL;
-  constexpr int D = DC + DR;
-  constexpr int DCP = (DC + 31) / 32 * 32;
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int NT = NW * 64;
-  constexpr int KS = D + VEC;       // row-major key tile stride (+16 B)
-  constexpr int CS = KTILE + 4;     // transposed latent tile stride
+// Compile-time geometry of one instantiation.
+template <typename T, int DC, int DR, int KTILE> struct TileGeo {
   using VT = typename std::conditional<sizeof(T) == 2, f16, float>::type;  // value-product operand
-  constexpr int KS_EL = KTILE * KS;
-  constexpr int BUF_EL = KS_EL + DCP * CS;
+  static_assert(sizeof(VT) == sizeof(T), "tile sizing assumes equal widths");
+  static constexpr int D = DC + DR;
+  static constexpr int DCP = (DC + 31) / 32 * 32;
+  static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-B chunk
+  static constexpr int KS = D + VEC;               // row-major tile row (+16 B)
+  static constexpr int CS = KTILE + VEC;           // transposed tile row (+16 B)
+  static constexpr int KCH = KS / VEC;             // 16-B chunks per row-major row
+  static constexpr int CCH = CS / VEC;             // 16-B chunks per transposed row
+  static constexpr int KPOS = KTILE * KCH;         // chunks of the row-major tile
+  static constexpr int CPOS = DCP * CCH;           // chunks of the transposed tile
+  static constexpr int KS_EL = KTILE * KS;
+  static constexpr int BUF_EL = KS_EL + DCP * CS;
+  static constexpr int KI = (KPOS + 63) / 64;      // wave-wide 1-KB loads per stage
+  static constexpr int CI = (CPOS + 63) / 64;
+  static constexpr size_t IMG_BYTES = (size_t)CPOS * 16;
+  static_assert(DC % VEC == 0 && DR % VEC == 0, "unsupported widths");
+  static_assert((D / VEC) % 4 == 0, "chunk swizzle works within groups of 4 chunks");
+  static_assert(KTILE % 32 == 0, "bad tile");
+  __device__ static int perm_group(int kg) { return (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1); }
+};
+
+// Key row `key` of stream b, clamped to the last valid key (rows past n_keys
+// are masked out of the scores, so their contents never matter): ring rows
+// first, then the chunk's staged rows.
+template <typename T, int D>
+__device__ inline const T* key_row(const AttnArgs<T>& p, int b, int key) {
+  key = key < p.n_keys ? key : p.n_keys - 1;
+  return key < p.n_ring ? p.cache + (long)b * p.cbs + (long)key * D
+                        : p.stage + (long)b * p.sbs + (long)(key - p.n_ring) * D;
+}
+
+// Pre-pass: transposed value-tile images.  Image (b, t) holds, for the keys of
+// tile t, rows = latent channels (zero rows pad DC up to a multiple of 32) in the
+// value-operand type, keys permuted within 16-key groups.
+template <typename T, int DC, int DR, int KTILE>
+__global__ __launch_bounds__(256) void latent_value_tiles(AttnArgs<T> p) {
+  using G = TileGeo<T, DC, DR, KTILE>;
+  using VT = typename G::VT;
+  constexpr int KG = KTILE / 4, CV = DC / G::VEC;
+  const int t = blockIdx.x, b = blockIdx.y;
+  VT* img = reinterpret_cast<VT*>(static_cast<char*>(p.vtiles) + ((size_t)b * p.KT + t) * G::IMG_BYTES);
+  for (int v = threadIdx.x; v < KG * CV; v += 256) {
+    const int kg = v % KG, c = v / KG;
+    u32x4 k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = ld16(key_row<T, G::D>(p, b, t * KTILE + 4 * kg + j) + c * G::VEC);
+    const int pcol = 4 * G::perm_group(kg);
+#pragma unroll
+    for (int e = 0; e < G::VEC; ++e) {
+      VT* dst = img + (c * G::VEC + e) * G::CS + pcol;
+      if constexpr (sizeof(T) == 2) {
+        const int dw = e >> 1;
+        auto widen = [&](uint32_t word) {
+          return (e & 1) ? __uint_as_float(word & 0xFFFF0000u) : __uint_as_float(word << 16);
+        };
+        f16x4 h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = (f16)widen(k[j][dw]);
+        *reinterpret_cast<f16x4*>(dst) = h;
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{k[0][e], k[1][e], k[2][e], k[3][e]};
+      }
+    }
+  }
+  for (int i = threadIdx.x; i < (G::DCP - DC) * G::CS; i += 256) img[DC * G::CS + i] = VT(0.f);
+}
+
+template <typename T, int DC, int DR, int KTILE, int NW, int NB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(8 / NW, 8 / NW)))
+void latent_attn_kernel(AttnArgs<T> p) {
+  using G = TileGeo<T, DC, DR, KTILE>;
+  using VT = typename G::VT;
+  using MF = Mfma<T>;
+  constexpr bool HALF = sizeof(T) == 2;
+  constexpr int KPL = MF::KPL;
+  constexpr int D = G::D, DCP = G::DCP, VEC = G::VEC, KS = G::KS, CS = G::CS;
+  constexpr int RW = 32 * NB;               // query rows per wave
   constexpr int NKS = D / (2 * KPL);
   constexpr int NKB = KTILE / 32;
   constexpr int NFB = DCP / 32;
-  constexpr int CV = DC / VEC, RV = DR / VEC;
-  constexpr int NCB = (KTILE / 4) * CV;  // blocks of 4 keys x VEC latent channels
-  constexpr int NRC = KTILE * RV;        // 16-B chunks of the rotary part
-  constexpr int CB_PER = (NCB + NT - 1) / NT;
-  constexpr int RC_PER = (NRC + NT - 1) / NT;
-  static_assert(D % (2 * KPL) == 0 && DC % VEC == 0 && DR % VEC == 0, "unsupported widths");
-  static_assert(KTILE % 32 == 0 && NW * 32 <= kAttnMaxRows, "bad tile");
+  constexpr int NI = G::KI + G::CI;         // 1-KB loads per stage, spread over the waves
+  constexpr int NI_W = (NI + NW - 1) / NW;
+  static_assert(NW * RW <= kAttnMaxRows, "row block too large");
 
-  __shared__ __attribute__((aligned(16))) T lds[2 * BUF_EL];
+  __shared__ __attribute__((aligned(16))) T lds0[G::BUF_EL];
+  __shared__ __attribute__((aligned(16))) T lds1[G::BUF_EL];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
   const float NEG_INF = -__builtin_huge_valf();
 
-  if constexpr (DCP > DC) {  // padded channels of the transposed tile stay finite
-    for (int i = tid; i < 2 * (DCP - DC) * CS; i += NT) {
-      const int buf = i / ((DCP - DC) * CS), r = i % ((DCP - DC) * CS);
-      reinterpret_cast<VT*>(lds + buf * BUF_EL + KS_EL)[DC * CS + r] = VT(0.f);
-    }
+  // Row-major staging: for each of this wave's loads, the (row, chunk) whose
+  // swizzled LDS position is this lane's slot, packed as row << 12 | element offset.
+  int kslot[NI_W];
+#pragma unroll
+  for (int k = 0; k < NI_W; ++k) {
+    const int pos = (wave + k * NW) * 64 + lane;
+    const int r = pos / G::KCH, phys = pos % G::KCH;
+    const int q = phys < G::KCH - 1 ? (phys ^ ((r >> 4) & 3)) : 0;  // pad slot: any valid chunk
+    kslot[k] = (r << 12) | (q * VEC);
   }
 
-  u32x4 creg[CB_PER][4];
-  u32x4 rreg[RC_PER];
-
-  auto row_ptr = [&](int b, int key) -> const T* {
-    if (key < p.n_ring) return p.cache + b * p.cbs + (long)key * D;
-    if (key < p.n_keys) return p.stage + b * p.sbs + (long)(key - p.n_ring) * D;
-    return nullptr;
-  };
-
-  auto load_tile = [&](int b, int kt) {
+  // Issue the LDS-DMA loads of tile kt (both layouts) into stage `buf`.
+  auto issue_tile = [&](int b, int kt, T* buf) {
     const int kbase = kt * KTILE;
+    const T* base = nullptr;
+    if (kbase + KTILE <= p.n_ring) base = p.cache + (long)b * p.cbs + (long)kbase * D;
+    else if (kbase >= p.n_ring && kbase + KTILE <= p.n_keys)
+      base = p.stage + (long)b * p.sbs + (long)(kbase - p.n_ring) * D;
+    const char* img = static_cast<const char*>(p.vtiles) + ((size_t)b * p.KT + kt) * G::IMG_BYTES;
 #pragma unroll
-    for (int i = 0; i < CB_PER; ++i) {
-      const int v = tid + i * NT;
-      if (NCB % NT == 0 || v < NCB) {
-        const int c = v % CV, kg = v / CV;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const T* src = row_ptr(b, kbase + 4 * kg + j);
-          creg[i][j] = src ? ld16(src + c * VEC) : u32x4{0, 0, 0, 0};
+    for (int k = 0; k < NI_W; ++k) {
+      const int idx = wave + k * NW;  // wave-uniform
+      if (idx < G::KI) {
+        const int pos = idx * 64 + lane;
+        if (G::KPOS % 64 == 0 || pos < G::KPOS) {
+          const int r = kslot[k] >> 12, off = kslot[k] & 0xFFF;
+          const T* src = base ? base + r * D + off : key_row<T, D>(p, b, kbase + r) + off;
+          lds_dma16(src, buf + idx * 64 * VEC);
         }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < RC_PER; ++i) {
-      const int v = tid + i * NT;
-      if (NRC % NT == 0 || v < NRC) {
-        const int c = v % RV, key = v / RV;
-        const T* src = row_ptr(b, kbase + key);
-        rreg[i] = src ? ld16(src + DC + c * VEC) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    T* Ks = lds + buf * BUF_EL;
-    VT* Ct = reinterpret_cast<VT*>(Ks + KS_EL);
-#pragma unroll
-    for (int i = 0; i < CB_PER; ++i) {
-      const int v = tid + i * NT;
-      if (NCB % NT == 0 || v < NCB) {
-        const int c = v % CV, kg = v / CV;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&Ks[(4 * kg + j) * KS + c * VEC]) = creg[i][j];
-        // transpose the 4 keys x VEC channels block into C^T rows
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          VT* dst = &Ct[(c * VEC + e) * CS + 4 * kg];
-          if constexpr (sizeof(T) == 2) {
-            const int dw = e >> 1;
-            auto widen = [&](uint32_t word) {
-              return (e & 1) ? __uint_as_float(word & 0xFFFF0000u) : __uint_as_float(word << 16);
-            };
-            f16x4 h;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) h[j] = (f16)widen(creg[i][j][dw]);
-            *reinterpret_cast<f16x4*>(dst) = h;
-          } else {
-            *reinterpret_cast<u32x4*>(dst) = u32x4{creg[i][0][e], creg[i][1][e], creg[i][2][e], creg[i][3][e]};
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < RC_PER; ++i) {
-      const int v = tid + i * NT;
-      if (NRC % NT == 0 || v < NRC) {
-        const int c = v % RV, key = v / RV;
-        *reinterpret_cast<u32x4*>(&Ks[key * KS + DC + c * VEC]) = rreg[i];
+      } else if (idx < NI) {
+        const int ci = idx - G::KI, pos = ci * 64 + lane;
+        if (G::CPOS % 64 == 0 || pos < G::CPOS)
+          lds_dma16(img + (size_t)pos * 16, buf + G::KS_EL + ci * 64 * VEC);
       }
     }
   };
@@ -172,108 +204,157 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
     const int kt1 = (int)((long)kt0 + (it1 - it) < p.KT ? (long)kt0 + (it1 - it) : p.KT);
     const int b = (int)(unit / p.RB), rb = (int)(unit % p.RB);
     const bool first_piece = (it == it0);
-    const int row0 = rb * (NW * 32) + wave * 32;
-    const bool wave_active = row0 < p.R;
-    const int qrow = row0 + l32;
+    const int row0 = rb * (NW * RW) + wave * RW;
 
-    typename MF::Frag qf[NKS];
-    {
+    typename MF::Frag qf[NB][NKS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int qrow = row0 + 32 * nb + l32;
       const T* qsrc = p.qt + ((long)b * p.R + qrow) * D + KPL * h32;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[ks] = qrow < p.R ? MF::load(qsrc + ks * 2 * KPL) : MF::zero();
+      for (int ks = 0; ks < NKS; ++ks) qf[nb][ks] = qrow < p.R ? MF::load(qsrc + ks * 2 * KPL) : MF::zero();
     }
-    f32x16 o[NFB];
+    f32x16 o[NB][NFB];
+    float m_run[NB], l_run[NB];
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) o[fb] = f32x16{};
-    float m_run = NEG_INF, l_run = 0.f;
-
-    load_tile(b, kt0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int buf = (kt - kt0) & 1;
-      if (kt + 1 < kt1) load_tile(b, kt + 1);
-      if (wave_active) {
-        const T* Ks = lds + buf * BUF_EL;
-        const VT* Ct = reinterpret_cast<const VT*>(Ks + KS_EL);
-        const int kbase = kt * KTILE;
+    for (int nb = 0; nb < NB; ++nb) {
+      m_run[nb] = NEG_INF;
+      l_run[nb] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          // S^T for 32 keys x 32 query rows
-          f32x16 s = f32x16{};
+      for (int fb = 0; fb < NFB; ++fb) o[nb][fb] = f32x16{};
+    }
+
+    // all query-row blocks of one tile held in `cur`
+    auto compute = [&](int kt, const T* cur) {
+      const T* Ks = cur;
+      const VT* Ct = reinterpret_cast<const VT*>(cur + G::KS_EL) + l32 * CS;
+      const int kbase = kt * KTILE;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        // S^T for 32 keys x RW query rows; each K fragment feeds NB MFMAs
+        f32x16 s[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+        const int r = 32 * kb + l32;
+        if constexpr (HALF) {  // chunk 2ks+h, swizzled: two per-lane bases, immediate offsets
+          const int sw = (r >> 4) & 3;
+          const T* b0 = Ks + r * KS + ((h32 ^ sw) * VEC);
+          const T* b1 = Ks + r * KS + (((2 + h32) ^ sw) * VEC);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            const auto a = MF::load(&Ks[(32 * kb + l32) * KS + ks * 2 * KPL + KPL * h32]);
-            s = MF::mma(a, qf[ks], s);
-          }
-          if (kbase + 32 * kb + 32 > p.n_keys) {
+            const auto a = MF::load((ks & 1 ? b1 : b0) + 4 * VEC * (ks >> 1));
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (kbase + 32 * kb + 8 * (r >> 2) + 4 * h32 + (r & 3) >= p.n_keys) s[r] = NEG_INF;
+            for (int nb = 0; nb < NB; ++nb) s[nb] = MF::mma(a, qf[nb][ks], s[nb]);
           }
-          // online softmax; every 32-key block holds at least one valid key
-          // except blocks wholly past n_keys, whose probabilities are all zero
-          float mx = NEG_INF;
+        } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-          mx = fmaxf(mx, xor32(mx));
-          const bool need = mx > m_run + kRescaleSlack;
-          if (__any(need)) {
-            const float mnew = need ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
-            m_run = mnew;
-            l_run *= alpha;
+          for (int ks = 0; ks < NKS; ++ks) {
+            const int e = ks * 2 * KPL + KPL * h32;
+            const auto a = MF::load(&Ks[r * KS + (((e / VEC) ^ ((r >> 4) & 3)) * VEC) + e % VEC]);
 #pragma unroll
-            for (int fb = 0; fb < NFB; ++fb) o[fb] *= alpha;
+            for (int nb = 0; nb < NB; ++nb) s[nb] = MF::mma(a, qf[nb][ks], s[nb]);
           }
+        }
+        if (kbase + 32 * kb + 32 > p.n_keys) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (kbase + 32 * kb + 8 * (rr >> 2) + 4 * h32 + (rr & 3) >= p.n_keys)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) s[nb][rr] = NEG_INF;
+        }
+        // online softmax per query row (lane pair); every piece's first block
+        // holds a valid key, so m_run is finite before any all-masked block
+        bool need[NB], any_need = false;
+        float mx[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float m = s[nb][0];
+#pragma unroll
+          for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, s[nb][rr]);
+          mx[nb] = fmaxf(m, xor32(m));
+          need[nb] = mx[nb] > m_run[nb] + kRescaleSlack;
+          any_need |= need[nb];
+        }
+        if (__any(any_need)) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const float mnew = need[nb] ? mx[nb] : m_run[nb];
+            const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - mnew);
+            m_run[nb] = mnew;
+            l_run[nb] *= alpha;
+#pragma unroll
+            for (int fb = 0; fb < NFB; ++fb) o[nb][fb] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
           float lsum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[r] - m_run);
-            s[r] = e;
+          for (int rr = 0; rr < 16; ++rr) {
+            const float e = __builtin_amdgcn_exp2f(s[nb][rr] - m_run[nb]);
+            s[nb][rr] = e;
             lsum += e;
           }
-          l_run += lsum;
-          // O^T += C^T[f][keys] * P^T[keys][rows]
-          if constexpr (sizeof(T) == 2) {
-            f16x8 pf[2];
+          l_run[nb] += lsum;
+        }
+        // O^T += C^T[f][keys] * P^T[keys][rows]; each C^T fragment feeds NB MFMAs
+        if constexpr (HALF) {
+          f16x8 pf[NB][2];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-              for (int j = 0; j < 8; ++j) pf[u][j] = (f16)s[8 * u + j];
+              for (int j = 0; j < 8; ++j) pf[nb][u][j] = (f16)s[nb][8 * u + j];
 #pragma unroll
-            for (int fb = 0; fb < NFB; ++fb) {
-              const VT* crow = &Ct[(32 * fb + l32) * CS + 32 * kb + 4 * h32];
+          for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-              for (int u = 0; u < 2; ++u) {
-                const f16x4 lo = *reinterpret_cast<const f16x4*>(crow + 16 * u);
-                const f16x4 hi = *reinterpret_cast<const f16x4*>(crow + 16 * u + 8);
-                const f16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[u], o[fb], 0, 0, 0);
-              }
+            for (int u = 0; u < 2; ++u) {
+              const f16x8 a = *reinterpret_cast<const f16x8*>(Ct + 32 * fb * CS + 32 * kb + 16 * u + 8 * h32);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                o[nb][fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][u], o[nb][fb], 0, 0, 0);
             }
-          } else {
+        } else {
 #pragma unroll
-            for (int fb = 0; fb < NFB; ++fb) {
-              const VT* crow = &Ct[(32 * fb + l32) * CS + 32 * kb + 4 * h32];
+          for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const f32x4 run = *reinterpret_cast<const f32x4*>(crow + 8 * g);
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 run = *reinterpret_cast<const f32x4*>(Ct + 32 * fb * CS + 32 * kb + 16 * (g >> 1) +
+                                                                8 * h32 + 4 * (g & 1));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[fb] = Mfma<float>::mma(run[i], s[4 * g + i], o[fb]);
-              }
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[nb][fb] = Mfma<float>::mma(run[i], s[nb][4 * g + i], o[nb][fb]);
             }
-          }
         }
       }
-      if (kt + 1 < kt1) store_tile(buf ^ 1);
+    };
+
+    // One tile: prefetch the next tile into the other stage, compute this one,
+    // then wait for this thread's loads and meet at the barrier (which also
+    // retires every read of `cur` before it is refilled).
+    auto step = [&](int kt, const T* cur, T* nxt) {
+      if (kt + 1 < kt1) issue_tile(b, kt + 1, nxt);
+      compute(kt, cur);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+    };
+
+    issue_tile(b, kt0, lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      step(kt, lds0, lds1);
+      if (kt + 1 < kt1) step(kt + 1, lds1, lds0);
     }
 
-    const float l_tot = l_run + xor32(l_run);
-    if (wave_active) {
-      if (kt0 == 0 && kt1 == p.KT) {
+    const bool full = (kt0 == 0 && kt1 == p.KT);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float l_tot = l_run[nb] + xor32(l_run[nb]);
+      const int qrow = row0 + 32 * nb + l32;
+      if (full) {
         if (qrow < p.R) {
           T* dst = p.out + ((long)b * p.R + qrow) * DC;
           const float inv = 1.f / l_tot;
@@ -283,12 +364,13 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
             for (int q = 0; q < 4; ++q) {
               const int f = 32 * fb + 8 * q + 4 * h32;
               if (f < DC)
-                store4(dst + f, o[fb][4 * q] * inv, o[fb][4 * q + 1] * inv, o[fb][4 * q + 2] * inv,
-                       o[fb][4 * q + 3] * inv);
+                store4(dst + f, o[nb][fb][4 * q] * inv, o[nb][fb][4 * q + 1] * inv, o[nb][fb][4 * q + 2] * inv,
+                       o[nb][fb][4 * q + 3] * inv);
             }
         }
-      } else {
-        const long slot_row = (long)(2 * blockIdx.x + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * 32 + l32;
+      } else if (row0 < p.R) {
+        const long slot_row =
+            (long)(2 * blockIdx.x + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * RW + 32 * nb + l32;
         float* po = p.part_o + slot_row * DC;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
@@ -296,10 +378,11 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
           for (int q = 0; q < 4; ++q) {
             const int f = 32 * fb + 8 * q + 4 * h32;
             if (f < DC)
-              *reinterpret_cast<f32x4*>(po + f) = f32x4{o[fb][4 * q], o[fb][4 * q + 1], o[fb][4 * q + 2], o[fb][4 * q + 3]};
+              *reinterpret_cast<f32x4*>(po + f) =
+                  f32x4{o[nb][fb][4 * q], o[nb][fb][4 * q + 1], o[nb][fb][4 * q + 2], o[nb][fb][4 * q + 3]};
           }
         if (h32 == 0) {
-          p.part_ml[slot_row * 2] = m_run;
+          p.part_ml[slot_row * 2] = m_run[nb];
           p.part_ml[slot_row * 2 + 1] = l_tot;
         }
       }
@@ -314,7 +397,9 @@ __global__ __launch_bounds__(NW * 64) void latent_attn_kernel(AttnArgs<T> p) {
 // (slot 2w0+1) when w0 started inside an earlier row block.
 template <typename T, int DC, int ROWS>
 __global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
-  const long unit = blockIdx.x;
+  constexpr int SLICE = 16;  // rows per workgroup: many small workgroups hide load latency
+  const long unit = blockIdx.x / (ROWS / SLICE);
+  const int r0 = (int)(blockIdx.x % (ROWS / SLICE)) * SLICE;
   const long I = (long)p.B * p.RB * p.KT;
   const long i0 = unit * p.KT, i1 = i0 + p.KT;
   auto start = [&](long w) { return w * I / p.G; };
@@ -327,8 +412,8 @@ __global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
   const int npieces = (int)(w1 - w0 + 1);
   const int b = (int)(unit / p.RB), rb = (int)(unit % p.RB);
   constexpr int Q = DC / 4;  // float4 columns per row
-  for (int task = threadIdx.x; task < ROWS * Q; task += 256) {
-    const int r = task / Q, f = (task % Q) * 4;
+  for (int task = threadIdx.x; task < SLICE * Q; task += 256) {
+    const int r = r0 + task / Q, f = (task % Q) * 4;
     const int row = rb * ROWS + r;
     if (row >= p.R) continue;
     float M = -__builtin_huge_valf();
@@ -349,9 +434,9 @@ __global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
   }
 }
 
-template <typename T, int DC, int DR, int KTILE, int NW>
+template <typename T, int DC, int DR, int KTILE, int NW, int NB>
 static hipError_t launch_latent(const AttnCall& c, hipStream_t s) {
-  constexpr int ROWS = NW * 32;
+  constexpr int ROWS = NW * 32 * NB;
   AttnArgs<T> a;
   a.qt = static_cast<const T*>(c.qt);
   a.cache = static_cast<const T*>(c.cache);
@@ -359,6 +444,7 @@ static hipError_t launch_latent(const AttnCall& c, hipStream_t s) {
   a.out = static_cast<T*>(c.out);
   a.part_o = c.part_o;
   a.part_ml = c.part_ml;
+  a.vtiles = c.vtiles;
   a.cbs = c.cache_bstride;
   a.sbs = c.stage_bstride;
   a.R = c.R;
@@ -369,27 +455,55 @@ static hipError_t launch_latent(const AttnCall& c, hipStream_t s) {
   a.B = c.B;
   const long I = (long)a.B * a.RB * a.KT;
   a.G = (int)(c.G < I ? c.G : I);
-  latent_attn_kernel<T, DC, DR, KTILE, NW><<<a.G, NW * 64, 0, s>>>(a);
+  latent_value_tiles<T, DC, DR, KTILE><<<dim3(a.KT, a.B), 256, 0, s>>>(a);
+  latent_attn_kernel<T, DC, DR, KTILE, NW, NB><<<a.G, NW * 64, 0, s>>>(a);
   if (I != (long)a.G * a.KT)
-    latent_attn_combine<T, DC, ROWS><<<a.B * a.RB, 256, 0, s>>>(a);
+    latent_attn_combine<T, DC, ROWS><<<a.B * a.RB * (ROWS / 16), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
+// Kernel shape per built (dtype, d_c, d_rope): keys per tile, waves per
+// workgroup, 32-row blocks per wave.
+struct LatentShape {
+  int ktile, nw, nb;
+};
+
+static bool latent_shape(DType dt, int dc, int dr, LatentShape& sh) {
+  if (dt == DType::F32) {
+    if (dc == 24 && dr == 8) return sh = {64, 4, 1}, true;
+    return false;
+  }
+  if (dc == 24 && dr == 8) return sh = {64, 4, 1}, true;
+  if (dr == 32 && dc == 96) return sh = {64, 8, 1}, true;
+  if (dr == 32 && dc == 192) return sh = {64, 8, 1}, true;
+  if (dr == 32 && dc == 448) return sh = {32, 4, 1}, true;
+  return false;
+}
+
 bool latent_attention_supported(DType dt, int dc, int dr) {
-  if (dt == DType::F32) return dc == 24 && dr == 8;
-  return (dc == 24 && dr == 8) || (dr == 32 && (dc == 96 || dc == 192 || dc == 448));
+  LatentShape sh;
+  return latent_shape(dt, dc, dr, sh);
+}
+
+size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_keys) {
+  LatentShape sh;
+  if (!latent_shape(dt, dc, dr, sh)) return 0;
+  const size_t es = dt == DType::F32 ? 4 : 2;
+  const size_t dcp = (size_t)(dc + 31) / 32 * 32;
+  const size_t tiles = (size_t)(max_keys + sh.ktile - 1) / sh.ktile;
+  return (size_t)B * tiles * dcp * (sh.ktile + 16 / es) * es;
 }
 
 hipError_t run_latent_attention(const AttnCall& c, hipStream_t s) {
   if (c.dtype == DType::F32) {
-    if (c.dc == 24 && c.dr == 8) return launch_latent<float, 24, 8, 64, 4>(c, s);
+    if (c.dc == 24 && c.dr == 8) return launch_latent<float, 24, 8, 64, 4, 1>(c, s);
     return hipErrorInvalidValue;
   }
-  if (c.dc == 24 && c.dr == 8) return launch_latent<bf16, 24, 8, 64, 4>(c, s);
+  if (c.dc == 24 && c.dr == 8) return launch_latent<bf16, 24, 8, 64, 4, 1>(c, s);
   if (c.dr == 32) {
-    if (c.dc == 96) return launch_latent<bf16, 96, 32, 64, 8>(c, s);
-    if (c.dc == 192) return launch_latent<bf16, 192, 32, 64, 8>(c, s);
-    if (c.dc == 448) return launch_latent<bf16, 448, 32, 32, 4>(c, s);
+    if (c.dc == 96) return launch_latent<bf16, 96, 32, 64, 8, 1>(c, s);
+    if (c.dc == 192) return launch_latent<bf16, 192, 32, 64, 8, 1>(c, s);
+    if (c.dc == 448) return launch_latent<bf16, 448, 32, 32, 4, 1>(c, s);
   }
   return hipErrorInvalidValue;
 }

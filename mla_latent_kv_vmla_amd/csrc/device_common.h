@@ -56,6 +56,13 @@ __device__ inline void store4(float* p, float a, float b, float c, float d) {
 // 16-byte global load / zero of one vector of storage elements.
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// LDS-DMA load: each active lane copies 16 bytes from `src` to LDS; lane L's
+// bytes land at lds_wave_base + 16*L (lds_wave_base must be wave-uniform).
+// Completion is tracked by the vector-memory counter.
+__device__ inline void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 // 3D-RoPE description: per complex pair p its axis (t, h, w by index ranges)
 // and angular frequency.  Token (frame f, position s in the frame) has
 // coordinates (f, s / grid_w, s % grid_w).

@@ -199,6 +199,7 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
     a.out = p.olat;
     a.part_o = p.part_o;
     a.part_ml = p.part_ml;
+    a.vtiles = p.vtiles;
     a.cache_bstride = (long)p.W * p.Tpf * p.D;
     a.stage_bstride = (long)p.Nq * p.D;
     a.B = p.B;

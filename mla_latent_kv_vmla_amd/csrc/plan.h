@@ -35,10 +35,11 @@ struct Plan {
   void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV
   float *part_o; // [2G][kAttnMaxRows][dc] unnormalised partial outputs
   float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
+  void *vtiles;  // transposed value-tile images of the visible keys (per call)
 };
 
 struct WorkspaceLayout {
-  size_t stage, cq, qnope, qt, olat, o, part_o, part_ml, total;
+  size_t stage, cq, qnope, qt, olat, o, part_o, part_ml, vtiles, total;
 };
 
 WorkspaceLayout workspace_layout(const Plan& p);
@@ -63,11 +64,14 @@ struct AttnCall {
   void* out;
   float* part_o;
   float* part_ml;
+  void* vtiles;
   long cache_bstride, stage_bstride;  // elements
   int B, R, n_ring, n_stage;
   int G;
 };
 hipError_t run_latent_attention(const AttnCall& a, hipStream_t s);
 bool latent_attention_supported(DType dt, int dc, int dr);
+// Workspace bytes of the transposed value-tile images for up to max_keys keys.
+size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_keys);
 
 }  // namespace vmla

@@ -1,7 +1,7 @@
 // Host runtime of libvmla.so: config validation, ring-buffer metadata,
 // workspace carve-up and the C ABI declared in include/vmla.h.  Every check
 // runs before anything is enqueued; only run_compress / run_attend touch HIP.
-#include "../../include/vmla.h"
+#include "vmla.h"
 
 #include <math.h>
 #include <new>
@@ -105,6 +105,7 @@ WorkspaceLayout workspace_layout(const Plan& p) {
   L.o = take(M * p.nh * (size_t)p.dv * es);
   L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * sizeof(float));
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
+  L.vtiles = take(latent_value_tiles_bytes(p.dtype, p.dc, p.dr, p.B, p.W * p.Tpf + p.Nq));
   L.total = off;
   return L;
 }
@@ -184,6 +185,7 @@ static Plan make_plan(const vmla_ctx* c) {
   p.o = ws + L.o;
   p.part_o = reinterpret_cast<float*>(ws + L.part_o);
   p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  p.vtiles = ws + L.vtiles;
   return p;
 }
 

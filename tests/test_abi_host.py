@@ -31,6 +31,12 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, s), f"{s} declared but not exported"
 
 
+def test_library_resolves_every_symbol_at_load():
+    """Eager binding: a kernel whose host launch stub was not emitted shows up as
+    an undefined symbol here instead of on first use."""
+    ctypes.CDLL(vmla.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_status_strings_and_codes():
     assert vmla.STATUS["VMLA_OK"] == 0
     assert len(set(vmla.STATUS.values())) == len(vmla.STATUS)
