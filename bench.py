@@ -218,7 +218,7 @@ def main():
                    "attends_per_step": args.steps_per_chunk, "appends_per_step": 1},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_from_counters(),
-                     "kernel": "latent_attn_kernel (+ split combine)",
+                     "kernel": "latent_attn_kernel",
                      "flops_per_launch": flops_attn, "avg_launch_ms": attn_avg},
         "attend_call_tflops": call_flops * args.steps_per_chunk / (ms_per_step * 1e-3) / 1e12,
         "wall_s_timed_region": wall,

@@ -141,9 +141,10 @@ VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stre
 VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream);
 
 /* Same as vmla_attend, and additionally records attn_start on the stream right
- * before the latent-attention kernels and attn_stop right after them, so a caller
- * can time the dominant kernels of the call with hipEventElapsedTime.  Both
- * events must be created by the caller (hipEventCreate); NULL -> VMLA_ERR_NULL. */
+ * before the latent-attention kernel (the call's dominant kernel) and attn_stop
+ * right after it, so a caller can time that kernel with hipEventElapsedTime.
+ * Both events must be created by the caller (hipEventCreate); NULL ->
+ * VMLA_ERR_NULL. */
 VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEvent_t attn_start,
                                   hipEvent_t attn_stop, hipStream_t stream);
 

@@ -456,7 +456,10 @@ static hipError_t launch_latent(const AttnCall& c, hipStream_t s) {
   const long I = (long)a.B * a.RB * a.KT;
   a.G = (int)(c.G < I ? c.G : I);
   latent_value_tiles<T, DC, DR, KTILE><<<dim3(a.KT, a.B), 256, 0, s>>>(a);
+  hipError_t err;
+  if (c.ev_start && (err = hipEventRecord(c.ev_start, s)) != hipSuccess) return err;
   latent_attn_kernel<T, DC, DR, KTILE, NW, NB><<<a.G, NW * 64, 0, s>>>(a);
+  if (c.ev_stop && (err = hipEventRecord(c.ev_stop, s)) != hipSuccess) return err;
   if (I != (long)a.G * a.KT)
     latent_attn_combine<T, DC, ROWS><<<a.B * a.RB * (ROWS / 16), 256, 0, s>>>(a);
   return hipGetLastError();

@@ -207,10 +207,10 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
     a.n_ring = (int)((n < p.W ? n : p.W) * p.Tpf);
     a.n_stage = p.Nq;
     a.G = p.G;
-    if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+    a.ev_start = ev0;
+    a.ev_stop = ev1;
     err = run_latent_attention(a, s);
     if (err != hipSuccess) return err;
-    if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
   }
   {  // o_h = W_UV^h o~_h (z = head)
     EpiStore<T> e{static_cast<T*>(p.o), (long)p.nh * p.dv, p.dv};

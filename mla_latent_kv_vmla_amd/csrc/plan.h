@@ -65,6 +65,7 @@ struct AttnCall {
   float* part_o;
   float* part_ml;
   void* vtiles;
+  hipEvent_t ev_start, ev_stop;       // optional: recorded around the attention kernel itself
   long cache_bstride, stage_bstride;  // elements
   int B, R, n_ring, n_stage;
   int G;
