@@ -31,23 +31,30 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (for fp32 workloads)
 PEAK_HBM_GBS = 8000.0
 METRIC = "query tokens/s and MFMA TFLOP/s (% peak) per layer, Wan-1.3B latent attn"
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "latent_attn_wan_layer_pmc.json")
 ATTN_SOURCE = os.path.join(ROOT, "mla_latent_kv_vmla_amd", "csrc", "attention.hip")
 
 
+def is_dense(g) -> bool:
+    return g.d_c == 0
+
+
 def attention_flops(g, n_frames: int) -> float:
-    """Algorithmic FLOPs of one latent-attention launch: per (query row, key)
-    2*(d_c+d_r) for the score and 2*d_c for the value sum."""
+    """Algorithmic FLOPs of one attention launch: per (query row, key) 2*(d_c+d_r)
+    for the score and 2*d_c for the value sum (latent), or 2*d_h + 2*d_v (dense)."""
     rows = g.batch * g.n_q * g.n_heads
-    return rows * g.n_k(n_frames) * (2.0 * (g.d_c + g.d_rope) + 2.0 * g.d_c)
+    per = 2.0 * g.head_dim + 2.0 * g.d_v if is_dense(g) else 2.0 * (g.d_c + g.d_rope) + 2.0 * g.d_c
+    return rows * g.n_k(n_frames) * per
 
 
 def attend_call_flops(g, n_frames: int) -> float:
-    """All algorithmic FLOPs of one vmla_attend call (projections + attention)."""
+    """All algorithmic FLOPs of one attend call (projections + attention)."""
     M = g.batch * g.n_q
     d, nh = g.hidden, g.n_heads
-    gemm = 2.0 * M * (d * (g.d_c + g.d_rope) + d * g.d_q + g.d_q * nh * g.head_dim
-                      + nh * g.d_nope * g.d_c + nh * g.d_c * g.d_v + nh * g.d_v * d)
+    if is_dense(g):
+        gemm = 2.0 * M * d * nh * (2 * g.head_dim + g.d_v) + 2.0 * M * nh * g.d_v * d
+    else:
+        gemm = 2.0 * M * (d * (g.d_c + g.d_rope) + d * g.d_q + g.d_q * nh * g.head_dim
+                          + nh * g.d_nope * g.d_c + nh * g.d_c * g.d_v + nh * g.d_v * d)
     return gemm + attention_flops(g, n_frames)
 
 
@@ -75,11 +82,15 @@ class HipEvents:
         self.h.hipEventDestroy(e)
 
 
-def traffic_from_counters():
+def pmc_summary_path(g) -> str:
+    return os.path.join(ROOT, "profiles", f"attn_{g.name}_pmc.json")
+
+
+def traffic_from_counters(g):
     """HBM bytes per launch of the attention kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+    counter summary of this workload, if it was taken on the current kernel source."""
     try:
-        s = json.load(open(PMC_SUMMARY))
+        s = json.load(open(pmc_summary_path(g)))
         sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
         if s.get("attention_source_sha256") == sha:
             return s.get("hbm_bytes_per_launch")
@@ -93,6 +104,7 @@ def cpu_baseline(g, w, hist, n, x, sample_tokens: int):
     tokens of the same call; returns query tokens/s of the sample."""
     import numpy as np
     from oracle import mla
+    attend = mla.attend_dense if is_dense(g) else mla.attend
     threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -101,7 +113,7 @@ def cpu_baseline(g, w, hist, n, x, sample_tokens: int):
         pass
     q = np.arange(sample_tokens)
     t0 = time.perf_counter()
-    mla.attend(g, w, hist, n, x, query_tokens=q)
+    attend(g, w, hist, n, x, query_tokens=q)
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "query tokens/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
@@ -137,8 +149,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dt = vmla.torch_dtype(g)
-    w = wl.latent_weights(g, mode="literal")
-    layer = vmla.LatentAttention(g, {k: torch.from_numpy(v) for k, v in w.as_dict().items()})
+    if is_dense(g):
+        w = wl.dense_weights(g, mode="literal")
+        layer = vmla.DenseAttention(g, {k: torch.from_numpy(v) for k, v in vars(w).items()})
+        attend_profiled, append = vmla.vmla_dense_attend_profiled, vmla.vmla_dense_append
+        kernel = "flash_attn_kernel (dense, per-head K/V)"
+    else:
+        w = wl.latent_weights(g, mode="literal")
+        layer = vmla.LatentAttention(g, {k: torch.from_numpy(v) for k, v in w.as_dict().items()})
+        attend_profiled, append = vmla.vmla_attend_profiled, vmla.vmla_compress_append
+        kernel = "flash_attn_kernel (latent, absorbed)"
     hist = {}
     for k in range(g.prefill_chunks):
         xk = wl.hidden_states(g, chunk=k)
@@ -161,8 +181,8 @@ def main():
     def step(i):
         for s in range(args.steps_per_chunk):
             a, b = ev_pairs[i * args.steps_per_chunk + s]
-            vmla.vmla_attend_profiled(layer.ctx, xs[s], out, a, b, sh)
-        vmla.vmla_compress_append(layer.ctx, xs[-1], sh)
+            attend_profiled(layer.ctx, xs[s], out, a, b, sh)
+        append(layer.ctx, xs[-1], sh)
 
     for i in range(args.warmup):
         step(i)
@@ -213,12 +233,13 @@ def main():
         "dtype": "f32" if g.dtype == wl.F32 else "bf16",
         "data": "synthetic (seeded N(0,1)/sqrt(fan_in) weights and hidden states)",
         "config": {"workload": g.name, "batch": g.batch, "query_tokens_per_call": g.n_q,
-                   "keys_per_call": g.n_k(n_frames), "heads": g.n_heads, "d_c": g.d_c, "d_rope": g.d_rope,
+                   "keys_per_call": g.n_k(n_frames), "heads": g.n_heads, "head_dim": g.head_dim,
+                   "d_c": g.d_c, "d_rope": g.d_rope,
                    "window_frames": g.window_frames, "chunk_frames": g.chunk_frames,
                    "attends_per_step": args.steps_per_chunk, "appends_per_step": 1},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_from_counters(),
-                     "kernel": "latent_attn_kernel",
+                     "frac": achieved / peak, "traffic": traffic_from_counters(g),
+                     "kernel": kernel,
                      "flops_per_launch": flops_attn, "avg_launch_ms": attn_avg},
         "attend_call_tflops": call_flops * args.steps_per_chunk / (ms_per_step * 1e-3) / 1e12,
         "wall_s_timed_region": wall,

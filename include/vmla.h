@@ -165,6 +165,71 @@ VMLA_API int vmla_reset(vmla_ctx* ctx);
 /* Free a ctx (host memory only).  NULL is ignored. */
 VMLA_API void vmla_destroy(vmla_ctx* ctx);
 
+/*
+ * Dense per-head baseline (paper section 1 and appendix C.1: the layer VideoMLA
+ * replaces, whose cache holds every head's key and value, n_heads*2*d_h scalars
+ * per token).  Same chunk-causal window, ring eviction and 3D-RoPE as the
+ * latent layer; per head h and token x:
+ *   q_h = RoPE(W_Q^h x), k_h = RoPE(W_K^h x) (all d_h channels rotated, pairs
+ *   (2p, 2p+1), axis order t, h, w), v_h = W_V^h x,
+ *   o_h = softmax(q_h k_h^T / sqrt(d_h)) v_h, out = W_O [o_1; ...; o_H].
+ * It takes the same vmla_config, read this way: d_rope = d_h (the rotated
+ * per-head width; rope_pairs_* split its d_h/2 pairs), d_v = value width, and
+ * d_nope = d_c = d_q = 0 (else VMLA_ERR_CONFIG).  Built kernels (else
+ * VMLA_ERR_UNSUPPORTED): bf16 with d_rope = d_v = 128.
+ *
+ * Weights (Linear layout, bf16):
+ *   w_q, w_k [n_heads*d_rope, hidden]; w_v [n_heads*d_v, hidden];
+ *   w_o [hidden, n_heads*d_v].
+ *
+ * Cache layout (vmla_dense_cache_bytes), P = window_frames*T rounded up to a
+ * multiple of 64:
+ *   keys   [batch][n_heads][P][d_rope] bf16, rotated with the absolute frame index;
+ *   values [batch][n_heads][d_v][P] fp16, transposed: the value of ring key j
+ *          (frame f in slot f % window_frames, key j = slot*T + s) sits in
+ *          column j with bits 2 and 3 of j swapped; columns past the valid
+ *          keys (up to the next multiple of 64) are kept at zero by the library.
+ * The values are stored as fp16 so the value product runs on fp16 operands
+ * (the bf16 rounding of probabilities near 1 is too coarse, see the latent
+ * path); the cache size equals the bf16 one.
+ */
+typedef struct vmla_dense_weights {
+  const void *w_q, *w_k, *w_v, *w_o;
+} vmla_dense_weights;
+
+typedef struct vmla_dense_ctx vmla_dense_ctx; /* opaque; host-side metadata only */
+
+/* Bytes of the dense ring cache (layout above); 0 for an invalid config. */
+VMLA_API size_t vmla_dense_cache_bytes(const vmla_config* cfg);
+
+/* Bytes of scratch device memory a dense ctx needs (rotated queries, the
+ * chunk's keys and values, attention output, partial softmax states). */
+VMLA_API size_t vmla_dense_workspace_bytes(const vmla_config* cfg);
+
+/* Create a dense ctx over caller-owned memory; same rules as vmla_create
+ * (rope_freqs: d_rope/2 floats or NULL for theta^(-2i/(2p_a)) per axis). */
+VMLA_API int vmla_dense_create(const vmla_config* cfg, const vmla_dense_weights* w, void* cache,
+                               void* workspace, const float* rope_freqs, vmla_dense_ctx** out);
+
+/* Append one chunk (x [batch, C*T, hidden]): keys and values of frames
+ * n..n+C-1 into their ring slots, evicting the oldest frames; n += C. */
+VMLA_API int vmla_dense_append(vmla_dense_ctx* ctx, const void* x, hipStream_t stream);
+
+/* Attend one chunk (x, out [batch, C*T, hidden]) against the cached frames
+ * [max(0, n-W), n) and the chunk itself; the cache and n are unchanged. */
+VMLA_API int vmla_dense_attend(vmla_dense_ctx* ctx, const void* x, void* out, hipStream_t stream);
+
+/* vmla_dense_attend plus caller-made events recorded right before and right
+ * after the attention kernel (NULL -> VMLA_ERR_NULL). */
+VMLA_API int vmla_dense_attend_profiled(vmla_dense_ctx* ctx, const void* x, void* out,
+                                        hipEvent_t attn_start, hipEvent_t attn_stop, hipStream_t stream);
+
+/* As vmla_cache_state / vmla_reset / vmla_destroy, for a dense ctx. */
+VMLA_API int vmla_dense_cache_state(const vmla_dense_ctx* ctx, int64_t* frames_appended,
+                                    int64_t* first_valid_frame, int32_t* n_valid_frames);
+VMLA_API int vmla_dense_reset(vmla_dense_ctx* ctx);
+VMLA_API void vmla_dense_destroy(vmla_dense_ctx* ctx);
+
 /* Static description of a status code. */
 VMLA_API const char* vmla_status_string(int status);
 

@@ -1,38 +1,44 @@
-// Flash-style absorbed latent attention for gfx950.
-//
-// Every query row (token, head) of a chunk attends to the same keys: the cache
-// rows [c | k_r] of the visible frames followed by the chunk's own rows
-// (VideoMLA paper, appendix D.4: chunk-causal, the whole chunk and the whole
-// window are visible).  With the per-head key and value lifts absorbed
-// (score = q~ . [c | k_r], output = sum p * c, lifted by W_UV afterwards), all
-// heads share one [c | k_r] key tile and one c value tile, so each tile is
-// staged in LDS once per workgroup and reused by all of its query rows.
+// Flash-style attention for gfx950 over a chunk's visible keys, used by both
+// layer types the library runs:
+//   latent (absorbed) attention: every query row (token, head) scores the
+//     head-shared cache rows [c | k_r] and sums c (VideoMLA paper, section 3.3;
+//     the per-head key and value lifts are absorbed into the query and applied
+//     to the output), so all heads share one key tile and one value tile;
+//   dense per-head attention: the baseline of the paper's section 1 and
+//     appendix C.1, per-head key rows and per-head values.
+// Every chunk query sees every key of the window and of its own chunk
+// (appendix D.4: chunk-causal, no mask inside the chunk or the window).  The
+// keys come in two segments: segment 0 holds the ring rows of the cached frames
+// in slot order (softmax does not depend on key order), segment 1 the chunk's
+// own rows.  Each segment is tiled on its own; keys past a segment's end are
+// masked.
 //
 // Work layout (one workgroup = NW waves, 32*NB query rows per wave):
-//   S^T[key][row]  = K_tile[key][:] . Qt[row][:]      (32x32x16 MFMA, keys as MFMA rows)
-//   O^T[f][row]   += C^T[f][key] * P^T[key][row]     (the S^T accumulator is already
+//   S^T[key][row]  = K_tile[key][:] . Q[row][:]       (32x32x16 MFMA, keys as MFMA rows)
+//   O^T[f][row]   += V^T[f][key] * P^T[key][row]      (the S^T accumulator is already
 //                                                      the B operand of this product)
 // so softmax statistics live per lane (one query row per lane pair) and P never
 // leaves registers.
 //
 // Staging.  A key tile lives in LDS twice: row-major [key][D] (storage type) for
-// the score product, and transposed [channel][key] for the value product.  The
-// row-major copy is loaded straight from the cache / chunk rows with LDS-DMA
-// loads (global_load_lds_dwordx4: lane L's 16 bytes land at M0 + 16 L), and the
-// transposed copy is an image that a pre-pass kernel builds once per call in the
-// workspace, already in LDS layout, so staging needs no registers and no VALU.
+// the score product, and transposed [channel][key] for the value product.  Both
+// are copied with LDS-DMA loads (global_load_lds_dwordx4: lane L's 16 bytes land
+// at M0 + 16 L), so staging needs no registers and no VALU.  The transposed tile
+// comes either from images a pre-pass builds once per call in the workspace,
+// already in LDS layout (latent: the value is the key's first DV channels), or
+// straight from value rows [f][key] that the dense cache stores transposed.
 // LDS layouts (per stage; two stages in two distinct arrays):
 //   Ks  [KTILE][D + 16 B]: 16-B chunk q of row r lives at chunk q ^ ((r >> 4) & 3)
-//   C^T [DCP][KTILE + 16 B]: within every 16-key group the key index has bits 2
+//   V^T [DVP][KTILE + 16 B]: within every 16-key group the key index has bits 2
 //       and 3 swapped, so the 8 keys a lane feeds to one value MFMA are one
 //       contiguous 16-B read.  Both layouts read without bank conflicts.
 //
-// Numerics.  With bf16 storage the value product runs on fp16 operands: the
-// transposed image holds the latents converted bf16 -> fp16 (exact for
-// magnitudes in fp16's normal range, below 65504) and P is rounded to fp16.  When
-// the softmax is nearly flat every probability sits just below 1, where bf16's
-// spacing (2^-8) exceeds the spread of the probabilities themselves; fp16's
-// spacing there is 2^-11, at the same MFMA rate.
+// Numerics.  With bf16 storage the value product runs on fp16 operands: values
+// are held as fp16 (latents converted bf16 -> fp16 by the pre-pass, exact in
+// fp16's normal range; the dense cache stores V as fp16) and P is rounded to
+// fp16.  When the softmax is nearly flat every probability sits just below 1,
+// where bf16's spacing (2^-8) exceeds the spread of the probabilities
+// themselves; fp16's spacing there is 2^-11, at the same MFMA rate.
 //
 // Scheduling is stream-K over (stream, row block, key tile): workgroup w owns
 // iterations [w*I/G, (w+1)*I/G).  A row block finished by one workgroup is
@@ -48,71 +54,87 @@
 
 namespace vmla {
 
-template <typename T> struct AttnArgs {
-  const T* qt;     // [B][R][D]
-  const T* cache;  // [B][.][D]
-  const T* stage;  // [B][n_stage][D]
-  T* out;          // [B][R][DC]
-  float* part_o;   // [2G][kAttnMaxRows][DC]
-  float* part_ml;  // [2G][kAttnMaxRows][2]
-  void* vtiles;    // [B][KT] value-tile images
-  long cbs, sbs;
-  int R, n_ring, n_keys, RB, KT, B, G;
+// One attention launch.  Stream s (0..S-1) is an independent attention problem:
+// a batch stream for latent attention (rows = token*heads + head), a (batch
+// stream, head) pair for dense attention (rows = tokens).
+template <typename T> struct FlashArgs {
+  const T* q;               // row r of stream s: q + s*q_ss + r*D
+  long q_ss;
+  const T* key0;            // ring segment: key k of stream s at key0 + s*key_ss0 + k*D
+  const T* key1;            // chunk segment
+  long key_ss0, key_ss1;
+  const void* val0;         // value rows [f][key] (fp16 for bf16 storage) of the ring segment,
+  const void* val1;         //   of the chunk segment; or the per-call value-tile images (val0)
+  long val_ss0, val_ss1;    // elements per stream
+  int val_rs0, val_rs1;     // elements per value row
+  T* out;                   // row r of stream s: out + (s/heads)*out_so + (s%heads)*out_sh + r*out_rs
+  long out_so, out_sh, out_rs;
+  int heads;
+  float* part_o;            // [2G][kAttnMaxRows][DV]
+  float* part_ml;           // [2G][kAttnMaxRows][2]
+  int len0, len1, tiles0;   // keys per segment, key tiles of segment 0
+  int R, RB, KT, S, G;      // rows per stream, row blocks per stream, key tiles, streams, workgroups
 };
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
 
-// Compile-time geometry of one instantiation.
-template <typename T, int DC, int DR, int KTILE> struct TileGeo {
+// Compile-time geometry of one instantiation: score width D, value width DV.
+template <typename T, int D_, int DV, int KTILE> struct TileGeo {
   using VT = typename std::conditional<sizeof(T) == 2, f16, float>::type;  // value-product operand
   static_assert(sizeof(VT) == sizeof(T), "tile sizing assumes equal widths");
-  static constexpr int D = DC + DR;
-  static constexpr int DCP = (DC + 31) / 32 * 32;
+  static constexpr int D = D_;
+  static constexpr int DVP = (DV + 31) / 32 * 32;
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-B chunk
   static constexpr int KS = D + VEC;               // row-major tile row (+16 B)
   static constexpr int CS = KTILE + VEC;           // transposed tile row (+16 B)
   static constexpr int KCH = KS / VEC;             // 16-B chunks per row-major row
   static constexpr int CCH = CS / VEC;             // 16-B chunks per transposed row
   static constexpr int KPOS = KTILE * KCH;         // chunks of the row-major tile
-  static constexpr int CPOS = DCP * CCH;           // chunks of the transposed tile
+  static constexpr int CPOS = DVP * CCH;           // chunks of the transposed tile
   static constexpr int KS_EL = KTILE * KS;
-  static constexpr int BUF_EL = KS_EL + DCP * CS;
+  static constexpr int BUF_EL = KS_EL + DVP * CS;
   static constexpr int KI = (KPOS + 63) / 64;      // wave-wide 1-KB loads per stage
   static constexpr int CI = (CPOS + 63) / 64;
   static constexpr size_t IMG_BYTES = (size_t)CPOS * 16;
-  static_assert(DC % VEC == 0 && DR % VEC == 0, "unsupported widths");
+  static_assert(D % VEC == 0 && DV % VEC == 0 && DV <= D, "unsupported widths");
   static_assert((D / VEC) % 4 == 0, "chunk swizzle works within groups of 4 chunks");
-  static_assert(KTILE % 32 == 0, "bad tile");
+  static_assert(KTILE % 32 == 0 && KTILE / VEC < 256, "bad tile");
   __device__ static int perm_group(int kg) { return (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1); }
 };
 
-// Key row `key` of stream b, clamped to the last valid key (rows past n_keys
-// are masked out of the scores, so their contents never matter): ring rows
-// first, then the chunk's staged rows.
-template <typename T, int D>
-__device__ inline const T* key_row(const AttnArgs<T>& p, int b, int key) {
-  key = key < p.n_keys ? key : p.n_keys - 1;
-  return key < p.n_ring ? p.cache + (long)b * p.cbs + (long)key * D
-                        : p.stage + (long)b * p.sbs + (long)(key - p.n_ring) * D;
+// Segment of key tile t: (segment, first key, keys in the segment).
+template <typename T, int KTILE>
+__device__ inline void tile_segment(const FlashArgs<T>& p, int t, int& g, int& kbase, int& len) {
+  g = t >= p.tiles0 ? 1 : 0;
+  kbase = (t - (g ? p.tiles0 : 0)) * KTILE;
+  len = g ? p.len1 : p.len0;
 }
 
-// Pre-pass: transposed value-tile images.  Image (b, t) holds, for the keys of
-// tile t, rows = latent channels (zero rows pad DC up to a multiple of 32) in the
-// value-operand type, keys permuted within 16-key groups.
-template <typename T, int DC, int DR, int KTILE>
-__global__ __launch_bounds__(256) void latent_value_tiles(AttnArgs<T> p) {
-  using G = TileGeo<T, DC, DR, KTILE>;
+// Pre-pass (latent attention): transposed value-tile images.  Image (s, t)
+// holds, for the keys of tile t, rows = the first DV key channels (zero rows
+// pad DV up to a multiple of 32) in the value-operand type, keys permuted
+// within 16-key groups.  Keys past the segment's end repeat its last key
+// (their probabilities are zero).
+template <typename T, int D, int DV, int KTILE>
+__global__ __launch_bounds__(256) void latent_value_tiles(FlashArgs<T> p) {
+  using G = TileGeo<T, D, DV, KTILE>;
   using VT = typename G::VT;
-  constexpr int KG = KTILE / 4, CV = DC / G::VEC;
-  const int t = blockIdx.x, b = blockIdx.y;
-  VT* img = reinterpret_cast<VT*>(static_cast<char*>(p.vtiles) + ((size_t)b * p.KT + t) * G::IMG_BYTES);
+  constexpr int KG = KTILE / 4, CV = DV / G::VEC;
+  const int t = blockIdx.x, s = blockIdx.y;
+  int g, kbase, len;
+  tile_segment<T, KTILE>(p, t, g, kbase, len);
+  const T* keys = g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0;
+  VT* img = reinterpret_cast<VT*>(const_cast<void*>(p.val0)) + ((size_t)s * p.KT + t) * (G::IMG_BYTES / sizeof(VT));
   for (int v = threadIdx.x; v < KG * CV; v += 256) {
     const int kg = v % KG, c = v / KG;
     u32x4 k[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) k[j] = ld16(key_row<T, G::D>(p, b, t * KTILE + 4 * kg + j) + c * G::VEC);
+    for (int j = 0; j < 4; ++j) {
+      const int key = min(kbase + 4 * kg + j, len - 1);
+      k[j] = ld16(keys + (long)key * D + c * G::VEC);
+    }
     const int pcol = 4 * G::perm_group(kg);
 #pragma unroll
     for (int e = 0; e < G::VEC; ++e) {
@@ -131,25 +153,29 @@ __global__ __launch_bounds__(256) void latent_value_tiles(AttnArgs<T> p) {
       }
     }
   }
-  for (int i = threadIdx.x; i < (G::DCP - DC) * G::CS; i += 256) img[DC * G::CS + i] = VT(0.f);
+  for (int i = threadIdx.x; i < (G::DVP - DV) * G::CS; i += 256) img[DV * G::CS + i] = VT(0.f);
 }
 
-template <typename T, int DC, int DR, int KTILE, int NW, int NB>
+// VROWS = false: the transposed tile is copied from the pre-pass images (val0);
+// VROWS = true: from value rows val0/val1 ([f][key], keys permuted within
+// 16-key groups, zero past the segment's end up to the tile boundary).
+template <typename T, int D, int DV, int KTILE, int NW, int NB, bool VROWS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(8 / NW, 8 / NW)))
-void latent_attn_kernel(AttnArgs<T> p) {
-  using G = TileGeo<T, DC, DR, KTILE>;
+void flash_attn_kernel(FlashArgs<T> p) {
+  using G = TileGeo<T, D, DV, KTILE>;
   using VT = typename G::VT;
   using MF = Mfma<T>;
   constexpr bool HALF = sizeof(T) == 2;
   constexpr int KPL = MF::KPL;
-  constexpr int D = G::D, DCP = G::DCP, VEC = G::VEC, KS = G::KS, CS = G::CS;
+  constexpr int DVP = G::DVP, VEC = G::VEC, KS = G::KS, CS = G::CS;
   constexpr int RW = 32 * NB;               // query rows per wave
   constexpr int NKS = D / (2 * KPL);
   constexpr int NKB = KTILE / 32;
-  constexpr int NFB = DCP / 32;
+  constexpr int NFB = DVP / 32;
   constexpr int NI = G::KI + G::CI;         // 1-KB loads per stage, spread over the waves
   constexpr int NI_W = (NI + NW - 1) / NW;
   static_assert(NW * RW <= kAttnMaxRows, "row block too large");
+  static_assert(!VROWS || DV % 32 == 0, "value rows need whole 32-channel blocks");
 
   __shared__ __attribute__((aligned(16))) T lds0[G::BUF_EL];
   __shared__ __attribute__((aligned(16))) T lds1[G::BUF_EL];
@@ -158,51 +184,73 @@ void latent_attn_kernel(AttnArgs<T> p) {
   const int l32 = lane & 31, h32 = lane >> 5;
   const float NEG_INF = -__builtin_huge_valf();
 
-  // Row-major staging: for each of this wave's loads, the (row, chunk) whose
-  // swizzled LDS position is this lane's slot, packed as row << 12 | element offset.
-  int kslot[NI_W];
+  // This lane's source in each of this wave's LDS-DMA loads of a stage, as an
+  // element offset from the tile's base: row-major key tile (row r, swizzled
+  // chunk) packed as r << 12 | offset in the row; value rows (channel f, chunk)
+  // packed as f << 8 | offset in the row; images: byte offset.
+  uint32_t slot[NI_W];
 #pragma unroll
   for (int k = 0; k < NI_W; ++k) {
-    const int pos = (wave + k * NW) * 64 + lane;
-    const int r = pos / G::KCH, phys = pos % G::KCH;
-    const int q = phys < G::KCH - 1 ? (phys ^ ((r >> 4) & 3)) : 0;  // pad slot: any valid chunk
-    kslot[k] = (r << 12) | (q * VEC);
+    const int idx = wave + k * NW;
+    if (idx < G::KI) {
+      const int pos = idx * 64 + lane;
+      const int r = pos / G::KCH, phys = pos % G::KCH;
+      const int q = phys < G::KCH - 1 ? (phys ^ ((r >> 4) & 3)) : 0;  // pad slot: any valid chunk
+      slot[k] = ((uint32_t)r << 12) | (uint32_t)(q * VEC);
+    } else {
+      const int pos = (idx - G::KI) * 64 + lane;
+      if constexpr (VROWS) {
+        const int f = pos / G::CCH, c = pos % G::CCH;
+        slot[k] = ((uint32_t)f << 8) | (uint32_t)((c < G::CCH - 1 ? c : 0) * VEC);
+      } else {
+        slot[k] = (uint32_t)pos * 16u;
+      }
+    }
   }
 
-  // Issue the LDS-DMA loads of tile kt (both layouts) into stage `buf`.
-  auto issue_tile = [&](int b, int kt, T* buf) {
-    const int kbase = kt * KTILE;
-    const T* base = nullptr;
-    if (kbase + KTILE <= p.n_ring) base = p.cache + (long)b * p.cbs + (long)kbase * D;
-    else if (kbase >= p.n_ring && kbase + KTILE <= p.n_keys)
-      base = p.stage + (long)b * p.sbs + (long)(kbase - p.n_ring) * D;
-    const char* img = static_cast<const char*>(p.vtiles) + ((size_t)b * p.KT + kt) * G::IMG_BYTES;
+  // Issue the LDS-DMA loads of tile t of stream s (both layouts) into stage `buf`.
+  auto issue_tile = [&](int s, int t, T* buf) {
+    int g, kbase, len;
+    tile_segment<T, KTILE>(p, t, g, kbase, len);
+    const char* kb = reinterpret_cast<const char*>(g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0);
+    const char* vb;
+    int vrs = 0;
+    if constexpr (VROWS) {
+      vb = static_cast<const char*>(g ? p.val1 : p.val0) + ((g ? p.val_ss1 : p.val_ss0) * s + kbase) * sizeof(VT);
+      vrs = g ? p.val_rs1 : p.val_rs0;
+    } else {
+      vb = static_cast<const char*>(p.val0) + ((size_t)s * p.KT + t) * G::IMG_BYTES;
+    }
 #pragma unroll
     for (int k = 0; k < NI_W; ++k) {
       const int idx = wave + k * NW;  // wave-uniform
       if (idx < G::KI) {
         const int pos = idx * 64 + lane;
         if (G::KPOS % 64 == 0 || pos < G::KPOS) {
-          const int r = kslot[k] >> 12, off = kslot[k] & 0xFFF;
-          const T* src = base ? base + r * D + off : key_row<T, D>(p, b, kbase + r) + off;
-          lds_dma16(src, buf + idx * 64 * VEC);
+          const int r = min(kbase + (int)(slot[k] >> 12), len - 1);
+          const uint32_t off = ((uint32_t)r * D + (slot[k] & 0xFFFu)) * (uint32_t)sizeof(T);
+          lds_dma16(kb + off, buf + idx * 64 * VEC);
         }
       } else if (idx < NI) {
         const int ci = idx - G::KI, pos = ci * 64 + lane;
-        if (G::CPOS % 64 == 0 || pos < G::CPOS)
-          lds_dma16(img + (size_t)pos * 16, buf + G::KS_EL + ci * 64 * VEC);
+        if (G::CPOS % 64 == 0 || pos < G::CPOS) {
+          uint32_t off;
+          if constexpr (VROWS) off = ((slot[k] >> 8) * (uint32_t)vrs + (slot[k] & 0xFFu)) * (uint32_t)sizeof(VT);
+          else off = slot[k];
+          lds_dma16(vb + off, buf + G::KS_EL + ci * 64 * VEC);
+        }
       }
     }
   };
 
-  const long I = (long)p.B * p.RB * p.KT;
+  const long I = (long)p.S * p.RB * p.KT;
   const long it0 = (long)blockIdx.x * I / p.G, it1 = (long)(blockIdx.x + 1) * I / p.G;
 
   for (long it = it0; it < it1;) {
     const long unit = it / p.KT;
     const int kt0 = (int)(it % p.KT);
     const int kt1 = (int)((long)kt0 + (it1 - it) < p.KT ? (long)kt0 + (it1 - it) : p.KT);
-    const int b = (int)(unit / p.RB), rb = (int)(unit % p.RB);
+    const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
     const bool first_piece = (it == it0);
     const int row0 = rb * (NW * RW) + wave * RW;
 
@@ -210,7 +258,7 @@ void latent_attn_kernel(AttnArgs<T> p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int qrow = row0 + 32 * nb + l32;
-      const T* qsrc = p.qt + ((long)b * p.R + qrow) * D + KPL * h32;
+      const T* qsrc = p.q + s * p.q_ss + (long)qrow * D + KPL * h32;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) qf[nb][ks] = qrow < p.R ? MF::load(qsrc + ks * 2 * KPL) : MF::zero();
     }
@@ -225,16 +273,17 @@ void latent_attn_kernel(AttnArgs<T> p) {
     }
 
     // all query-row blocks of one tile held in `cur`
-    auto compute = [&](int kt, const T* cur) {
+    auto compute = [&](int t, const T* cur) {
+      int g, kbase, len;
+      tile_segment<T, KTILE>(p, t, g, kbase, len);
       const T* Ks = cur;
       const VT* Ct = reinterpret_cast<const VT*>(cur + G::KS_EL) + l32 * CS;
-      const int kbase = kt * KTILE;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         // S^T for 32 keys x RW query rows; each K fragment feeds NB MFMAs
-        f32x16 s[NB];
+        f32x16 sc[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+        for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
         const int r = 32 * kb + l32;
         if constexpr (HALF) {  // chunk 2ks+h, swizzled: two per-lane bases, immediate offsets
           const int sw = (r >> 4) & 3;
@@ -244,7 +293,7 @@ void latent_attn_kernel(AttnArgs<T> p) {
           for (int ks = 0; ks < NKS; ++ks) {
             const auto a = MF::load((ks & 1 ? b1 : b0) + 4 * VEC * (ks >> 1));
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) s[nb] = MF::mma(a, qf[nb][ks], s[nb]);
+            for (int nb = 0; nb < NB; ++nb) sc[nb] = MF::mma(a, qf[nb][ks], sc[nb]);
           }
         } else {
 #pragma unroll
@@ -252,15 +301,15 @@ void latent_attn_kernel(AttnArgs<T> p) {
             const int e = ks * 2 * KPL + KPL * h32;
             const auto a = MF::load(&Ks[r * KS + (((e / VEC) ^ ((r >> 4) & 3)) * VEC) + e % VEC]);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) s[nb] = MF::mma(a, qf[nb][ks], s[nb]);
+            for (int nb = 0; nb < NB; ++nb) sc[nb] = MF::mma(a, qf[nb][ks], sc[nb]);
           }
         }
-        if (kbase + 32 * kb + 32 > p.n_keys) {
+        if (kbase + 32 * kb + 32 > len) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr)
-            if (kbase + 32 * kb + 8 * (rr >> 2) + 4 * h32 + (rr & 3) >= p.n_keys)
+            if (kbase + 32 * kb + 8 * (rr >> 2) + 4 * h32 + (rr & 3) >= len)
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) s[nb][rr] = NEG_INF;
+              for (int nb = 0; nb < NB; ++nb) sc[nb][rr] = NEG_INF;
         }
         // online softmax per query row (lane pair); every piece's first block
         // holds a valid key, so m_run is finite before any all-masked block
@@ -268,9 +317,9 @@ void latent_attn_kernel(AttnArgs<T> p) {
         float mx[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          float m = s[nb][0];
+          float m = sc[nb][0];
 #pragma unroll
-          for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, s[nb][rr]);
+          for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, sc[nb][rr]);
           mx[nb] = fmaxf(m, xor32(m));
           need[nb] = mx[nb] > m_run[nb] + kRescaleSlack;
           any_need |= need[nb];
@@ -291,13 +340,13 @@ void latent_attn_kernel(AttnArgs<T> p) {
           float lsum = 0.f;
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
-            const float e = __builtin_amdgcn_exp2f(s[nb][rr] - m_run[nb]);
-            s[nb][rr] = e;
+            const float e = __builtin_amdgcn_exp2f(sc[nb][rr] - m_run[nb]);
+            sc[nb][rr] = e;
             lsum += e;
           }
           l_run[nb] += lsum;
         }
-        // O^T += C^T[f][keys] * P^T[keys][rows]; each C^T fragment feeds NB MFMAs
+        // O^T += V^T[f][keys] * P^T[keys][rows]; each V^T fragment feeds NB MFMAs
         if constexpr (HALF) {
           f16x8 pf[NB][2];
 #pragma unroll
@@ -305,7 +354,7 @@ void latent_attn_kernel(AttnArgs<T> p) {
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
-              for (int j = 0; j < 8; ++j) pf[nb][u][j] = (f16)s[nb][8 * u + j];
+              for (int j = 0; j < 8; ++j) pf[nb][u][j] = (f16)sc[nb][8 * u + j];
 #pragma unroll
           for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
@@ -319,13 +368,13 @@ void latent_attn_kernel(AttnArgs<T> p) {
 #pragma unroll
           for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 run = *reinterpret_cast<const f32x4*>(Ct + 32 * fb * CS + 32 * kb + 16 * (g >> 1) +
-                                                                8 * h32 + 4 * (g & 1));
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4 run = *reinterpret_cast<const f32x4*>(Ct + 32 * fb * CS + 32 * kb + 16 * (q4 >> 1) +
+                                                                8 * h32 + 4 * (q4 & 1));
 #pragma unroll
               for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) o[nb][fb] = Mfma<float>::mma(run[i], s[nb][4 * g + i], o[nb][fb]);
+                for (int nb = 0; nb < NB; ++nb) o[nb][fb] = Mfma<float>::mma(run[i], sc[nb][4 * q4 + i], o[nb][fb]);
             }
         }
       }
@@ -334,52 +383,53 @@ void latent_attn_kernel(AttnArgs<T> p) {
     // One tile: prefetch the next tile into the other stage, compute this one,
     // then wait for this thread's loads and meet at the barrier (which also
     // retires every read of `cur` before it is refilled).
-    auto step = [&](int kt, const T* cur, T* nxt) {
-      if (kt + 1 < kt1) issue_tile(b, kt + 1, nxt);
-      compute(kt, cur);
+    auto step = [&](int t, const T* cur, T* nxt) {
+      if (t + 1 < kt1) issue_tile(s, t + 1, nxt);
+      compute(t, cur);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
 
-    issue_tile(b, kt0, lds0);
+    issue_tile(s, kt0, lds0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = kt0; kt < kt1; kt += 2) {
-      step(kt, lds0, lds1);
-      if (kt + 1 < kt1) step(kt + 1, lds1, lds0);
+    for (int t = kt0; t < kt1; t += 2) {
+      step(t, lds0, lds1);
+      if (t + 1 < kt1) step(t + 1, lds1, lds0);
     }
 
     const bool full = (kt0 == 0 && kt1 == p.KT);
+    T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float l_tot = l_run[nb] + xor32(l_run[nb]);
       const int qrow = row0 + 32 * nb + l32;
       if (full) {
         if (qrow < p.R) {
-          T* dst = p.out + ((long)b * p.R + qrow) * DC;
+          T* dst = out_s + (long)qrow * p.out_rs;
           const float inv = 1.f / l_tot;
 #pragma unroll
           for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int f = 32 * fb + 8 * q + 4 * h32;
-              if (f < DC)
-                store4(dst + f, o[nb][fb][4 * q] * inv, o[nb][fb][4 * q + 1] * inv, o[nb][fb][4 * q + 2] * inv,
-                       o[nb][fb][4 * q + 3] * inv);
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int f = 32 * fb + 8 * q4 + 4 * h32;
+              if (f < DV)
+                store4(dst + f, o[nb][fb][4 * q4] * inv, o[nb][fb][4 * q4 + 1] * inv, o[nb][fb][4 * q4 + 2] * inv,
+                       o[nb][fb][4 * q4 + 3] * inv);
             }
         }
       } else if (row0 < p.R) {
         const long slot_row =
             (long)(2 * blockIdx.x + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * RW + 32 * nb + l32;
-        float* po = p.part_o + slot_row * DC;
+        float* po = p.part_o + slot_row * DV;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int f = 32 * fb + 8 * q + 4 * h32;
-            if (f < DC)
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int f = 32 * fb + 8 * q4 + 4 * h32;
+            if (f < DV)
               *reinterpret_cast<f32x4*>(po + f) =
-                  f32x4{o[nb][fb][4 * q], o[nb][fb][4 * q + 1], o[nb][fb][4 * q + 2], o[nb][fb][4 * q + 3]};
+                  f32x4{o[nb][fb][4 * q4], o[nb][fb][4 * q4 + 1], o[nb][fb][4 * q4 + 2], o[nb][fb][4 * q4 + 3]};
           }
         if (h32 == 0) {
           p.part_ml[slot_row * 2] = m_run[nb];
@@ -395,12 +445,12 @@ void latent_attn_kernel(AttnArgs<T> p) {
 // Workgroups w0..w1 hold the pieces of row block `unit`; every piece is its
 // workgroup's first (slot 2w) except possibly w0's, which is its second
 // (slot 2w0+1) when w0 started inside an earlier row block.
-template <typename T, int DC, int ROWS>
-__global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
+template <typename T, int DV, int ROWS>
+__global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
   constexpr int SLICE = 16;  // rows per workgroup: many small workgroups hide load latency
   const long unit = blockIdx.x / (ROWS / SLICE);
   const int r0 = (int)(blockIdx.x % (ROWS / SLICE)) * SLICE;
-  const long I = (long)p.B * p.RB * p.KT;
+  const long I = (long)p.S * p.RB * p.KT;
   const long i0 = unit * p.KT, i1 = i0 + p.KT;
   auto start = [&](long w) { return w * I / p.G; };
   long w0 = i0 * p.G / I;
@@ -410,8 +460,9 @@ __global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
   if (w0 == w1) return;  // one workgroup finished this row block and wrote it
   const long slot0 = 2 * w0 + (start(w0) < i0 ? 1 : 0);
   const int npieces = (int)(w1 - w0 + 1);
-  const int b = (int)(unit / p.RB), rb = (int)(unit % p.RB);
-  constexpr int Q = DC / 4;  // float4 columns per row
+  const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
+  T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
+  constexpr int Q = DV / 4;  // float4 columns per row
   for (int task = threadIdx.x; task < SLICE * Q; task += 256) {
     const int r = r0 + task / Q, f = (task % Q) * 4;
     const int row = rb * ROWS + r;
@@ -427,45 +478,32 @@ __global__ __launch_bounds__(256) void latent_attn_combine(AttnArgs<T> p) {
       const long sr = (k == 0 ? slot0 : 2 * (w0 + k)) * kAttnMaxRows + r;
       const float sc = __builtin_amdgcn_exp2f(p.part_ml[sr * 2] - M);
       L += p.part_ml[sr * 2 + 1] * sc;
-      acc += sc * *reinterpret_cast<const f32x4*>(p.part_o + sr * DC + f);
+      acc += sc * *reinterpret_cast<const f32x4*>(p.part_o + sr * DV + f);
     }
     const float inv = 1.f / L;
-    store4(p.out + ((long)b * p.R + row) * DC + f, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    store4(out_s + (long)row * p.out_rs + f, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   }
 }
 
-template <typename T, int DC, int DR, int KTILE, int NW, int NB>
-static hipError_t launch_latent(const AttnCall& c, hipStream_t s) {
+// Fill in the tiling fields, then launch: (pre-pass,) attention, (combine).
+template <typename T, int D, int DV, int KTILE, int NW, int NB, bool VROWS>
+static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
   constexpr int ROWS = NW * 32 * NB;
-  AttnArgs<T> a;
-  a.qt = static_cast<const T*>(c.qt);
-  a.cache = static_cast<const T*>(c.cache);
-  a.stage = static_cast<const T*>(c.stage);
-  a.out = static_cast<T*>(c.out);
-  a.part_o = c.part_o;
-  a.part_ml = c.part_ml;
-  a.vtiles = c.vtiles;
-  a.cbs = c.cache_bstride;
-  a.sbs = c.stage_bstride;
-  a.R = c.R;
-  a.n_ring = c.n_ring;
-  a.n_keys = c.n_ring + c.n_stage;
-  a.RB = (c.R + ROWS - 1) / ROWS;
-  a.KT = (a.n_keys + KTILE - 1) / KTILE;
-  a.B = c.B;
-  const long I = (long)a.B * a.RB * a.KT;
-  a.G = (int)(c.G < I ? c.G : I);
-  latent_value_tiles<T, DC, DR, KTILE><<<dim3(a.KT, a.B), 256, 0, s>>>(a);
+  a.RB = (a.R + ROWS - 1) / ROWS;
+  a.tiles0 = (a.len0 + KTILE - 1) / KTILE;
+  a.KT = a.tiles0 + (a.len1 + KTILE - 1) / KTILE;
+  const long I = (long)a.S * a.RB * a.KT;
+  a.G = (int)(G < I ? G : I);
+  if constexpr (!VROWS) latent_value_tiles<T, D, DV, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
   hipError_t err;
-  if (c.ev_start && (err = hipEventRecord(c.ev_start, s)) != hipSuccess) return err;
-  latent_attn_kernel<T, DC, DR, KTILE, NW, NB><<<a.G, NW * 64, 0, s>>>(a);
-  if (c.ev_stop && (err = hipEventRecord(c.ev_stop, s)) != hipSuccess) return err;
-  if (I != (long)a.G * a.KT)
-    latent_attn_combine<T, DC, ROWS><<<a.B * a.RB * (ROWS / 16), 256, 0, s>>>(a);
+  if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+  flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS><<<a.G, NW * 64, 0, s>>>(a);
+  if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
+  if (I != (long)a.G * a.KT) flash_attn_combine<T, DV, ROWS><<<a.S * a.RB * (ROWS / 16), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
-// Kernel shape per built (dtype, d_c, d_rope): keys per tile, waves per
+// Kernel shape per built latent (dtype, d_c, d_rope): keys per tile, waves per
 // workgroup, 32-row blocks per wave.
 struct LatentShape {
   int ktile, nw, nb;
@@ -488,27 +526,86 @@ bool latent_attention_supported(DType dt, int dc, int dr) {
   return latent_shape(dt, dc, dr, sh);
 }
 
-size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_keys) {
+size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, int stage_keys) {
   LatentShape sh;
   if (!latent_shape(dt, dc, dr, sh)) return 0;
   const size_t es = dt == DType::F32 ? 4 : 2;
   const size_t dcp = (size_t)(dc + 31) / 32 * 32;
-  const size_t tiles = (size_t)(max_keys + sh.ktile - 1) / sh.ktile;
+  const size_t tiles = (size_t)(max_ring_keys + sh.ktile - 1) / sh.ktile + (stage_keys + sh.ktile - 1) / sh.ktile;
   return (size_t)B * tiles * dcp * (sh.ktile + 16 / es) * es;
 }
 
-hipError_t run_latent_attention(const AttnCall& c, hipStream_t s) {
-  if (c.dtype == DType::F32) {
-    if (c.dc == 24 && c.dr == 8) return launch_latent<float, 24, 8, 64, 4, 1>(c, s);
+template <typename T>
+static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
+  FlashArgs<T> a = {};
+  a.q = static_cast<const T*>(c.qt);
+  a.q_ss = (long)c.R * (c.dc + c.dr);
+  a.key0 = static_cast<const T*>(c.cache);
+  a.key1 = static_cast<const T*>(c.stage);
+  a.key_ss0 = c.cache_bstride;
+  a.key_ss1 = c.stage_bstride;
+  a.val0 = c.vtiles;
+  a.out = static_cast<T*>(c.out);
+  a.out_so = (long)c.R * c.dc;
+  a.out_sh = 0;
+  a.out_rs = c.dc;
+  a.heads = 1;
+  a.part_o = c.part_o;
+  a.part_ml = c.part_ml;
+  a.len0 = c.n_ring;
+  a.len1 = c.n_stage;
+  a.R = c.R;
+  a.S = c.B;
+  if constexpr (std::is_same<T, float>::value) {
+    if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+    return hipErrorInvalidValue;
+  } else {
+    if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+    if (c.dr == 32) {
+      if (c.dc == 96) return launch_flash<T, 128, 96, 64, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+      if (c.dc == 192) return launch_flash<T, 224, 192, 64, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+      if (c.dc == 448) return launch_flash<T, 480, 448, 32, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+    }
     return hipErrorInvalidValue;
   }
-  if (c.dc == 24 && c.dr == 8) return launch_latent<bf16, 24, 8, 64, 4, 1>(c, s);
-  if (c.dr == 32) {
-    if (c.dc == 96) return launch_latent<bf16, 96, 32, 64, 8, 1>(c, s);
-    if (c.dc == 192) return launch_latent<bf16, 192, 32, 64, 8, 1>(c, s);
-    if (c.dc == 448) return launch_latent<bf16, 448, 32, 32, 4, 1>(c, s);
-  }
-  return hipErrorInvalidValue;
+}
+
+hipError_t run_latent_attention(const AttnCall& c, hipStream_t s) {
+  if (c.dtype == DType::F32) return latent_t<float>(c, s);
+  return latent_t<bf16>(c, s);
+}
+
+bool dense_attention_supported(DType dt, int dh, int dv) {
+  return dt == DType::BF16 && dh == 128 && dv == 128;
+}
+
+hipError_t run_dense_attention(const DenseAttnCall& c, hipStream_t s) {
+  if (!dense_attention_supported(DType::BF16, c.dh, c.dv)) return hipErrorInvalidValue;
+  FlashArgs<bf16> a = {};
+  a.q = static_cast<const bf16*>(c.q);
+  a.q_ss = (long)c.Nq * c.dh;
+  a.key0 = static_cast<const bf16*>(c.kring);
+  a.key1 = static_cast<const bf16*>(c.kstage);
+  a.key_ss0 = (long)c.ring_stride * c.dh;
+  a.key_ss1 = (long)c.stage_stride * c.dh;
+  a.val0 = c.vring;
+  a.val1 = c.vstage;
+  a.val_ss0 = (long)c.dv * c.ring_stride;
+  a.val_ss1 = (long)c.dv * c.stage_stride;
+  a.val_rs0 = c.ring_stride;
+  a.val_rs1 = c.stage_stride;
+  a.out = static_cast<bf16*>(c.out);
+  a.out_so = (long)c.Nq * c.H * c.dv;
+  a.out_sh = c.dv;
+  a.out_rs = (long)c.H * c.dv;
+  a.heads = c.H;
+  a.part_o = c.part_o;
+  a.part_ml = c.part_ml;
+  a.len0 = c.n_ring;
+  a.len1 = c.Nq;
+  a.R = c.Nq;
+  a.S = c.B * c.H;
+  return launch_flash<bf16, 128, 128, kDenseKeyTile, 8, 1, true>(a, c.G, c.ev_start, c.ev_stop, s);
 }
 
 }  // namespace vmla

@@ -1,0 +1,194 @@
+// Launch sequences of the dense per-head baseline (VideoMLA paper, section 1 and
+// appendix C.1: the layer whose cache holds every head's key and value).
+//
+//   append: one GEMM x . [W_K; W_V]^T whose epilogue rotates each head's key by
+//     3D-RoPE (all d_h channels, absolute frame index), writes it to the key row
+//     of its ring slot, and writes the value transposed (fp16) to the value
+//     column of that slot; then the value columns past the valid keys up to the
+//     next key-tile boundary are zeroed, so the attention kernel can stage
+//     whole tiles.
+//   attend: q = RoPE(W_Q x) scaled by log2(e)/sqrt(d_h); the chunk's own keys
+//     and values into staging with the same epilogue; dense flash attention
+//     over ring + chunk (attention.hip); out = W_O o.
+#include "gemm.h"
+#include "plan.h"
+
+namespace vmla {
+
+// Column of key j in a transposed value row: bits 2 and 3 of j swapped, so the
+// 8 keys one lane feeds to a value MFMA are contiguous.
+__device__ inline int perm16(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+static Rope dense_rope(const DensePlan& p) {
+  Rope r;
+  r.pairs_t = p.pairs_t;
+  r.pairs_h = p.pairs_h;
+  r.grid_w = p.grid_w;
+  r.tokens_per_frame = p.Tpf;
+  for (int i = 0; i < kMaxRopePairs; ++i) r.freq[i] = p.freq[i];
+  return r;
+}
+
+// q[(b*nh + h)][t][j] = qscale * RoPE(W_Q^h x_t)[j]; token m is chunk token
+// m % Nq of stream m / Nq, in frame frame0 + t / T.
+struct EpiDenseQ {
+  bf16* q;
+  int Nq, nh, dh;
+  float qscale;
+  int64_t frame0;
+  Rope rope;
+  __device__ void operator()(int, int m, int n, const float* v) const {
+    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
+    const int64_t frame = frame0 + t / rope.tokens_per_frame;
+    const int s = t % rope.tokens_per_frame;
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    rope.rotate2(j >> 1, frame, s, a0, a1);
+    rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
+    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0 * qscale, a1 * qscale, a2 * qscale, a3 * qscale);
+  }
+};
+
+// Features [0, nh*dh) are keys, [nh*dh, nh*(dh+dv)) values.  Key row / value
+// column of token t: its ring slot row (frame % W)*T + s, or t for staging.
+struct EpiDenseKV {
+  bf16* k;  // [B][nh][P][dh]
+  f16* v;   // [B][nh][dv][P]
+  long P;
+  int Nq, nh, dh, dv, W;
+  int ring;
+  int64_t frame0;
+  Rope rope;
+  __device__ void operator()(int, int m, int n, const float* x) const {
+    const int b = m / Nq, t = m % Nq;
+    const int64_t frame = frame0 + t / rope.tokens_per_frame;
+    const int s = t % rope.tokens_per_frame;
+    const long row = ring ? (long)(frame % W) * rope.tokens_per_frame + s : (long)t;
+    if (n < nh * dh) {
+      const int h = n / dh, j = n % dh;
+      float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
+      rope.rotate2(j >> 1, frame, s, a0, a1);
+      rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
+      store4(k + (((long)b * nh + h) * P + row) * dh + j, a0, a1, a2, a3);
+    } else {
+      const int n2 = n - nh * dh, h = n2 / dv, f = n2 % dv;
+      f16* dst = v + (((long)b * nh + h) * dv + f) * P + (row & ~15L) + perm16((int)(row & 15));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i * P] = (f16)x[i];
+    }
+  }
+};
+
+// Zero the value columns of keys [c0, c1) in `rows` transposed rows of stride P.
+__global__ __launch_bounds__(256) void zero_value_columns(f16* v, long rows, long P, int c0, int c1) {
+  const long w = c1 - c0;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < rows * w; i += (long)gridDim.x * 256) {
+    const long r = i / w;
+    const int j = c0 + (int)(i % w);
+    v[r * P + (j & ~15) + perm16(j & 15)] = (f16)0.f;
+  }
+}
+
+static void zero_columns(void* v, long rows, long P, int c0, int c1, hipStream_t s) {
+  if (c1 <= c0) return;
+  const long work = rows * (c1 - c0);
+  const int grid = (int)((work + 255) / 256 < 1024 ? (work + 255) / 256 : 1024);
+  zero_value_columns<<<grid, 256, 0, s>>>(static_cast<f16*>(v), rows, P, c0, c1);
+}
+
+static GemmOps<bf16> dense_ops(const void* w, const void* w2, int n_split, const void* x, long ldx, int N,
+                               int M, int K) {
+  GemmOps<bf16> o;
+  o.w = static_cast<const bf16*>(w);
+  o.w2 = static_cast<const bf16*>(w2);
+  o.ldw = K;
+  o.wz = 0;
+  o.x = static_cast<const bf16*>(x);
+  o.ldx = ldx;
+  o.xz = 0;
+  o.N = N;
+  o.M = M;
+  o.K = K;
+  o.n_split = n_split;
+  return o;
+}
+
+// K/V of x's tokens (frames frame0..) into the ring or the staging buffers.
+static void dense_kv(const DensePlan& p, const void* x, int64_t frame0, bool ring, hipStream_t s) {
+  EpiDenseKV e;
+  e.k = static_cast<bf16*>(ring ? p.kring : p.kstage);
+  e.v = static_cast<f16*>(ring ? p.vring : p.vstage);
+  e.P = ring ? p.ring_stride : p.stage_stride;
+  e.Nq = p.Nq;
+  e.nh = p.nh;
+  e.dh = p.dh;
+  e.dv = p.dv;
+  e.W = p.W;
+  e.ring = ring ? 1 : 0;
+  e.frame0 = frame0;
+  e.rope = dense_rope(p);
+  gemm<bf16, false>(dense_ops(p.w_k, p.w_v, p.nh * p.dh, x, p.d, p.nh * (p.dh + p.dv), p.B * p.Nq, p.d), 1, e, s);
+}
+
+static int round_tile(long keys) {
+  return (int)((keys + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile);
+}
+
+hipError_t run_dense_append(const DensePlan& p, int64_t n, const void* x, hipStream_t s) {
+  dense_kv(p, x, n, true, s);
+  // valid ring keys after this append: min(n + C, W) frames
+  const int64_t frames = n + p.C < p.W ? n + p.C : p.W;
+  const long valid = (long)frames * p.Tpf;
+  zero_columns(p.vring, (long)p.B * p.nh * p.dv, p.ring_stride, (int)valid, round_tile(valid), s);
+  return hipGetLastError();
+}
+
+hipError_t run_dense_attend(const DensePlan& p, int64_t n, const void* x, void* out, hipStream_t s,
+                            hipEvent_t ev0, hipEvent_t ev1) {
+  const int M = p.B * p.Nq;
+  {
+    EpiDenseQ e;
+    e.q = static_cast<bf16*>(p.q);
+    e.Nq = p.Nq;
+    e.nh = p.nh;
+    e.dh = p.dh;
+    e.qscale = p.qscale;
+    e.frame0 = n;
+    e.rope = dense_rope(p);
+    gemm<bf16, false>(dense_ops(p.w_q, p.w_q, p.nh * p.dh, x, p.d, p.nh * p.dh, M, p.d), 1, e, s);
+  }
+  dense_kv(p, x, n, false, s);
+  zero_columns(p.vstage, (long)p.B * p.nh * p.dv, p.stage_stride, p.Nq, p.stage_stride, s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  {
+    DenseAttnCall a;
+    a.dh = p.dh;
+    a.dv = p.dv;
+    a.q = p.q;
+    a.kring = p.kring;
+    a.vring = p.vring;
+    a.kstage = p.kstage;
+    a.vstage = p.vstage;
+    a.out = p.o;
+    a.part_o = p.part_o;
+    a.part_ml = p.part_ml;
+    a.ev_start = ev0;
+    a.ev_stop = ev1;
+    a.B = p.B;
+    a.H = p.nh;
+    a.Nq = p.Nq;
+    a.n_ring = (int)((n < p.W ? n : p.W) * p.Tpf);
+    a.ring_stride = p.ring_stride;
+    a.stage_stride = p.stage_stride;
+    a.G = p.G;
+    err = run_dense_attention(a, s);
+    if (err != hipSuccess) return err;
+  }
+  {  // out = W_O o
+    EpiStore<bf16> e{static_cast<bf16*>(out), p.d, 0};
+    gemm<bf16, false>(dense_ops(p.w_o, p.w_o, p.d, p.o, (long)p.nh * p.dv, p.d, M, p.nh * p.dv), 1, e, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vmla

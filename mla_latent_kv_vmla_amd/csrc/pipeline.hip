@@ -23,15 +23,6 @@ static Rope make_rope(const Plan& p) {
   return r;
 }
 
-// Y[m][n] -> y[z*yz + m*ldy + n]
-template <typename T> struct EpiStore {
-  T* y;
-  long ldy, yz;
-  __device__ void operator()(int z, int m, int n, const float* v) const {
-    store4(y + (long)z * yz + (long)m * ldy + n, v[0], v[1], v[2], v[3]);
-  }
-};
-
 // Latent cache rows: features [0, dc) are c, [dc, dc+dr) the decoupled key,
 // rotated with the token's (frame, row, column).  Token m is chunk token
 // m % Nq of stream m / Nq, frame frame0 + t / T.
@@ -94,32 +85,6 @@ template <typename T> struct EpiAbsorb {
     store4(qt + ((long)m * nh + z) * D + n, v[0] * qscale, v[1] * qscale, v[2] * qscale, v[3] * qscale);
   }
 };
-
-// Tile shape: the largest of (features x tokens) = 128x128, 128x64, 64x128,
-// 64x64 that wastes at most 15% of the padded tile area and still launches
-// >= 384 workgroups (1.5 per compute unit); otherwise the shape with the most
-// workgroups.
-template <typename T, bool W_KN, class Epi>
-static void gemm(const GemmOps<T>& op, int Z, const Epi& epi, hipStream_t s) {
-  const int shapes[4][2] = {{128, 128}, {128, 64}, {64, 128}, {64, 64}};
-  int pick = -1, best = 3;
-  long best_wg = -1;
-  for (int i = 0; i < 4; ++i) {
-    const long bn = shapes[i][0], bm = shapes[i][1];
-    const long tn = (op.N + bn - 1) / bn, tm = (op.M + bm - 1) / bm;
-    const long wg = tn * tm * Z;
-    const double waste = (double)(tn * bn) * (tm * bm) / ((double)op.N * op.M);
-    if (pick < 0 && waste <= 1.15 && wg >= 384) pick = i;
-    if (wg > best_wg) best_wg = wg, best = i;
-  }
-  if (pick < 0) pick = best;
-  const int BN = shapes[pick][0], BM = shapes[pick][1];
-  dim3 grid((op.N + BN - 1) / BN, (op.M + BM - 1) / BM, Z);
-  if (BN == 128 && BM == 128) gemm_kernel<T, 128, 128, W_KN, Epi><<<grid, 256, 0, s>>>(op, epi);
-  else if (BN == 128) gemm_kernel<T, 128, 64, W_KN, Epi><<<grid, 256, 0, s>>>(op, epi);
-  else if (BM == 128) gemm_kernel<T, 64, 128, W_KN, Epi><<<grid, 256, 0, s>>>(op, epi);
-  else gemm_kernel<T, 64, 64, W_KN, Epi><<<grid, 256, 0, s>>>(op, epi);
-}
 
 template <typename T>
 static GemmOps<T> ops(const void* w, long ldw, long wz, const void* x, long ldx, long xz, int N, int M, int K) {

@@ -1,5 +1,6 @@
 // Internal interface between the host runtime (vmla_host.cpp) and the kernel
-// pipelines (pipeline.hip, attention.hip).  Host-only types; no HIP kernels.
+// pipelines (pipeline.hip, dense.hip, attention.hip).  Host-only types; no HIP
+// kernels.
 #pragma once
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
@@ -13,6 +14,9 @@ enum class DType : int { BF16 = 0, F32 = 1 };
 // (the largest row block any built attention kernel uses).
 constexpr int kAttnMaxRows = 256;
 constexpr int kMaxRopePairs = 64;
+// Key-tile size of the dense attention kernel; the dense ring and the chunk's
+// staged keys are padded to a multiple of it.
+constexpr int kDenseKeyTile = 64;
 
 // Everything one layer call needs: geometry, borrowed device pointers and the
 // workspace carve-up.  Filled by the host runtime; read by the pipelines.
@@ -53,8 +57,8 @@ hipError_t run_compress(const Plan& p, const void* x, int64_t frame0, void* dst,
 hipError_t run_attend(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s,
                       hipEvent_t attn_start = nullptr, hipEvent_t attn_stop = nullptr);
 
-// Latent attention kernels (attention.hip): keys = n_ring cache rows followed by
-// the chunk's staged rows.  Returns hipErrorInvalidValue for an unbuilt shape.
+// Latent attention kernels (attention.hip): keys = n_ring cache rows, then the
+// chunk's staged rows.  Returns hipErrorInvalidValue for an unbuilt shape.
 struct AttnCall {
   DType dtype;
   int dc, dr;
@@ -72,7 +76,60 @@ struct AttnCall {
 };
 hipError_t run_latent_attention(const AttnCall& a, hipStream_t s);
 bool latent_attention_supported(DType dt, int dc, int dr);
-// Workspace bytes of the transposed value-tile images for up to max_keys keys.
-size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_keys);
+// Workspace bytes of the transposed value-tile images for up to max_ring_keys
+// ring keys plus stage_keys chunk keys.
+size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, int stage_keys);
+
+// ---------------------------------------------------------------- dense baseline
+// Per-head keys and values (the dense layer of the paper's section 1 and
+// appendix C.1).  Per (stream b, head h):
+//   keys   [P][dh] bf16, rotated by 3D-RoPE on all dh channels;
+//   values [dv][P] fp16, transposed, key j at column perm16(j) (bits 2 and 3
+//          of j swapped), zero at every column past the valid keys up to P;
+// P = ring_stride (ring: W*T keys, frame f in slots (f % W)*T..) or
+// stage_stride (the chunk's own C*T keys), both multiples of kDenseKeyTile.
+struct DensePlan {
+  int B, d, nh, dh, dv;
+  int Tpf, grid_w, W, C, Nq;
+  int pairs_t, pairs_h, pairs_w;
+  float freq[kMaxRopePairs];
+  float qscale;  // log2(e) / sqrt(dh)
+  int G;
+  int ring_stride, stage_stride;
+  const void *w_q, *w_k, *w_v, *w_o;
+  void *kring, *vring;  // cache
+  // workspace regions
+  void *q;       // [B][nh][Nq][dh]  rotated, scaled queries
+  void *kstage;  // [B][nh][stage_stride][dh]
+  void *vstage;  // [B][nh][dv][stage_stride]
+  void *o;       // [B][Nq][nh*dv]  attention output
+  float *part_o, *part_ml;
+};
+
+struct DenseLayout {
+  size_t kring, vring, cache_total;                         // cache
+  size_t q, kstage, vstage, o, part_o, part_ml, ws_total;   // workspace
+};
+DenseLayout dense_layout(const DensePlan& p);
+
+// append: K/V of the chunk (frames n..n+C-1) into ring slots.
+hipError_t run_dense_append(const DensePlan& p, int64_t n, const void* x, hipStream_t s);
+// attend: chunk attention against the ring holding n frames, then W_O.
+hipError_t run_dense_attend(const DensePlan& p, int64_t n, const void* x, void* out, hipStream_t s,
+                            hipEvent_t attn_start = nullptr, hipEvent_t attn_stop = nullptr);
+
+struct DenseAttnCall {
+  int dh, dv;
+  const void* q;
+  const void *kring, *vring, *kstage, *vstage;
+  void* out;  // [B][Nq][H][dv]
+  float* part_o;
+  float* part_ml;
+  hipEvent_t ev_start, ev_stop;
+  int B, H, Nq, n_ring, ring_stride, stage_stride;
+  int G;
+};
+hipError_t run_dense_attention(const DenseAttnCall& a, hipStream_t s);
+bool dense_attention_supported(DType dt, int dh, int dv);
 
 }  // namespace vmla

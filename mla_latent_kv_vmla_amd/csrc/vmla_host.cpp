@@ -1,6 +1,7 @@
 // Host runtime of libvmla.so: config validation, ring-buffer metadata,
-// workspace carve-up and the C ABI declared in include/vmla.h.  Every check
-// runs before anything is enqueued; only run_compress / run_attend touch HIP.
+// workspace carve-up and the C ABI declared in include/vmla.h, for the latent
+// layer (vmla_*) and the dense per-head baseline (vmla_dense_*).  Every check
+// runs before anything is enqueued; only the run_* pipelines touch HIP.
 #include "vmla.h"
 
 #include <math.h>
@@ -10,6 +11,7 @@
 #include "plan.h"
 
 using vmla::DType;
+using vmla::DensePlan;
 using vmla::Plan;
 
 struct vmla_ctx {
@@ -21,16 +23,27 @@ struct vmla_ctx {
   int64_t n;  // frames appended (lockstep over the batch)
 };
 
+struct vmla_dense_ctx {
+  vmla_config cfg;
+  vmla_dense_weights w;
+  void* cache;
+  void* workspace;
+  float freq[vmla::kMaxRopePairs];
+  int64_t n;
+};
+
 namespace {
 
 constexpr int kDefaultWorkgroups = 256;  // MI355X compute units
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_config(const vmla_config* c) {
-  if (!c) return VMLA_ERR_NULL;
-  if (c->batch <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->d_nope <= 0 || c->d_rope <= 0 ||
-      c->d_v <= 0 || c->d_c <= 0 || c->d_q <= 0 || c->grid_h <= 0 || c->grid_w <= 0 ||
+size_t elem_bytes(const vmla_config* c) { return c->dtype == VMLA_DTYPE_F32 ? 4 : 2; }
+
+// Checks common to both layer types.
+int check_common(const vmla_config* c) {
+  if (c->batch <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->d_rope <= 0 || c->d_v <= 0 ||
+      c->d_nope < 0 || c->d_c < 0 || c->d_q < 0 || c->grid_h <= 0 || c->grid_w <= 0 ||
       c->window_frames <= 0 || c->chunk_frames <= 0 || c->attn_workgroups < 0)
     return VMLA_ERR_CONFIG;
   if (c->chunk_frames > c->window_frames) return VMLA_ERR_CONFIG;
@@ -47,12 +60,52 @@ int check_config(const vmla_config* c) {
   const long long rows = T * c->window_frames + T * c->chunk_frames;
   if (rows * c->n_heads > (1LL << 30) || (long long)c->batch * T * c->chunk_frames > (1LL << 30))
     return VMLA_ERR_CONFIG;
+  return VMLA_OK;
+}
+
+int check_config(const vmla_config* c) {
+  if (!c) return VMLA_ERR_NULL;
+  int st = check_common(c);
+  if (st != VMLA_OK) return st;
+  if (c->d_nope <= 0 || c->d_c <= 0 || c->d_q <= 0) return VMLA_ERR_CONFIG;
+  // one stream's ring rows are addressed with 32-bit byte offsets
+  const long long T = (long long)c->grid_h * c->grid_w;
+  if (T * c->window_frames * (c->d_c + c->d_rope) * (long long)elem_bytes(c) >= (1LL << 31))
+    return VMLA_ERR_CONFIG;
   if (!vmla::latent_attention_supported(static_cast<DType>(c->dtype), c->d_c, c->d_rope))
     return VMLA_ERR_UNSUPPORTED;
   return VMLA_OK;
 }
 
-size_t elem_bytes(const vmla_config* c) { return c->dtype == VMLA_DTYPE_F32 ? 4 : 2; }
+// Keys per (stream, head) row of the dense ring: W*T padded to the key tile.
+long long dense_ring_stride(const vmla_config* c) {
+  const long long keys = (long long)c->grid_h * c->grid_w * c->window_frames;
+  return (keys + vmla::kDenseKeyTile - 1) / vmla::kDenseKeyTile * vmla::kDenseKeyTile;
+}
+
+// Dense baseline: per-head query/key width d_rope (every channel rotated),
+// value width d_v; the latent-only widths must be 0.
+int check_dense_config(const vmla_config* c) {
+  if (!c) return VMLA_ERR_NULL;
+  int st = check_common(c);
+  if (st != VMLA_OK) return st;
+  if (c->d_nope != 0 || c->d_c != 0 || c->d_q != 0) return VMLA_ERR_CONFIG;
+  // one (stream, head)'s keys and values are addressed with 32-bit byte offsets
+  const int wmax = c->d_rope > c->d_v ? c->d_rope : c->d_v;
+  if (dense_ring_stride(c) * wmax * 2 >= (1LL << 31)) return VMLA_ERR_CONFIG;
+  if (!vmla::dense_attention_supported(static_cast<DType>(c->dtype), c->d_rope, c->d_v))
+    return VMLA_ERR_UNSUPPORTED;
+  return VMLA_OK;
+}
+
+// Default rotary table: omega_i = theta^(-2i / (2 p_a)) for i = 0..p_a-1 on each
+// axis (t, h, w).
+void default_freqs(const vmla_config* cfg, float* freq) {
+  const int pa[3] = {cfg->rope_pairs_t, cfg->rope_pairs_h, cfg->rope_pairs_w};
+  int k = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int i = 0; i < pa[a]; ++i) freq[k++] = (float)pow((double)cfg->rope_theta, -2.0 * i / (2.0 * pa[a]));
+}
 
 // Geometry-only part of a plan (no pointers).
 Plan geometry(const vmla_config* c) {
@@ -105,11 +158,59 @@ WorkspaceLayout workspace_layout(const Plan& p) {
   L.o = take(M * p.nh * (size_t)p.dv * es);
   L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * sizeof(float));
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
-  L.vtiles = take(latent_value_tiles_bytes(p.dtype, p.dc, p.dr, p.B, p.W * p.Tpf + p.Nq));
+  L.vtiles = take(latent_value_tiles_bytes(p.dtype, p.dc, p.dr, p.B, p.W * p.Tpf, p.Nq));
   L.total = off;
   return L;
 }
+
+DenseLayout dense_layout(const DensePlan& p) {
+  DenseLayout L;
+  const size_t heads = (size_t)p.B * p.nh;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.kring = take(heads * p.ring_stride * p.dh * 2);
+  L.vring = take(heads * p.ring_stride * p.dv * 2);
+  L.cache_total = off;
+  off = 0;
+  L.q = take(heads * p.Nq * p.dh * 2);
+  L.kstage = take(heads * p.stage_stride * p.dh * 2);
+  L.vstage = take(heads * p.stage_stride * p.dv * 2);
+  L.o = take((size_t)p.B * p.Nq * p.nh * p.dv * 2);
+  L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dv * sizeof(float));
+  L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
+  L.ws_total = off;
+  return L;
+}
 }  // namespace vmla
+
+namespace {
+DensePlan dense_geometry(const vmla_config* c) {
+  DensePlan p;
+  memset(&p, 0, sizeof(p));
+  p.B = c->batch;
+  p.d = c->hidden;
+  p.nh = c->n_heads;
+  p.dh = c->d_rope;
+  p.dv = c->d_v;
+  p.Tpf = c->grid_h * c->grid_w;
+  p.grid_w = c->grid_w;
+  p.W = c->window_frames;
+  p.C = c->chunk_frames;
+  p.Nq = c->chunk_frames * p.Tpf;
+  p.pairs_t = c->rope_pairs_t;
+  p.pairs_h = c->rope_pairs_h;
+  p.pairs_w = c->rope_pairs_w;
+  p.qscale = (float)(1.4426950408889634 / sqrt((double)p.dh));
+  p.G = c->attn_workgroups > 0 ? c->attn_workgroups : kDefaultWorkgroups;
+  p.ring_stride = (int)dense_ring_stride(c);
+  p.stage_stride = (p.Nq + vmla::kDenseKeyTile - 1) / vmla::kDenseKeyTile * vmla::kDenseKeyTile;
+  return p;
+}
+}  // namespace
 
 extern "C" {
 
@@ -153,12 +254,7 @@ VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* ca
   if (rope_freqs) {
     for (int i = 0; i < npairs; ++i) c->freq[i] = rope_freqs[i];
   } else {
-    // omega_i = theta^(-2i / (2 p_a)) for i = 0..p_a-1 on each axis (t, h, w)
-    const int pa[3] = {cfg->rope_pairs_t, cfg->rope_pairs_h, cfg->rope_pairs_w};
-    int k = 0;
-    for (int a = 0; a < 3; ++a)
-      for (int i = 0; i < pa[a]; ++i)
-        c->freq[k++] = (float)pow((double)cfg->rope_theta, -2.0 * i / (2.0 * pa[a]));
+    default_freqs(cfg, c->freq);
   }
   *out = c;
   return VMLA_OK;
@@ -244,12 +340,122 @@ VMLA_API int vmla_reset(vmla_ctx* ctx) {
 
 VMLA_API void vmla_destroy(vmla_ctx* ctx) { delete ctx; }
 
+/* ------------------------------------------------------------ dense baseline */
+
+VMLA_API size_t vmla_dense_cache_bytes(const vmla_config* cfg) {
+  if (check_dense_config(cfg) != VMLA_OK) return 0;
+  return vmla::dense_layout(dense_geometry(cfg)).cache_total;
+}
+
+VMLA_API size_t vmla_dense_workspace_bytes(const vmla_config* cfg) {
+  if (check_dense_config(cfg) != VMLA_OK) return 0;
+  return vmla::dense_layout(dense_geometry(cfg)).ws_total;
+}
+
+VMLA_API int vmla_dense_create(const vmla_config* cfg, const vmla_dense_weights* w, void* cache,
+                               void* workspace, const float* rope_freqs, vmla_dense_ctx** out) {
+  if (!out) return VMLA_ERR_NULL;
+  *out = nullptr;
+  int st = check_dense_config(cfg);
+  if (st != VMLA_OK) return st;
+  if (!w || !cache || !workspace) return VMLA_ERR_NULL;
+  const void* ptrs[] = {w->w_q, w->w_k, w->w_v, w->w_o};
+  for (const void* q : ptrs)
+    if (!q) return VMLA_ERR_NULL;
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return VMLA_ERR_ALIGN;
+  if (!aligned16(cache) || !aligned16(workspace)) return VMLA_ERR_ALIGN;
+  const int npairs = cfg->d_rope / 2;
+  if (rope_freqs)
+    for (int i = 0; i < npairs; ++i)
+      if (!isfinite(rope_freqs[i])) return VMLA_ERR_ARG;
+  vmla_dense_ctx* c = new (std::nothrow) vmla_dense_ctx;
+  if (!c) return VMLA_ERR_STATE;
+  memset(c, 0, sizeof(*c));
+  c->cfg = *cfg;
+  c->w = *w;
+  c->cache = cache;
+  c->workspace = workspace;
+  c->n = 0;
+  if (rope_freqs) {
+    for (int i = 0; i < npairs; ++i) c->freq[i] = rope_freqs[i];
+  } else {
+    default_freqs(cfg, c->freq);
+  }
+  *out = c;
+  return VMLA_OK;
+}
+
+static DensePlan make_dense_plan(const vmla_dense_ctx* c) {
+  DensePlan p = dense_geometry(&c->cfg);
+  for (int i = 0; i < vmla::kMaxRopePairs; ++i) p.freq[i] = c->freq[i];
+  p.w_q = c->w.w_q;
+  p.w_k = c->w.w_k;
+  p.w_v = c->w.w_v;
+  p.w_o = c->w.w_o;
+  const vmla::DenseLayout L = vmla::dense_layout(p);
+  char* cache = static_cast<char*>(c->cache);
+  char* ws = static_cast<char*>(c->workspace);
+  p.kring = cache + L.kring;
+  p.vring = cache + L.vring;
+  p.q = ws + L.q;
+  p.kstage = ws + L.kstage;
+  p.vstage = ws + L.vstage;
+  p.o = ws + L.o;
+  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  return p;
+}
+
+VMLA_API int vmla_dense_append(vmla_dense_ctx* ctx, const void* x, hipStream_t stream) {
+  if (!ctx || !x) return VMLA_ERR_NULL;
+  if (!aligned16(x)) return VMLA_ERR_ALIGN;
+  if (ctx->n > INT64_MAX / 2) return VMLA_ERR_STATE;
+  if (vmla::run_dense_append(make_dense_plan(ctx), ctx->n, x, stream) != hipSuccess) return VMLA_ERR_HIP;
+  ctx->n += ctx->cfg.chunk_frames;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_dense_attend(vmla_dense_ctx* ctx, const void* x, void* out, hipStream_t stream) {
+  if (!ctx || !x || !out) return VMLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (vmla::run_dense_attend(make_dense_plan(ctx), ctx->n, x, out, stream) != hipSuccess) return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_dense_attend_profiled(vmla_dense_ctx* ctx, const void* x, void* out, hipEvent_t attn_start,
+                                        hipEvent_t attn_stop, hipStream_t stream) {
+  if (!ctx || !x || !out || !attn_start || !attn_stop) return VMLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (vmla::run_dense_attend(make_dense_plan(ctx), ctx->n, x, out, stream, attn_start, attn_stop) != hipSuccess)
+    return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_dense_cache_state(const vmla_dense_ctx* ctx, int64_t* frames_appended,
+                                    int64_t* first_valid_frame, int32_t* n_valid_frames) {
+  if (!ctx) return VMLA_ERR_NULL;
+  const int64_t W = ctx->cfg.window_frames;
+  if (frames_appended) *frames_appended = ctx->n;
+  if (first_valid_frame) *first_valid_frame = ctx->n > W ? ctx->n - W : 0;
+  if (n_valid_frames) *n_valid_frames = (int32_t)(ctx->n < W ? ctx->n : W);
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_dense_reset(vmla_dense_ctx* ctx) {
+  if (!ctx) return VMLA_ERR_NULL;
+  ctx->n = 0;
+  return VMLA_OK;
+}
+
+VMLA_API void vmla_dense_destroy(vmla_dense_ctx* ctx) { delete ctx; }
+
 VMLA_API const char* vmla_status_string(int status) {
   switch (status) {
     case VMLA_OK: return "ok";
     case VMLA_ERR_NULL: return "required pointer is NULL";
     case VMLA_ERR_CONFIG: return "invalid configuration";
-    case VMLA_ERR_UNSUPPORTED: return "no kernel built for this (dtype, d_c, d_rope)";
+    case VMLA_ERR_UNSUPPORTED: return "no kernel built for this (dtype, widths)";
     case VMLA_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case VMLA_ERR_STATE: return "call not valid in the current state";
     case VMLA_ERR_ARG: return "argument out of range";

@@ -5,8 +5,9 @@ of the computation runs in the HIP library.  Device memory comes from torch
 (plumbing); the library borrows it.  If the library is missing this module
 raises on first use -- there is no fallback path.
 
-`LatentAttention` is a convenience owner of one layer's device tensors (weights,
-ring cache, workspace) that calls the same entry points.
+`LatentAttention` (and `DenseAttention` for the dense per-head baseline) is a
+convenience owner of one layer's device tensors (weights, ring cache,
+workspace) that calls the same entry points.
 """
 from __future__ import annotations
 
@@ -42,6 +43,10 @@ class vmla_config(ctypes.Structure):
 
 class vmla_weights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_uk", "w_uv", "w_o")]
+
+
+class vmla_dense_weights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("w_q", "w_k", "w_v", "w_o")]
 
 
 class VmlaError(RuntimeError):
@@ -84,6 +89,25 @@ def lib():
         L.vmla_reset.restype = c_int
         L.vmla_destroy.argtypes = [c_void_p]
         L.vmla_destroy.restype = None
+        L.vmla_dense_cache_bytes.argtypes = [POINTER(vmla_config)]
+        L.vmla_dense_cache_bytes.restype = c_size_t
+        L.vmla_dense_workspace_bytes.argtypes = [POINTER(vmla_config)]
+        L.vmla_dense_workspace_bytes.restype = c_size_t
+        L.vmla_dense_create.argtypes = [POINTER(vmla_config), POINTER(vmla_dense_weights), c_void_p, c_void_p,
+                                        POINTER(c_float), POINTER(c_void_p)]
+        L.vmla_dense_create.restype = c_int
+        L.vmla_dense_append.argtypes = [c_void_p, c_void_p, c_void_p]
+        L.vmla_dense_append.restype = c_int
+        L.vmla_dense_attend.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
+        L.vmla_dense_attend.restype = c_int
+        L.vmla_dense_attend_profiled.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.vmla_dense_attend_profiled.restype = c_int
+        L.vmla_dense_cache_state.argtypes = [c_void_p, POINTER(c_int64), POINTER(c_int64), POINTER(c_int32)]
+        L.vmla_dense_cache_state.restype = c_int
+        L.vmla_dense_reset.argtypes = [c_void_p]
+        L.vmla_dense_reset.restype = c_int
+        L.vmla_dense_destroy.argtypes = [c_void_p]
+        L.vmla_dense_destroy.restype = None
         L.vmla_status_string.argtypes = [c_int]
         L.vmla_status_string.restype = c_char_p
         _lib = L
@@ -124,12 +148,8 @@ def vmla_workspace_bytes(cfg: vmla_config) -> int:
 
 def vmla_create(cfg: vmla_config, weights: vmla_weights, cache, workspace, rope_freqs=None) -> c_void_p:
     ctx = c_void_p()
-    freqs = None
-    if rope_freqs is not None:
-        arr = (c_float * len(rope_freqs))(*[float(v) for v in rope_freqs])
-        freqs = ctypes.cast(arr, POINTER(c_float))
-    _check(lib().vmla_create(byref(cfg), byref(weights), _ptr(cache), _ptr(workspace), freqs, byref(ctx)),
-           "vmla_create")
+    _check(lib().vmla_create(byref(cfg), byref(weights), _ptr(cache), _ptr(workspace), _freq_array(rope_freqs),
+                             byref(ctx)), "vmla_create")
     return ctx
 
 
@@ -162,6 +182,55 @@ def vmla_reset(ctx) -> None:
 
 def vmla_destroy(ctx) -> None:
     lib().vmla_destroy(ctx)
+
+
+def _freq_array(rope_freqs):
+    if rope_freqs is None:
+        return None
+    arr = (c_float * len(rope_freqs))(*[float(v) for v in rope_freqs])
+    return ctypes.cast(arr, POINTER(c_float))
+
+
+def vmla_dense_cache_bytes(cfg: vmla_config) -> int:
+    return lib().vmla_dense_cache_bytes(byref(cfg))
+
+
+def vmla_dense_workspace_bytes(cfg: vmla_config) -> int:
+    return lib().vmla_dense_workspace_bytes(byref(cfg))
+
+
+def vmla_dense_create(cfg: vmla_config, weights: vmla_dense_weights, cache, workspace, rope_freqs=None) -> c_void_p:
+    ctx = c_void_p()
+    _check(lib().vmla_dense_create(byref(cfg), byref(weights), _ptr(cache), _ptr(workspace),
+                                   _freq_array(rope_freqs), byref(ctx)), "vmla_dense_create")
+    return ctx
+
+
+def vmla_dense_append(ctx, x, stream=None) -> None:
+    _check(lib().vmla_dense_append(ctx, _ptr(x), _stream(stream)), "vmla_dense_append")
+
+
+def vmla_dense_attend(ctx, x, out, stream=None) -> None:
+    _check(lib().vmla_dense_attend(ctx, _ptr(x), _ptr(out), _stream(stream)), "vmla_dense_attend")
+
+
+def vmla_dense_attend_profiled(ctx, x, out, attn_start: int, attn_stop: int, stream=None) -> None:
+    _check(lib().vmla_dense_attend_profiled(ctx, _ptr(x), _ptr(out), attn_start, attn_stop, _stream(stream)),
+           "vmla_dense_attend_profiled")
+
+
+def vmla_dense_cache_state(ctx):
+    n, first, nv = c_int64(), c_int64(), c_int32()
+    _check(lib().vmla_dense_cache_state(ctx, byref(n), byref(first), byref(nv)), "vmla_dense_cache_state")
+    return n.value, first.value, nv.value
+
+
+def vmla_dense_reset(ctx) -> None:
+    _check(lib().vmla_dense_reset(ctx), "vmla_dense_reset")
+
+
+def vmla_dense_destroy(ctx) -> None:
+    lib().vmla_dense_destroy(ctx)
 
 
 def vmla_status_string(code: int) -> str:
@@ -248,6 +317,69 @@ class LatentAttention:
     def close(self):
         if self.ctx:
             vmla_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class DenseAttention:
+    """Dense per-head baseline layer: device weights, per-head K/V ring cache and
+    workspace (torch-allocated), driven through the vmla_dense_* entry points.
+    The geometry has d_nope = d_c = d_q = 0 and d_rope = per-head width."""
+
+    WEIGHT_NAMES = ("w_q", "w_k", "w_v", "w_o")
+
+    def __init__(self, g, weights: dict, device="cuda", attn_workgroups: int = 0, rope_freqs=None,
+                 cache_fill: float | None = None):
+        import torch
+        self.g = g
+        self.dtype = torch_dtype(g)
+        self.cfg = config_from_geometry(g, attn_workgroups)
+        cb, wb = vmla_dense_cache_bytes(self.cfg), vmla_dense_workspace_bytes(self.cfg)
+        if cb == 0 or wb == 0:
+            raise ValueError(f"geometry {g.name} is not accepted by the dense library path")
+        self.w = {}
+        for n in self.WEIGHT_NAMES:
+            t = weights[n]
+            t = torch.as_tensor(t) if not isinstance(t, torch.Tensor) else t
+            self.w[n] = t.to(device=device, dtype=self.dtype).contiguous()
+        self.cache = torch.empty(cb, dtype=torch.uint8, device=device)
+        if cache_fill is not None:
+            self.cache.view(torch.float16).fill_(cache_fill)
+        self.workspace = torch.empty(wb, dtype=torch.uint8, device=device)
+        wts = vmla_dense_weights(**{n: self.w[n].data_ptr() for n in self.WEIGHT_NAMES})
+        self.ctx = vmla_dense_create(self.cfg, wts, self.cache, self.workspace, rope_freqs)
+
+    def _check_x(self, x):
+        g = self.g
+        if tuple(x.shape) != (g.batch, g.n_q, g.hidden) or x.dtype != self.dtype or not x.is_contiguous():
+            raise ValueError(f"x must be contiguous {self.dtype} of shape {(g.batch, g.n_q, g.hidden)}")
+
+    def append(self, x, stream=None):
+        self._check_x(x)
+        vmla_dense_append(self.ctx, x, stream)
+
+    def attend(self, x, out=None, stream=None):
+        import torch
+        self._check_x(x)
+        if out is None:
+            out = torch.empty_like(x)
+        vmla_dense_attend(self.ctx, x, out, stream)
+        return out
+
+    def state(self):
+        return vmla_dense_cache_state(self.ctx)
+
+    def reset(self):
+        vmla_dense_reset(self.ctx)
+
+    def close(self):
+        if self.ctx:
+            vmla_dense_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):

@@ -93,8 +93,14 @@ WAN_ROLLOUT = WAN_LAYER.replace(name="wan1.3b-rollout-30L", layers=30, chunks=20
 
 # Dense per-head baseline: 12 heads x 128 per-head K and V, full 3D-RoPE on the
 # 128-d keys split near-equally over (t, h, w) with t taking the remainder.
-WAN_DENSE = WAN_LAYER.replace(name="wan1.3b-dense", d_nope=0, d_rope=128, d_c=0,
+WAN_DENSE = WAN_LAYER.replace(name="wan1.3b-dense", d_nope=0, d_rope=128, d_c=0, d_q=0,
                               rope_pairs=(22, 21, 21))
+
+# The dense baseline at the Wan widths on the small grid (parity at sizes the
+# oracle finishes in seconds), and a tiny dense layer for the brute force.
+WAN_DENSE_SMALL_GRID = WAN_DENSE.replace(name="wan-dense-grid6x10", grid_h=6, grid_w=10, window_frames=5,
+                                         prefill_chunks=2)
+TINY_DENSE = TINY.replace(name="tiny-dense", d_nope=0, d_rope=16, d_c=0, d_q=0, rope_pairs=(2, 3, 3))
 
 STRESS = {dc: WAN_LAYER.replace(name=f"stress-b4-w42-dc{dc}", batch=4, window_frames=42, d_c=dc,
                                 prefill_chunks=14)
@@ -106,7 +112,8 @@ STRESS = {dc: WAN_LAYER.replace(name=f"stress-b4-w42-dc{dc}", batch=4, window_fr
 WAN_SMALL_GRID = WAN_LAYER.replace(name="wan-widths-grid6x10", grid_h=6, grid_w=10,
                                    window_frames=5, prefill_chunks=2)
 
-GEOMETRIES = {g.name: g for g in (TINY, WAN_LAYER, WAN_ROLLOUT, WAN_DENSE, WAN_SMALL_GRID,
+GEOMETRIES = {g.name: g for g in (TINY, TINY_DENSE, WAN_LAYER, WAN_ROLLOUT, WAN_DENSE, WAN_DENSE_SMALL_GRID,
+                                  WAN_SMALL_GRID,
                                   *STRESS.values())}
 
 

@@ -79,3 +79,39 @@ def attend(g, wts, history, n, chunk_x):
             o += [sum(e[j] / z * V[j][h][d] for j in range(len(K))) for d in range(g.d_v)]
         out.append(_mat_vec(w_o, o))
     return out
+
+
+def attend_dense(g, wts, history, n, chunk_x):
+    """Dense per-head baseline, same loops: q_h = RoPE(W_Q^h x), k_h = RoPE(W_K^h x)
+    on every head channel, v_h = W_V^h x, window-local temporal coordinate."""
+    T = g.grid_h * g.grid_w
+    W, C = g.window_frames, g.chunk_frames
+    tolist = lambda a: [[float(v) for v in row] for row in a]
+    first = n - W if n > W else 0
+    keys_x, keys_pos = [], []
+    for fr in list(range(first, n)) + list(range(n, n + C)):
+        rows = tolist(history[fr]) if fr < n else tolist(chunk_x)[(fr - n) * T:(fr - n + 1) * T]
+        for s in range(T):
+            keys_x.append(rows[s])
+            keys_pos.append((fr - first, s // g.grid_w, s % g.grid_w))
+    w_q, w_k, w_v, w_o = (tolist(getattr(wts, k)) for k in ("w_q", "w_k", "w_v", "w_o"))
+    dh = g.d_nope + g.d_rope
+    K, V = [], []
+    for xj, pj in zip(keys_x, keys_pos):
+        kall, vall = _mat_vec(w_k, xj), _mat_vec(w_v, xj)
+        K.append([_rotate(kall[h * dh:(h + 1) * dh], pj, g.rope_pairs, g.rope_theta) for h in range(g.n_heads)])
+        V.append([vall[h * g.d_v:(h + 1) * g.d_v] for h in range(g.n_heads)])
+    out = []
+    for i, xi in enumerate(tolist(chunk_x)):
+        pos = (n + i // T - first, (i % T) // g.grid_w, (i % T) % g.grid_w)
+        qall = _mat_vec(w_q, xi)
+        o = []
+        for h in range(g.n_heads):
+            q = _rotate(qall[h * dh:(h + 1) * dh], pos, g.rope_pairs, g.rope_theta)
+            s = [sum(q[d] * K[j][h][d] for d in range(dh)) / math.sqrt(dh) for j in range(len(K))]
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            z = sum(e)
+            o += [sum(e[j] / z * V[j][h][d] for j in range(len(K))) for d in range(g.d_v)]
+        out.append(_mat_vec(w_o, o))
+    return out

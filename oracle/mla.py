@@ -213,10 +213,12 @@ def chunk_latents(g, wts, x, frame0: int, dtype=np.float64):
 
 
 # ----------------------------------------------------------------------------- dense baseline
-def attend_dense(g, wts, history, n: int, chunk_x, query_tokens=None, dtype=np.float64):
+def attend_dense(g, wts, history, n: int, chunk_x, query_tokens=None, dtype=np.float64,
+                 return_scores: bool = False):
     """Dense per-head attention over the same window: K_h = RoPE(W_K^h x) on all
     head_dim channels, V_h = W_V^h x, same chunk-causal visibility and window-local
-    temporal coordinate (the baseline layout of section 1 / appendix C.1)."""
+    temporal coordinate (the baseline layout of section 1 / appendix C.1).
+    With return_scores, also the pre-softmax scores [n_heads, Nq, Nk]."""
     f = lambda a: np.asarray(a, dtype=dtype)
     T = g.grid_h * g.grid_w
     first, cached, chunk = visible_frames(n, g.window_frames, g.chunk_frames)
@@ -232,7 +234,11 @@ def attend_dense(g, wts, history, n: int, chunk_x, query_tokens=None, dtype=np.f
     qc = token_coordinates(np.array(chunk) - first, g.grid_h, g.grid_w)[qi]
     q = rope_rotate((xq @ f(wts.w_q).T).reshape(-1, g.n_heads, dh), qc, g.rope_pairs, freqs)
     o = np.empty((len(qi), g.n_heads, g.d_v), dtype=dtype)
+    sc = []
     for h in range(g.n_heads):
-        p = _softmax_rows((q[:, h] @ k[:, h].T) / np.sqrt(dh))
-        o[:, h] = p @ v[:, h]
-    return o.reshape(len(qi), -1) @ f(wts.w_o).T
+        s = (q[:, h] @ k[:, h].T) / np.sqrt(dh)
+        o[:, h] = _softmax_rows(s) @ v[:, h]
+        if return_scores:
+            sc.append(s)
+    u = o.reshape(len(qi), -1) @ f(wts.w_o).T
+    return (u, np.stack(sc)) if return_scores else u

@@ -135,3 +135,59 @@ def test_null_ctx_rejected():
     assert L.vmla_reset(None) == vmla.STATUS["VMLA_ERR_NULL"]
     assert L.vmla_cache_state(None, None, None, None) == vmla.STATUS["VMLA_ERR_NULL"]
     assert L.vmla_attend(None, FAKE, FAKE, None) == vmla.STATUS["VMLA_ERR_NULL"]
+    L = vmla.lib()
+    assert L.vmla_dense_reset(None) == vmla.STATUS["VMLA_ERR_NULL"]
+    assert L.vmla_dense_cache_state(None, None, None, None) == vmla.STATUS["VMLA_ERR_NULL"]
+    assert L.vmla_dense_attend(None, FAKE, FAKE, None) == vmla.STATUS["VMLA_ERR_NULL"]
+    assert L.vmla_dense_append(None, FAKE, None) == vmla.STATUS["VMLA_ERR_NULL"]
+
+
+# ----------------------------------------------------------------------------- dense baseline
+def test_dense_cache_and_workspace_bytes():
+    g = wl.WAN_DENSE
+    P = (21 * 1560 + 63) // 64 * 64  # ring keys per (stream, head), padded to the 64-key tile
+    assert P == 32768
+    assert vmla.vmla_dense_cache_bytes(_cfg(g)) == 12 * P * (128 + 128) * 2  # 201.3 MB: keys + values, 16-bit
+    ws = vmla.vmla_dense_workspace_bytes(_cfg(g))
+    S = (4680 + 63) // 64 * 64
+    assert ws >= 12 * (4680 * 128 + 2 * S * 128) * 2 + 4680 * 1536 * 2
+    # the latent entry points refuse the dense geometry and vice versa
+    assert vmla.vmla_cache_bytes(_cfg(g)) == 0
+    assert vmla.vmla_dense_cache_bytes(_cfg(wl.WAN_LAYER)) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_c", 192, "VMLA_ERR_CONFIG"), ("d_q", 768, "VMLA_ERR_CONFIG"), ("d_nope", 8, "VMLA_ERR_CONFIG"),
+    ("rope_pairs_w", 20, "VMLA_ERR_CONFIG"), ("batch", 0, "VMLA_ERR_CONFIG"),
+    ("d_v", 64, "VMLA_ERR_UNSUPPORTED"), ("dtype", vmla.VMLA_DTYPE_F32, "VMLA_ERR_UNSUPPORTED"),
+])
+def test_dense_invalid_configs_rejected(field, value, code):
+    c = _cfg(wl.WAN_DENSE, **{field: value})
+    assert vmla.vmla_dense_cache_bytes(c) == 0 and vmla.vmla_dense_workspace_bytes(c) == 0
+    w = vmla.vmla_dense_weights(w_q=FAKE, w_k=FAKE + 256, w_v=FAKE + 512, w_o=FAKE + 768)
+    with pytest.raises(vmla.VmlaError) as e:
+        vmla.vmla_dense_create(c, w, FAKE, FAKE)
+    assert e.value.code == vmla.STATUS[code]
+
+
+def test_dense_create_and_argument_checks():
+    c = _cfg(wl.WAN_DENSE)
+    names = vmla.DenseAttention.WEIGHT_NAMES
+    good = {n: FAKE + 256 * i for i, n in enumerate(names)}
+    for n in names:
+        for v, code in [(0, "VMLA_ERR_NULL"), (FAKE + 8, "VMLA_ERR_ALIGN")]:
+            with pytest.raises(vmla.VmlaError) as e:
+                vmla.vmla_dense_create(c, vmla.vmla_dense_weights(**{**good, n: v}), FAKE, FAKE)
+            assert e.value.code == vmla.STATUS[code]
+    ctx = vmla.vmla_dense_create(c, vmla.vmla_dense_weights(**good), FAKE, FAKE)
+    try:
+        for f, code in [(lambda: vmla.vmla_dense_attend(ctx, 0, FAKE, 0), "VMLA_ERR_NULL"),
+                        (lambda: vmla.vmla_dense_attend(ctx, FAKE, FAKE + 2, 0), "VMLA_ERR_ALIGN"),
+                        (lambda: vmla.vmla_dense_append(ctx, FAKE + 4, 0), "VMLA_ERR_ALIGN"),
+                        (lambda: vmla.vmla_dense_attend_profiled(ctx, FAKE, FAKE, 0, 0, 0), "VMLA_ERR_NULL")]:
+            with pytest.raises(vmla.VmlaError) as e:
+                f()
+            assert e.value.code == vmla.STATUS[code]
+        assert vmla.vmla_dense_cache_state(ctx) == (0, 0, 0)
+    finally:
+        vmla.vmla_dense_destroy(ctx)

@@ -1,0 +1,101 @@
+"""Parity of the dense per-head baseline (through the vmla_dense_* C ABI) with
+the CPU oracle's attend_dense.
+
+Same bar and tolerance derivation as the latent path (gpu_harness): keys and
+queries are rounded to bf16 once, values to fp16, probabilities to fp16.
+Cases: the Wan widths (12 heads x 128) on a 6x10 grid over empty, partial,
+full and wrapped windows with NaN canaries in every unwritten cache byte, two
+input scalings, batched streams, stream-K cuts, and the full Wan-1.3B layer
+(21 cached frames + a 3-frame chunk) on sampled query tokens.
+"""
+import numpy as np
+import pytest
+
+from gpu_harness import assert_parity, to_dev, to_np
+from mla_latent_kv_vmla_amd import vmla, workloads as wl
+from oracle import mla
+
+pytestmark = pytest.mark.gpu
+
+SMALL = wl.WAN_DENSE_SMALL_GRID
+
+
+def _print_case(*a):
+    print("case:", *a, flush=True)
+
+
+class DenseRollout:
+    def __init__(self, g, mode="literal", seed=0, attn_workgroups=0):
+        import torch
+        self.g, self.mode, self.seed = g, mode, seed
+        self.w = wl.dense_weights(g, seed=seed, mode=mode)
+        self.dev = vmla.DenseAttention(g, {k: to_dev(v, g) for k, v in vars(self.w).items()},
+                                       attn_workgroups=attn_workgroups)
+        self.dev.cache.fill_(255)      # NaN in both bf16 and fp16: reading an unwritten byte shows
+        self.dev.workspace.fill_(255)
+        torch.cuda.synchronize()
+        self.hist = [dict() for _ in range(g.batch)]
+        self.n = 0
+
+    def x(self, chunk, step=0):
+        return wl.hidden_states(self.g, chunk=chunk, step=step, seed=self.seed, mode=self.mode)
+
+    def append(self, x_np):
+        g = self.g
+        self.dev.append(to_dev(x_np, g))
+        for b in range(g.batch):
+            fr = x_np[b].reshape(g.chunk_frames, g.tokens_per_frame, g.hidden)
+            for i in range(g.chunk_frames):
+                self.hist[b][self.n + i] = fr[i]
+        self.n += g.chunk_frames
+
+    def check(self, got_b, x_np, b=0, query_tokens=None, what=""):
+        ref, s = mla.attend_dense(self.g, self.w, self.hist[b], self.n, x_np[b], query_tokens=query_tokens,
+                                  return_scores=True)
+        return assert_parity(got_b, ref, what, float(s.std(axis=-1).mean()), self.g.dtype)
+
+
+def _dense_rollout(g, mode, n_chunks, attn_workgroups=0):
+    r = DenseRollout(g, mode=mode, attn_workgroups=attn_workgroups)
+    for k in range(n_chunks):
+        x = r.x(chunk=100 + k)
+        _print_case("dense attend", g.name, mode, "n=", r.n, "G=", attn_workgroups)
+        got = to_np(r.dev.attend(to_dev(x, g)))
+        for b in range(g.batch):
+            ma, mr = r.check(got[b], x, b, what=f"{g.name} {mode} n={r.n} b={b}")
+            print(f"  b={b}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+        r.append(r.x(chunk=k))
+        assert r.dev.state()[0] == r.n
+
+
+@pytest.mark.parametrize("mode", ["literal", "unit", "sharp"])
+def test_dense_small_grid_all_window_states(mode):
+    # T = 60, W = 5, C = 3: n = 0 (chunk only), 3 (partial), 6 and 9 (full, wrapped);
+    # 180 queries per head (ragged row block), 180..480 keys (ragged ring and chunk tiles)
+    _dense_rollout(SMALL, mode, n_chunks=4)
+
+
+@pytest.mark.parametrize("G", [1, 7, 100000])
+def test_dense_stream_k_splits(G):
+    _dense_rollout(SMALL, "sharp", n_chunks=3, attn_workgroups=G)
+
+
+def test_dense_batched_streams():
+    _dense_rollout(SMALL.replace(batch=2, window_frames=4), "sharp", n_chunks=3)
+
+
+def test_dense_wan_layer_full_size_sampled():
+    """21 cached frames (32,760 keys per head) + a 3-frame chunk (4,680 queries x
+    12 heads), default launch configuration."""
+    g = wl.WAN_DENSE
+    _print_case("dense wan-full")
+    r = DenseRollout(g, mode="literal")
+    for k in range(g.prefill_chunks):
+        r.append(r.x(chunk=k))
+    x = r.x(chunk=g.prefill_chunks)
+    got = to_np(r.dev.attend(to_dev(x, g)))
+    assert np.all(np.isfinite(got))
+    q = np.unique(np.concatenate([np.arange(8), np.arange(g.n_q - 8, g.n_q),
+                                  np.random.default_rng(0).choice(g.n_q, 32, replace=False)]))
+    ma, mr = r.check(got[0][q], x, 0, q, "dense wan-full literal")
+    print(f"dense wan-full: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)

@@ -301,3 +301,43 @@ def test_seeded_inputs_are_deterministic_and_distinct():
     v = w.w_dq.view(np.uint32)
     assert np.all((v & 0xFFFF) == 0)
     assert abs(w.w_dq.std() * math.sqrt(1536) - 1.0) < 0.02
+
+
+# ----------------------------------------------------------------------------- dense baseline
+def _tiny_dense_inputs(n, mode="unit", seed=0):
+    g = wl.TINY_DENSE
+    w = wl.dense_weights(g, seed=seed, mode=mode)
+    hist = {f: wl.hidden_states(g, chunk=f, seed=seed, mode=mode)[0] for f in range(n)}  # one frame per chunk
+    chunk = wl.hidden_states(g, chunk=1000 + n, seed=seed, mode=mode)[0]
+    return g, w, hist, chunk
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 5])
+@pytest.mark.parametrize("mode", ["unit", "sharp"])
+def test_dense_brute_force_matches_numpy(n, mode):
+    """The dense baseline against the scalar-loop formulation (complex rotary pairs)."""
+    g, w, hist, chunk = _tiny_dense_inputs(n, mode)
+    u = mla.attend_dense(g, w, hist, n, chunk)
+    ub = np.array(brute.attend_dense(g, w, hist, n, chunk))
+    np.testing.assert_allclose(u, ub, rtol=1e-12, atol=1e-14 * np.abs(ub).max())
+
+
+def test_dense_zero_query_gives_mean_value():
+    """W_Q = 0 makes every score 0: each head returns the mean of its visible values."""
+    g, w, hist, chunk = _tiny_dense_inputs(5)
+    w.w_q = np.zeros_like(w.w_q)
+    u = mla.attend_dense(g, w, hist, 5, chunk)
+    xk = np.concatenate([hist[3], hist[4], chunk]).astype(np.float64)
+    o = (xk @ w.w_v.T.astype(np.float64)).mean(axis=0)
+    np.testing.assert_allclose(u, np.tile(o @ w.w_o.T.astype(np.float64), (16, 1)), rtol=1e-12)
+
+
+def test_dense_window_excludes_evicted_frames():
+    g, w, hist, chunk = _tiny_dense_inputs(5, "sharp")
+    u = mla.attend_dense(g, w, hist, 5, chunk)
+    h2 = dict(hist)
+    h2[2] = hist[0] * 3.0  # frame 2 left the 2-frame window at n = 5
+    np.testing.assert_array_equal(mla.attend_dense(g, w, h2, 5, chunk), u)
+    h3 = dict(hist)
+    h3[3] = hist[0] * 3.0  # oldest visible frame
+    assert np.abs(mla.attend_dense(g, w, h3, 5, chunk) - u).max() > 1e-6 * np.abs(u).max()
