@@ -28,10 +28,13 @@
 // already in LDS layout (latent: the value is the key's first DV channels), or
 // straight from value rows [f][key] that the dense cache stores transposed.
 // LDS layouts (per stage; two stages in two distinct arrays):
-//   Ks  [KTILE][D + 16 B]: 16-B chunk q of row r lives at chunk q ^ ((r >> 4) & 3)
+//   Ks  [KTILE][D + 16 B]
 //   V^T [DVP][KTILE + 16 B]: within every 16-key group the key index has bits 2
 //       and 3 swapped, so the 8 keys a lane feeds to one value MFMA are one
-//       contiguous 16-B read.  Both layouts read without bank conflicts.
+//       contiguous 16-B read.
+// A 128-bit LDS read is served 16 lanes at a time from 64 four-byte banks; with
+// the 16-B row pad the 16 rows one such group reads start in 16 distinct
+// 16-B bank groups, so both layouts read without bank conflicts.
 //
 // Numerics.  With bf16 storage the value product runs on fp16 operands: values
 // are held as fp16 (latents converted bf16 -> fp16 by the pre-pass, exact in
@@ -77,6 +80,10 @@ template <typename T> struct FlashArgs {
 };
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+#ifndef VMLA_FRAG_AHEAD
+#define VMLA_FRAG_AHEAD 4
+#endif
+constexpr int kAhead = VMLA_FRAG_AHEAD;  // LDS fragment reads in flight ahead of their MFMA
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
 
@@ -99,7 +106,6 @@ template <typename T, int D_, int DV, int KTILE> struct TileGeo {
   static constexpr int CI = (CPOS + 63) / 64;
   static constexpr size_t IMG_BYTES = (size_t)CPOS * 16;
   static_assert(D % VEC == 0 && DV % VEC == 0 && DV <= D, "unsupported widths");
-  static_assert((D / VEC) % 4 == 0, "chunk swizzle works within groups of 4 chunks");
   static_assert(KTILE % 32 == 0 && KTILE / VEC < 256, "bad tile");
   __device__ static int perm_group(int kg) { return (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1); }
 };
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(256) void latent_value_tiles(FlashArgs<T> p) {
 // VROWS = true: from value rows val0/val1 ([f][key], keys permuted within
 // 16-key groups, zero past the segment's end up to the tile boundary).
 template <typename T, int D, int DV, int KTILE, int NW, int NB, bool VROWS>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(8 / NW, 8 / NW)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void flash_attn_kernel(FlashArgs<T> p) {
   using G = TileGeo<T, D, DV, KTILE>;
   using VT = typename G::VT;
@@ -185,18 +191,18 @@ void flash_attn_kernel(FlashArgs<T> p) {
   const float NEG_INF = -__builtin_huge_valf();
 
   // This lane's source in each of this wave's LDS-DMA loads of a stage, as an
-  // element offset from the tile's base: row-major key tile (row r, swizzled
-  // chunk) packed as r << 12 | offset in the row; value rows (channel f, chunk)
-  // packed as f << 8 | offset in the row; images: byte offset.
+  // element offset from the tile's base: row-major key tile (row r, chunk)
+  // packed as r << 12 | offset in the row; value rows (channel f, chunk) packed
+  // as f << 8 | offset in the row; images: byte offset.  The pad chunk of a row
+  // loads any valid chunk.
   uint32_t slot[NI_W];
 #pragma unroll
   for (int k = 0; k < NI_W; ++k) {
     const int idx = wave + k * NW;
     if (idx < G::KI) {
       const int pos = idx * 64 + lane;
-      const int r = pos / G::KCH, phys = pos % G::KCH;
-      const int q = phys < G::KCH - 1 ? (phys ^ ((r >> 4) & 3)) : 0;  // pad slot: any valid chunk
-      slot[k] = ((uint32_t)r << 12) | (uint32_t)(q * VEC);
+      const int r = pos / G::KCH, c = pos % G::KCH;
+      slot[k] = ((uint32_t)r << 12) | (uint32_t)((c < G::KCH - 1 ? c : 0) * VEC);
     } else {
       const int pos = (idx - G::KI) * 64 + lane;
       if constexpr (VROWS) {
@@ -209,17 +215,23 @@ void flash_attn_kernel(FlashArgs<T> p) {
   }
 
   // Issue the LDS-DMA loads of tile t of stream s (both layouts) into stage `buf`.
+  // Key rows past the segment's end read as zero (buffer range check) and are
+  // masked out of the scores.
   auto issue_tile = [&](int s, int t, T* buf) {
     int g, kbase, len;
     tile_segment<T, KTILE>(p, t, g, kbase, len);
-    const char* kb = reinterpret_cast<const char*>(g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0);
-    const char* vb;
-    int vrs = 0;
+    const auto krs = raw_rsrc(g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0,
+                              (uint32_t)len * (uint32_t)(D * sizeof(T)));
+    __amdgpu_buffer_rsrc_t vrs;
+    uint32_t vrow = 0, vbase = 0;
     if constexpr (VROWS) {
-      vb = static_cast<const char*>(g ? p.val1 : p.val0) + ((g ? p.val_ss1 : p.val_ss0) * s + kbase) * sizeof(VT);
-      vrs = g ? p.val_rs1 : p.val_rs0;
+      const long ss = g ? p.val_ss1 : p.val_ss0;
+      vrs = raw_rsrc(static_cast<const VT*>(g ? p.val1 : p.val0) + ss * s, (uint32_t)(ss * sizeof(VT)));
+      vrow = (uint32_t)(g ? p.val_rs1 : p.val_rs0);
+      vbase = (uint32_t)kbase;
     } else {
-      vb = static_cast<const char*>(p.val0) + ((size_t)s * p.KT + t) * G::IMG_BYTES;
+      vrs = raw_rsrc(static_cast<const char*>(p.val0) + ((size_t)s * p.KT + t) * G::IMG_BYTES,
+                     (uint32_t)G::IMG_BYTES);
     }
 #pragma unroll
     for (int k = 0; k < NI_W; ++k) {
@@ -227,17 +239,16 @@ void flash_attn_kernel(FlashArgs<T> p) {
       if (idx < G::KI) {
         const int pos = idx * 64 + lane;
         if (G::KPOS % 64 == 0 || pos < G::KPOS) {
-          const int r = min(kbase + (int)(slot[k] >> 12), len - 1);
-          const uint32_t off = ((uint32_t)r * D + (slot[k] & 0xFFFu)) * (uint32_t)sizeof(T);
-          lds_dma16(kb + off, buf + idx * 64 * VEC);
+          const uint32_t row = (uint32_t)kbase + (slot[k] >> 12);
+          lds_dma16(krs, (row * D + (slot[k] & 0xFFFu)) * (uint32_t)sizeof(T), buf + idx * 64 * VEC);
         }
       } else if (idx < NI) {
         const int ci = idx - G::KI, pos = ci * 64 + lane;
         if (G::CPOS % 64 == 0 || pos < G::CPOS) {
           uint32_t off;
-          if constexpr (VROWS) off = ((slot[k] >> 8) * (uint32_t)vrs + (slot[k] & 0xFFu)) * (uint32_t)sizeof(VT);
+          if constexpr (VROWS) off = ((slot[k] >> 8) * vrow + vbase + (slot[k] & 0xFFu)) * (uint32_t)sizeof(VT);
           else off = slot[k];
-          lds_dma16(vb + off, buf + G::KS_EL + ci * 64 * VEC);
+          lds_dma16(vrs, off, buf + G::KS_EL + ci * 64 * VEC);
         }
       }
     }
@@ -285,21 +296,28 @@ void flash_attn_kernel(FlashArgs<T> p) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
         const int r = 32 * kb + l32;
-        if constexpr (HALF) {  // chunk 2ks+h, swizzled: two per-lane bases, immediate offsets
-          const int sw = (r >> 4) & 3;
-          const T* b0 = Ks + r * KS + ((h32 ^ sw) * VEC);
-          const T* b1 = Ks + r * KS + (((2 + h32) ^ sw) * VEC);
+        if constexpr (HALF) {  // chunk 2ks+h of row r: one per-lane base, immediate offsets
+          const T* kb0 = Ks + r * KS + h32 * VEC;
+          // fragments are read kAhead steps before their MFMA; the scheduling
+          // barriers keep the compiler from sinking each read onto its use
+          auto kfrag = [&](int ks) { return MF::load(kb0 + 2 * VEC * ks); };
+          typename MF::Frag kq[kAhead];
+#pragma unroll
+          for (int i = 0; i < kAhead && i < NKS; ++i) kq[i] = kfrag(i);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            const auto a = MF::load((ks & 1 ? b1 : b0) + 4 * VEC * (ks >> 1));
+            __builtin_amdgcn_sched_barrier(0);
+            const auto a = kq[ks % kAhead];
+            if (ks + kAhead < NKS) kq[ks % kAhead] = kfrag(ks + kAhead);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sc[nb] = MF::mma(a, qf[nb][ks], sc[nb]);
           }
+          __builtin_amdgcn_sched_barrier(0);
         } else {
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const int e = ks * 2 * KPL + KPL * h32;
-            const auto a = MF::load(&Ks[r * KS + (((e / VEC) ^ ((r >> 4) & 3)) * VEC) + e % VEC]);
+            const auto a = MF::load(&Ks[r * KS + e]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sc[nb] = MF::mma(a, qf[nb][ks], sc[nb]);
           }
@@ -355,15 +373,23 @@ void flash_attn_kernel(FlashArgs<T> p) {
             for (int u = 0; u < 2; ++u)
 #pragma unroll
               for (int j = 0; j < 8; ++j) pf[nb][u][j] = (f16)sc[nb][8 * u + j];
+          constexpr int NV = 2 * NFB;
+          auto vfrag = [&](int i) {
+            return *reinterpret_cast<const f16x8*>(Ct + 32 * (i >> 1) * CS + 32 * kb + 16 * (i & 1) + 8 * h32);
+          };
+          f16x8 vq[kAhead];
 #pragma unroll
-          for (int fb = 0; fb < NFB; ++fb)
+          for (int i = 0; i < kAhead && i < NV; ++i) vq[i] = vfrag(i);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const f16x8 a = *reinterpret_cast<const f16x8*>(Ct + 32 * fb * CS + 32 * kb + 16 * u + 8 * h32);
+          for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const f16x8 a = vq[i % kAhead];
+            if (i + kAhead < NV) vq[i % kAhead] = vfrag(i + kAhead);
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
-                o[nb][fb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][u], o[nb][fb], 0, 0, 0);
-            }
+            for (int nb = 0; nb < NB; ++nb)
+              o[nb][i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][i & 1], o[nb][i >> 1], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         } else {
 #pragma unroll
           for (int fb = 0; fb < NFB; ++fb)

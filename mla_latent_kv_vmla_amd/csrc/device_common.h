@@ -56,11 +56,21 @@ __device__ inline void store4(float* p, float a, float b, float c, float d) {
 // 16-byte global load / zero of one vector of storage elements.
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// LDS-DMA load: each active lane copies 16 bytes from `src` to LDS; lane L's
-// bytes land at lds_wave_base + 16*L (lds_wave_base must be wave-uniform).
-// Completion is tracked by the vector-memory counter.
-__device__ inline void lds_dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// Buffer resource over `bytes` bytes at `base` for raw byte-offset loads; the
+// hardware range check returns zero for any load past the end.
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// LDS-DMA load through a buffer resource: each active lane copies the 16 bytes
+// at byte offset `voff` of the buffer to LDS; lane L's bytes land at
+// lds_wave_base + 16*L (lds_wave_base must be wave-uniform).  Completion is
+// tracked by the vector-memory counter only (the MUBUF form, unlike the FLAT
+// one, leaves the LDS counter to ordinary LDS reads, so those can be waited
+// for one at a time).
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0,
+                                           0, 0);
 }
 
 // 3D-RoPE description: per complex pair p its axis (t, h, w by index ranges)
