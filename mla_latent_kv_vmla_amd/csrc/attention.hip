@@ -85,7 +85,17 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 #endif
 constexpr int kAhead = VMLA_FRAG_AHEAD;  // LDS fragment reads in flight ahead of their MFMA
 
-__device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
+// Max and sum over the lane pair (l, l ^ 32) that shares one query row: one
+// v_permlane32_swap exchanges the two half-waves, and combining both of its
+// results gives the pair's value in either lane.
+__device__ inline float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Compile-time geometry of one instantiation: score width D, value width DV.
 template <typename T, int D_, int DV, int KTILE> struct TileGeo {
@@ -322,7 +332,10 @@ void flash_attn_kernel(FlashArgs<T> p) {
             for (int nb = 0; nb < NB; ++nb) sc[nb] = MF::mma(a, qf[nb][ks], sc[nb]);
           }
         }
+        // the tail mask and the rescale below are rare: the empty volatile asm
+        // keeps each a real (uniform) branch instead of code run on every block
         if (kbase + 32 * kb + 32 > len) {
+          asm volatile("");
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr)
             if (kbase + 32 * kb + 8 * (rr >> 2) + 4 * h32 + (rr & 3) >= len)
@@ -338,11 +351,12 @@ void flash_attn_kernel(FlashArgs<T> p) {
           float m = sc[nb][0];
 #pragma unroll
           for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, sc[nb][rr]);
-          mx[nb] = fmaxf(m, xor32(m));
+          mx[nb] = pair_max(m);
           need[nb] = mx[nb] > m_run[nb] + kRescaleSlack;
           any_need |= need[nb];
         }
         if (__any(any_need)) {
+          asm volatile("");
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const float mnew = need[nb] ? mx[nb] : m_run[nb];
@@ -428,7 +442,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
     T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const float l_tot = l_run[nb] + xor32(l_run[nb]);
+      const float l_tot = pair_sum(l_run[nb]);
       const int qrow = row0 + 32 * nb + l32;
       if (full) {
         if (qrow < p.R) {
