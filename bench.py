@@ -83,7 +83,7 @@ class HipEvents:
 
 
 def pmc_summary_path(g) -> str:
-    return os.path.join(ROOT, "profiles", f"attn_{g.name}_pmc.json")
+    return os.path.join(ROOT, "profiles", f"flash_attn_{g.name}_pmc.json")
 
 
 def traffic_from_counters(g):
@@ -129,7 +129,8 @@ def main():
     ap.add_argument("--workload", default="wan1.3b-layer")
     ap.add_argument("--steps-per-chunk", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1560)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="query tokens the CPU oracle baseline times (0 = the whole attend call)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after timing, run plain device copies of this size (counter calibration)")
     args = ap.parse_args()
@@ -245,7 +246,7 @@ def main():
         "wall_s_timed_region": wall,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(g, w, hist, n_prefill, xs_np[0][0], args.cpu_sample_tokens)
+        res["cpu_baseline"] = cpu_baseline(g, w, hist, n_prefill, xs_np[0][0], args.cpu_sample_tokens or g.n_q)
     for a, b in ev_pairs:
         ev.destroy(a)
         ev.destroy(b)

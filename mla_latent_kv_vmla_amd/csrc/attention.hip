@@ -265,14 +265,26 @@ void flash_attn_kernel(FlashArgs<T> p) {
   };
 
   const long I = (long)p.S * p.RB * p.KT;
-  const long it0 = (long)blockIdx.x * I / p.G, it1 = (long)(blockIdx.x + 1) * I / p.G;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2); the virtual index gives the workgroups of one XCD one contiguous share
+  // of the work, so they stream the same streams' keys.
+  const int vw = p.G % 8 == 0 ? (int)(blockIdx.x % 8) * (p.G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const long it0 = (long)vw * I / p.G, it1 = (long)(vw + 1) * I / p.G;
 
-  for (long it = it0; it < it1;) {
-    const long unit = it / p.KT;
-    const int kt0 = (int)(it % p.KT);
-    const int kt1 = (int)((long)kt0 + (it1 - it) < p.KT ? (long)kt0 + (it1 - it) : p.KT);
+  // The range covers pieces of consecutive row blocks: the first may start and
+  // the last may end inside a row block.  The last piece (which starts at key
+  // tile 0) is processed first, so every workgroup sweeps the key tiles in
+  // increasing order from near tile 0 and the workgroups sharing an L2 stay
+  // within a few dozen tiles of one another.
+  const long u_first = it0 / p.KT;
+  const int npieces = (int)((it1 - 1) / p.KT - u_first + 1);
+  for (int k = 0; k < npieces; ++k) {
+    const int piece = npieces > 1 ? (k == 0 ? npieces - 1 : k - 1) : 0;
+    const long unit = u_first + piece;
+    const int kt0 = piece == 0 ? (int)(it0 % p.KT) : 0;
+    const int kt1 = piece == npieces - 1 ? (int)((it1 - 1) % p.KT) + 1 : p.KT;
     const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
-    const bool first_piece = (it == it0);
+    const bool first_piece = piece == 0;
     const int row0 = rb * (NW * RW) + wave * RW;
 
     typename MF::Frag qf[NB][NKS];
@@ -460,7 +472,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
         }
       } else if (row0 < p.R) {
         const long slot_row =
-            (long)(2 * blockIdx.x + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * RW + 32 * nb + l32;
+            (long)(2 * vw + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * RW + 32 * nb + l32;
         float* po = p.part_o + slot_row * DV;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
@@ -477,14 +489,13 @@ void flash_attn_kernel(FlashArgs<T> p) {
         }
       }
     }
-    it += kt1 - kt0;
   }
 }
 
 // Merge the partial states of every row block that was split across workgroups.
-// Workgroups w0..w1 hold the pieces of row block `unit`; every piece is its
-// workgroup's first (slot 2w) except possibly w0's, which is its second
-// (slot 2w0+1) when w0 started inside an earlier row block.
+// Workgroups w0..w1 (virtual indices) hold the pieces of row block `unit`;
+// every piece is its workgroup's first (slot 2w) except possibly w0's, which is
+// its second (slot 2w0+1) when w0 started inside an earlier row block.
 template <typename T, int DV, int ROWS>
 __global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
   constexpr int SLICE = 16;  // rows per workgroup: many small workgroups hide load latency
