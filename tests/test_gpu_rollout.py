@@ -1,0 +1,105 @@
+"""Full-size lifecycle tests through the C ABI.
+
+Rollout (the paper's streaming setting, appendix D.1/D.5): 30 latent-attention
+layers, each with its own seeded weights and ring cache, advance through 20
+chunks; per chunk every layer runs 4 frozen-cache attend calls and then appends
+the last step's hidden states (2,400 attends + 600 appends, 30 x 14.7 MB of
+cache).  Hidden states of layer l, chunk k, step s are the seeded base tensor
+of (k, s) rolled by 37*l tokens (same distribution, cheap to rebuild on both
+sides).  Sampled (layer, chunk) attends -- empty, partial, just-full and
+wrapped windows -- are compared with the oracle on sampled query tokens.
+
+Stress (B = 4 streams, 42-frame window = 65,520 cached keys, d_c in
+{96, 192, 448}): prefill the ring, then one attend, compared on sampled
+query tokens of two streams.
+"""
+import numpy as np
+import pytest
+
+from gpu_harness import assert_parity, to_dev, to_np
+from mla_latent_kv_vmla_amd import vmla, workloads as wl
+from oracle import mla
+
+pytestmark = pytest.mark.gpu
+
+ROLL = 37
+
+
+def _case(*a):
+    print("case:", *a, flush=True)
+
+
+def test_rollout_30_layers_20_chunks():
+    import torch
+    g = wl.WAN_ROLLOUT
+    L, K, S = g.layers, g.chunks, g.steps
+    T = g.tokens_per_frame
+    base = {}
+
+    def x_np(k, s):
+        if (k, s) not in base:
+            base[(k, s)] = wl.hidden_states(g, chunk=k, step=s)[0]
+        return base[(k, s)]
+
+    _case("rollout setup", L, "layers")
+    weights = [wl.latent_weights(g, layer=l) for l in range(L)]
+    layers = [vmla.LatentAttention(g, {n: to_dev(v, g) for n, v in weights[l].as_dict().items()},
+                                   cache_fill=float("nan")) for l in range(L)]
+    checks = {(0, 0), (0, 4), (17, 6), (29, 7), (17, 13), (0, 19), (29, 19)}  # (layer, chunk)
+    q = np.unique(np.concatenate([np.arange(4), np.random.default_rng(1).choice(g.n_q, 20, replace=False)]))
+    out = torch.empty(g.batch, g.n_q, g.hidden, dtype=torch.bfloat16, device="cuda")
+    pending = []
+    for k in range(K):
+        xd = [to_dev(x_np(k, s), g) for s in range(S)]
+        for l in range(L):
+            for s in range(S):
+                xl = torch.roll(xd[s], shifts=ROLL * l, dims=0).unsqueeze(0).contiguous()
+                layers[l].attend(xl, out=out)
+                if (l, k) in checks and s == 1:
+                    pending.append((l, k, to_np(out)[0][q]))
+            layers[l].append(torch.roll(xd[S - 1], shifts=ROLL * l, dims=0).unsqueeze(0).contiguous())
+        torch.cuda.synchronize()
+        _case("rollout chunk", k, "done")
+    for l in range(L):
+        assert layers[l].state() == (K * g.chunk_frames, K * g.chunk_frames - g.window_frames, g.window_frames)
+    for l, k, got in pending:
+        hist = {}
+        for kk in range(k):
+            fr = np.roll(x_np(kk, S - 1), ROLL * l, axis=0).reshape(g.chunk_frames, T, g.hidden)
+            for i in range(g.chunk_frames):
+                hist[kk * g.chunk_frames + i] = fr[i]
+        xq = np.roll(x_np(k, 1), ROLL * l, axis=0)
+        n = k * g.chunk_frames
+        ref = mla.attend(g, weights[l], hist, n, xq, query_tokens=q)
+        ma, mr = assert_parity(got, ref, f"rollout layer {l} chunk {k}")
+        print(f"  layer {l} chunk {k} (n={n}): max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+    for lay in layers:
+        lay.close()
+
+
+@pytest.mark.parametrize("dc", [96, 192, 448])
+def test_stress_b4_w42_full_size(dc):
+    g = wl.STRESS[dc]
+    _case("stress", g.name)
+    w = wl.latent_weights(g, mode="literal")
+    layer = vmla.LatentAttention(g, {n: to_dev(v, g) for n, v in w.as_dict().items()}, cache_fill=float("nan"))
+    hist = [dict() for _ in range(g.batch)]
+    for k in range(g.prefill_chunks):
+        xk = wl.hidden_states(g, chunk=k)
+        layer.append(to_dev(xk, g))
+        for b in range(g.batch):
+            fr = xk[b].reshape(g.chunk_frames, g.tokens_per_frame, g.hidden)
+            for i in range(g.chunk_frames):
+                hist[b][k * g.chunk_frames + i] = fr[i]
+    n = layer.state()[0]
+    assert n == g.window_frames
+    x = wl.hidden_states(g, chunk=g.prefill_chunks)
+    got = to_np(layer.attend(to_dev(x, g)))
+    assert np.all(np.isfinite(got))
+    q = np.unique(np.concatenate([np.arange(4), np.arange(g.n_q - 4, g.n_q),
+                                  np.random.default_rng(dc).choice(g.n_q, 16, replace=False)]))
+    for b in (0, g.batch - 1):
+        ref = mla.attend(g, w, hist[b], n, x[b], query_tokens=q)
+        ma, mr = assert_parity(got[b][q], ref, f"{g.name} b={b}")
+        print(f"  {g.name} b={b}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+    layer.close()
