@@ -38,24 +38,30 @@ def is_dense(g) -> bool:
     return g.d_c == 0
 
 
-def attention_flops(g, n_frames: int) -> float:
+def attention_flops(g, n_frames: int, expanded: bool = False) -> float:
     """Algorithmic FLOPs of one attention launch: per (query row, key) 2*(d_c+d_r)
-    for the score and 2*d_c for the value sum (latent), or 2*d_h + 2*d_v (dense)."""
+    for the score and 2*d_c for the value sum (latent, absorbed), or 2*d_h + 2*d_v
+    (dense, and the latent layer with its window expanded to per-head K/V)."""
     rows = g.batch * g.n_q * g.n_heads
-    per = 2.0 * g.head_dim + 2.0 * g.d_v if is_dense(g) else 2.0 * (g.d_c + g.d_rope) + 2.0 * g.d_c
+    per = 2.0 * g.head_dim + 2.0 * g.d_v if (is_dense(g) or expanded) else 2.0 * (g.d_c + g.d_rope) + 2.0 * g.d_c
     return rows * g.n_k(n_frames) * per
 
 
-def attend_call_flops(g, n_frames: int) -> float:
-    """All algorithmic FLOPs of one attend call (projections + attention)."""
+def attend_call_flops(g, n_frames: int, expanded: bool = False) -> float:
+    """All algorithmic FLOPs of one attend call (projections + attention); for the
+    expanded path the chunk's own keys/values are up-projected in the call (the
+    window's expansion, once per chunk, is not counted here)."""
     M = g.batch * g.n_q
-    d, nh = g.hidden, g.n_heads
+    d, nh, D = g.hidden, g.n_heads, g.d_c + g.d_rope
     if is_dense(g):
         gemm = 2.0 * M * d * nh * (2 * g.head_dim + g.d_v) + 2.0 * M * nh * g.d_v * d
+    elif expanded:
+        gemm = 2.0 * M * (d * D + d * g.d_q + g.d_q * nh * g.head_dim + nh * (g.head_dim * D + g.d_v * g.d_c)
+                          + nh * g.d_v * d)
     else:
-        gemm = 2.0 * M * (d * (g.d_c + g.d_rope) + d * g.d_q + g.d_q * nh * g.head_dim
+        gemm = 2.0 * M * (d * D + d * g.d_q + g.d_q * nh * g.head_dim
                           + nh * g.d_nope * g.d_c + nh * g.d_c * g.d_v + nh * g.d_v * d)
-    return gemm + attention_flops(g, n_frames)
+    return gemm + attention_flops(g, n_frames, expanded)
 
 
 class HipEvents:
@@ -128,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan1.3b-layer")
     ap.add_argument("--steps-per-chunk", type=int, default=4)
+    ap.add_argument("--path", choices=("absorbed", "expanded"), default="absorbed",
+                    help="latent layer: absorbed queries (default) or the window up-projected once per chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="query tokens the CPU oracle baseline times (0 = the whole attend call)")
@@ -160,6 +168,11 @@ def main():
         layer = vmla.LatentAttention(g, {k: torch.from_numpy(v) for k, v in w.as_dict().items()})
         attend_profiled, append = vmla.vmla_attend_profiled, vmla.vmla_compress_append
         kernel = "flash_attn_kernel (latent, absorbed)"
+        if args.path == "expanded":
+            expanded = torch.empty(vmla.vmla_expanded_bytes(layer.cfg), dtype=torch.uint8, device=dev)
+            attend_profiled = lambda ctx, x, o, a, b, st: vmla.vmla_attend_expanded_profiled(ctx, expanded, x, o, a,
+                                                                                            b, st)
+            kernel = "flash_attn_kernel (latent window expanded to per-head K/V)"
     hist = {}
     for k in range(g.prefill_chunks):
         xk = wl.hidden_states(g, chunk=k)
@@ -180,6 +193,8 @@ def main():
                for _ in range(args.warmup + args.steps)]
 
     def step(i):
+        if args.path == "expanded" and not is_dense(g):
+            vmla.vmla_expand(layer.ctx, expanded, sh)  # once per chunk: the frozen window's per-head K/V
         for s in range(args.steps_per_chunk):
             a, b = ev_pairs[i * args.steps_per_chunk + s]
             attend_profiled(layer.ctx, xs[s], out, a, b, sh)
@@ -205,12 +220,12 @@ def main():
     attn_ms = [ev.elapsed_ms(a, b) for a, b in ev_pairs[args.warmup * args.steps_per_chunk:]]
     attn_avg = float(np.mean(attn_ms))
     n_frames = min(layer.state()[0], g.window_frames)  # window full for every timed step
-    flops_attn = attention_flops(g, n_frames)
+    flops_attn = attention_flops(g, n_frames, expanded=args.path == "expanded")
     achieved = flops_attn / (attn_avg * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if g.dtype == wl.F32 else PEAK_BF16_TFLOPS
     tokens_per_step = g.batch * g.n_q * args.steps_per_chunk
     value = tokens_per_step / (ms_per_step * 1e-3)
-    call_flops = attend_call_flops(g, n_frames)
+    call_flops = attend_call_flops(g, n_frames, expanded=args.path == "expanded")
 
     if args.calibrate_copy_mb > 0:
         nbytes = args.calibrate_copy_mb << 20
@@ -233,13 +248,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if g.dtype == wl.F32 else "bf16",
         "data": "synthetic (seeded N(0,1)/sqrt(fan_in) weights and hidden states)",
-        "config": {"workload": g.name, "batch": g.batch, "query_tokens_per_call": g.n_q,
+        "config": {"workload": g.name if args.path == "absorbed" else f"{g.name}-expanded", "batch": g.batch, "query_tokens_per_call": g.n_q,
                    "keys_per_call": g.n_k(n_frames), "heads": g.n_heads, "head_dim": g.head_dim,
                    "d_c": g.d_c, "d_rope": g.d_rope,
                    "window_frames": g.window_frames, "chunk_frames": g.chunk_frames,
-                   "attends_per_step": args.steps_per_chunk, "appends_per_step": 1},
+                   "attends_per_step": args.steps_per_chunk, "appends_per_step": 1,
+                   "expands_per_step": 1 if args.path == "expanded" else 0},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_from_counters(g),
+                     "frac": achieved / peak, "traffic": traffic_from_counters(g) if args.path == "absorbed" else None,
                      "kernel": kernel,
                      "flops_per_launch": flops_attn, "avg_launch_ms": attn_avg},
         "attend_call_tflops": call_flops * args.steps_per_chunk / (ms_per_step * 1e-3) / 1e12,

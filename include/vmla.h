@@ -166,6 +166,36 @@ VMLA_API int vmla_reset(vmla_ctx* ctx);
 VMLA_API void vmla_destroy(vmla_ctx* ctx);
 
 /*
+ * Expanded (non-absorbed) latent path (paper section 3.3: the cached latents
+ * are up-projected to per-head keys and values, which are then attended like a
+ * dense layer).  Same result as vmla_attend up to rounding; for the
+ * frozen-cache denoising steps of a chunk (appendix D.5) the window is
+ * up-projected once and reused by every step.  Built for bf16 with
+ * d_nope + d_rope = d_v = 128 (else VMLA_ERR_UNSUPPORTED).
+ *
+ * vmla_expanded_bytes: size of the caller-owned `expanded` buffer (per-head
+ *   keys and values of the window in the dense cache layout, see
+ *   vmla_dense_*, plus the chunk's keys/values, queries, outputs and partial
+ *   states: ~260 MB at the Wan-1.3B layer).  0 if unsupported or invalid.
+ * vmla_expand: per stream, head h and valid ring key j,
+ *   K_h[j] = [W_UK^h c_j ; k_r_j] and V_h[j] = W_UV^h c_j into `expanded`,
+ *   from the ring as it stands (n frames).  Leaves the cache and n unchanged.
+ * vmla_attend_expanded: attend one chunk (x, out as vmla_attend) with per-head
+ *   queries [q_nope ; RoPE(q_rope)] against the expanded window and the
+ *   chunk's own up-projected keys/values, then W_O.  `expanded` must be the
+ *   buffer of the last vmla_expand, made after the last append (else
+ *   VMLA_ERR_STATE; vmla_reset forgets it).
+ * vmla_attend_expanded_profiled: same, recording caller-made events around the
+ *   attention kernel (NULL -> VMLA_ERR_NULL).
+ */
+VMLA_API size_t vmla_expanded_bytes(const vmla_config* cfg);
+VMLA_API int vmla_expand(vmla_ctx* ctx, void* expanded, hipStream_t stream);
+VMLA_API int vmla_attend_expanded(vmla_ctx* ctx, const void* expanded, const void* x, void* out,
+                                  hipStream_t stream);
+VMLA_API int vmla_attend_expanded_profiled(vmla_ctx* ctx, const void* expanded, const void* x, void* out,
+                                           hipEvent_t attn_start, hipEvent_t attn_stop, hipStream_t stream);
+
+/*
  * Dense per-head baseline (paper section 1 and appendix C.1: the layer VideoMLA
  * replaces, whose cache holds every head's key and value, n_heads*2*d_h scalars
  * per token).  Same chunk-causal window, ring eviction and 3D-RoPE as the
@@ -183,12 +213,12 @@ VMLA_API void vmla_destroy(vmla_ctx* ctx);
  *   w_o [hidden, n_heads*d_v].
  *
  * Cache layout (vmla_dense_cache_bytes), P = window_frames*T rounded up to a
- * multiple of 64:
+ * multiple of 128:
  *   keys   [batch][n_heads][P][d_rope] bf16, rotated with the absolute frame index;
  *   values [batch][n_heads][d_v][P] fp16, transposed: the value of ring key j
  *          (frame f in slot f % window_frames, key j = slot*T + s) sits in
  *          column j with bits 2 and 3 of j swapped; columns past the valid
- *          keys (up to the next multiple of 64) are kept at zero by the library.
+ *          keys (up to the next multiple of 128) are kept at zero by the library.
  * The values are stored as fp16 so the value product runs on fp16 operands
  * (the bf16 rounding of probabilities near 1 is too coarse, see the latent
  * path); the cache size equals the bf16 one.

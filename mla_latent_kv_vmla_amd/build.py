@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
           "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["vmla_host.cpp", "pipeline.hip", "dense.hip", "attention.hip"]
+SOURCES = ["vmla_host.cpp", "pipeline.hip", "dense.hip", "expanded.hip", "attention.hip"]
 
 # Per-source code generation options.  The attention kernels hold a 32*NB x DC
 # fp32 accumulator plus the absorbed query per wave; with MFMA results in the

@@ -15,10 +15,6 @@
 
 namespace vmla {
 
-// Column of key j in a transposed value row: bits 2 and 3 of j swapped, so the
-// 8 keys one lane feeds to a value MFMA are contiguous.
-__device__ inline int perm16(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
-
 static Rope dense_rope(const DensePlan& p) {
   Rope r;
   r.pairs_t = p.pairs_t;
@@ -88,7 +84,7 @@ __global__ __launch_bounds__(256) void zero_value_columns(f16* v, long rows, lon
   }
 }
 
-static void zero_columns(void* v, long rows, long P, int c0, int c1, hipStream_t s) {
+void zero_value_columns_async(void* v, long rows, long P, int c0, int c1, hipStream_t s) {
   if (c1 <= c0) return;
   const long work = rows * (c1 - c0);
   const int grid = (int)((work + 255) / 256 < 1024 ? (work + 255) / 256 : 1024);
@@ -138,7 +134,7 @@ hipError_t run_dense_append(const DensePlan& p, int64_t n, const void* x, hipStr
   // valid ring keys after this append: min(n + C, W) frames
   const int64_t frames = n + p.C < p.W ? n + p.C : p.W;
   const long valid = (long)frames * p.Tpf;
-  zero_columns(p.vring, (long)p.B * p.nh * p.dv, p.ring_stride, (int)valid, round_tile(valid), s);
+  zero_value_columns_async(p.vring, (long)p.B * p.nh * p.dv, p.ring_stride, (int)valid, round_tile(valid), s);
   return hipGetLastError();
 }
 
@@ -157,7 +153,7 @@ hipError_t run_dense_attend(const DensePlan& p, int64_t n, const void* x, void* 
     gemm<bf16, false>(dense_ops(p.w_q, p.w_q, p.nh * p.dh, x, p.d, p.nh * p.dh, M, p.d), 1, e, s);
   }
   dense_kv(p, x, n, false, s);
-  zero_columns(p.vstage, (long)p.B * p.nh * p.dv, p.stage_stride, p.Nq, p.stage_stride, s);
+  zero_value_columns_async(p.vstage, (long)p.B * p.nh * p.dv, p.stage_stride, p.Nq, p.stage_stride, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   {

@@ -73,6 +73,11 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* 
                                            0, 0);
 }
 
+// Column of key j in a transposed value row: bits 2 and 3 of j swapped, so the
+// 8 keys one lane feeds to a value MFMA are contiguous (and every aligned group
+// of 4 keys stays contiguous).
+__device__ inline int perm16(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
 // 3D-RoPE description: per complex pair p its axis (t, h, w by index ranges)
 // and angular frequency.  Token (frame f, position s in the frame) has
 // coordinates (f, s / grid_w, s % grid_w).

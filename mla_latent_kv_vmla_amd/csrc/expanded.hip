@@ -1,0 +1,197 @@
+// The latent layer computed without absorption (VideoMLA paper, section 3.3:
+// the cached latents are up-projected to per-head keys and values, which are
+// then attended like a dense layer).  For the frozen-cache steps of a rollout
+// (appendix D.5) the window is up-projected once per chunk and reused by every
+// step:
+//
+//   expand: per stream and head, keys [W_UK^h c | k_r] of the valid ring rows
+//     (one GEMM with the per-head lift [W_UK^h 0 ; 0 I], so the rotated k_r is
+//     copied exactly) and values W_UV^h c, transposed (a GEMM with the operand
+//     roles swapped, so each lane holds 4 consecutive keys of one value channel
+//     and stores them together), then the value columns past the valid keys are
+//     zeroed up to the key-tile boundary.
+//   attend: compress the chunk into staging (latent path), c^Q = W_DQ x, the
+//     per-head queries [q_nope | RoPE(q_rope)] (not absorbed), the chunk's own
+//     keys and values by the same up-projection, dense flash attention over the
+//     expanded window + chunk (attention.hip), out = W_O o.
+#include "gemm.h"
+#include "plan.h"
+
+namespace vmla {
+
+static Rope latent_rope(const Plan& p) {
+  Rope r;
+  r.pairs_t = p.pairs_t;
+  r.pairs_h = p.pairs_h;
+  r.grid_w = p.grid_w;
+  r.tokens_per_frame = p.Tpf;
+  for (int i = 0; i < kMaxRopePairs; ++i) r.freq[i] = p.freq[i];
+  return r;
+}
+
+// wext[h][r][c] (r < d_nope + d_r, c < d_c + d_r): W_UK^h[r][c] for r < d_nope and
+// c < d_c; 1 where r - d_nope == c - d_c (copies k_r); 0 elsewhere.
+__global__ __launch_bounds__(256) void build_key_lift(bf16* wext, const bf16* w_uk, int nh, int d_nope, int dc,
+                                                      int dr) {
+  const int D = dc + dr, dh = d_nope + dr;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < (long)nh * dh * D; i += (long)gridDim.x * 256) {
+    const int c = (int)(i % D);
+    const long hr = i / D;
+    const int r = (int)(hr % dh), h = (int)(hr / dh);
+    float v;
+    if (r < d_nope) v = c < dc ? (float)w_uk[((long)h * d_nope + r) * dc + c] : 0.f;
+    else v = c == dc + (r - d_nope) ? 1.f : 0.f;
+    wext[i] = (bf16)v;
+  }
+}
+
+// Key rows: K[b][h][row m][n] (z = head).
+struct EpiExpandKey {
+  bf16* k;
+  long P;
+  int nh, dh, b;
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    store4(k + (((long)b * nh + z) * P + m) * dh + n, v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Transposed values from the swapped GEMM: "tokens" m are value channels,
+// "features" n are key rows, so v holds keys n..n+3 of channel m.
+struct EpiExpandValueT {
+  f16* vt;
+  long P;
+  int nh, dv, b;
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    f16* dst = vt + (((long)b * nh + z) * dv + m) * P + (n & ~15) + perm16(n & 15);
+    f16x4 h4;
+    h4[0] = (f16)v[0];
+    h4[1] = (f16)v[1];
+    h4[2] = (f16)v[2];
+    h4[3] = (f16)v[3];
+    *reinterpret_cast<f16x4*>(dst) = h4;
+  }
+};
+
+// Per-head queries [q_nope | RoPE(q_rope)] * qscale into Q[b][h][t][dh].
+struct EpiQueryHead {
+  bf16* q;
+  int Nq, nh, dh, d_nope;
+  float qscale;
+  int64_t frame0;
+  Rope rope;
+  __device__ void operator()(int, int m, int n, const float* v) const {
+    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    if (j >= d_nope) {
+      const int64_t frame = frame0 + t / rope.tokens_per_frame;
+      const int s = t % rope.tokens_per_frame;
+      const int pair = (j - d_nope) >> 1;
+      rope.rotate2(pair, frame, s, a0, a1);
+      rope.rotate2(pair + 1, frame, s, a2, a3);
+    }
+    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0 * qscale, a1 * qscale, a2 * qscale, a3 * qscale);
+  }
+};
+
+static GemmOps<bf16> gops(const void* w, long ldw, long wz, const void* x, long ldx, long xz, int N, int M, int K) {
+  GemmOps<bf16> o;
+  o.w = o.w2 = static_cast<const bf16*>(w);
+  o.ldw = ldw;
+  o.wz = wz;
+  o.x = static_cast<const bf16*>(x);
+  o.ldx = ldx;
+  o.xz = xz;
+  o.N = N;
+  o.M = M;
+  o.K = K;
+  o.n_split = N;
+  return o;
+}
+
+static long round_up(long v, long m) { return (v + m - 1) / m * m; }
+
+bool expanded_supported(const Plan& p) {
+  return p.dtype == DType::BF16 && dense_attention_supported(DType::BF16, p.dh, p.dv);
+}
+
+// Up-project `rows` latent rows of every stream (row stride D, stream stride
+// lat_bstride) into key rows / transposed value columns [0, rows) of stride P.
+static void up_project(const Plan& p, const DensePlan&, const bf16* wext, const void* lat, long lat_bstride,
+                       int rows, bf16* kdst, f16* vdst, long P, hipStream_t s) {
+  if (rows <= 0) return;
+  for (int b = 0; b < p.B; ++b) {
+    const bf16* lb = static_cast<const bf16*>(lat) + (long)b * lat_bstride;
+    EpiExpandKey ek{kdst, P, p.nh, p.dh, b};
+    gemm<bf16, false>(gops(wext, p.D, (long)p.dh * p.D, lb, p.D, 0, p.dh, rows, p.D), p.nh, ek, s);
+    EpiExpandValueT ev{vdst, P, p.nh, p.dv, b};
+    gemm<bf16, false>(gops(lb, p.D, 0, p.w_uv, p.dc, (long)p.dv * p.dc, rows, p.dv, p.dc), p.nh, ev, s);
+  }
+  zero_value_columns_async(vdst, (long)p.B * p.nh * p.dv, P, rows, (int)round_up(rows, kDenseKeyTile), s);
+}
+
+hipError_t run_expand(const Plan& p, const DensePlan& ex, void* wext_buf, int64_t n, hipStream_t s) {
+  bf16* wext = static_cast<bf16*>(wext_buf);
+  const long total = (long)p.nh * p.dh * p.D;
+  build_key_lift<<<(int)((total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024), 256, 0, s>>>(
+      wext, static_cast<const bf16*>(p.w_uk), p.nh, p.d_nope, p.dc, p.dr);
+  const int n_ring = (int)((n < p.W ? n : p.W) * p.Tpf);
+  up_project(p, ex, wext, p.cache, (long)p.W * p.Tpf * p.D, n_ring, static_cast<bf16*>(ex.kring),
+             static_cast<f16*>(ex.vring), ex.ring_stride, s);
+  return hipGetLastError();
+}
+
+hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* wext, int64_t n, const void* x,
+                               void* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const int M = p.B * p.Nq;
+  hipError_t err = run_compress(p, x, n, p.stage, false, s);
+  if (err != hipSuccess) return err;
+  {  // c^Q = W_DQ x
+    EpiStore<bf16> e{static_cast<bf16*>(p.cq), p.dq, 0};
+    gemm<bf16, false>(gops(p.w_dq, p.d, 0, x, p.d, 0, p.dq, M, p.d), 1, e, s);
+  }
+  {  // per-head queries, not absorbed
+    EpiQueryHead e;
+    e.q = static_cast<bf16*>(ex.q);
+    e.Nq = p.Nq;
+    e.nh = p.nh;
+    e.dh = p.dh;
+    e.d_nope = p.d_nope;
+    e.qscale = p.qscale;
+    e.frame0 = n;
+    e.rope = latent_rope(p);
+    gemm<bf16, false>(gops(p.w_uq, p.dq, 0, p.cq, p.dq, 0, p.nh * p.dh, M, p.dq), 1, e, s);
+  }
+  up_project(p, ex, static_cast<const bf16*>(wext), p.stage, (long)p.Nq * p.D, p.Nq, static_cast<bf16*>(ex.kstage),
+             static_cast<f16*>(ex.vstage), ex.stage_stride, s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  {
+    DenseAttnCall a;
+    a.dh = p.dh;
+    a.dv = p.dv;
+    a.q = ex.q;
+    a.kring = ex.kring;
+    a.vring = ex.vring;
+    a.kstage = ex.kstage;
+    a.vstage = ex.vstage;
+    a.out = ex.o;
+    a.part_o = ex.part_o;
+    a.part_ml = ex.part_ml;
+    a.ev_start = ev0;
+    a.ev_stop = ev1;
+    a.B = p.B;
+    a.H = p.nh;
+    a.Nq = p.Nq;
+    a.n_ring = (int)((n < p.W ? n : p.W) * p.Tpf);
+    a.ring_stride = ex.ring_stride;
+    a.stage_stride = ex.stage_stride;
+    a.G = ex.G;
+    if ((err = run_dense_attention(a, s)) != hipSuccess) return err;
+  }
+  {  // out = W_O o
+    EpiStore<bf16> e{static_cast<bf16*>(out), p.d, 0};
+    gemm<bf16, false>(gops(p.w_o, (long)p.nh * p.dv, 0, ex.o, (long)p.nh * p.dv, 0, p.d, M, p.nh * p.dv), 1, e, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vmla

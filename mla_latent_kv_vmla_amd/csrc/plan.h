@@ -1,5 +1,5 @@
 // Internal interface between the host runtime (vmla_host.cpp) and the kernel
-// pipelines (pipeline.hip, dense.hip, attention.hip).  Host-only types; no HIP
+// pipelines (pipeline.hip, dense.hip, expanded.hip, attention.hip).  Host-only types; no HIP
 // kernels.
 #pragma once
 #include <hip/hip_runtime_api.h>
@@ -16,7 +16,7 @@ constexpr int kAttnMaxRows = 256;
 constexpr int kMaxRopePairs = 64;
 // Key-tile size of the dense attention kernel; the dense ring and the chunk's
 // staged keys are padded to a multiple of it.
-constexpr int kDenseKeyTile = 64;
+constexpr int kDenseKeyTile = 128;
 
 // Everything one layer call needs: geometry, borrowed device pointers and the
 // workspace carve-up.  Filled by the host runtime; read by the pipelines.
@@ -131,5 +131,26 @@ struct DenseAttnCall {
 };
 hipError_t run_dense_attention(const DenseAttnCall& a, hipStream_t s);
 bool dense_attention_supported(DType dt, int dh, int dv);
+// Zero the value columns of keys [c0, c1) (key order as stored: bits 2 and 3
+// swapped) in `rows` transposed value rows of stride P (dense.hip).
+void zero_value_columns_async(void* v, long rows, long P, int c0, int c1, hipStream_t s);
+
+// ---------------------------------------------------------------- expanded latent path
+// The latent layer computed without absorption: the window's latent rows are
+// up-projected once to per-head keys [W_UK^h c | k_r] and values W_UV^h c in the
+// dense layout (DensePlan regions of an "expanded" buffer), then attended with
+// the dense kernel.  ex.* regions live in the expanded buffer; p supplies the
+// latent geometry, weights, ring cache and the latent workspace (stage, c^Q).
+struct ExpandedLayout {
+  DenseLayout dense;  // kring/vring then q/kstage/vstage/o/part_o/part_ml
+  size_t wext;        // [nh][dh][d_c + d_r] bf16: per head [W_UK^h | 0 ; 0 | I]
+  size_t total;
+};
+ExpandedLayout expanded_layout(const Plan& p, DensePlan& ex);
+hipError_t run_expand(const Plan& p, const DensePlan& ex, void* wext, int64_t n, hipStream_t s);
+hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* wext, int64_t n, const void* x,
+                               void* out, hipStream_t s, hipEvent_t attn_start = nullptr,
+                               hipEvent_t attn_stop = nullptr);
+bool expanded_supported(const Plan& p);
 
 }  // namespace vmla

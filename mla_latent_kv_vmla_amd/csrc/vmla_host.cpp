@@ -12,6 +12,7 @@
 
 using vmla::DType;
 using vmla::DensePlan;
+using vmla::ExpandedLayout;
 using vmla::Plan;
 
 struct vmla_ctx {
@@ -21,6 +22,9 @@ struct vmla_ctx {
   void* workspace;
   float freq[vmla::kMaxRopePairs];
   int64_t n;  // frames appended (lockstep over the batch)
+  // expanded latent path: buffer and frame count of the last vmla_expand
+  const void* expanded;
+  int64_t expanded_n;
 };
 
 struct vmla_dense_ctx {
@@ -185,6 +189,33 @@ DenseLayout dense_layout(const DensePlan& p) {
   L.ws_total = off;
   return L;
 }
+
+ExpandedLayout expanded_layout(const Plan& p, DensePlan& ex) {
+  memset(&ex, 0, sizeof(ex));
+  ex.B = p.B;
+  ex.d = p.d;
+  ex.nh = p.nh;
+  ex.dh = p.dh;
+  ex.dv = p.dv;
+  ex.Tpf = p.Tpf;
+  ex.grid_w = p.grid_w;
+  ex.W = p.W;
+  ex.C = p.C;
+  ex.Nq = p.Nq;
+  ex.pairs_t = p.pairs_t;
+  ex.pairs_h = p.pairs_h;
+  ex.pairs_w = p.pairs_w;
+  for (int i = 0; i < kMaxRopePairs; ++i) ex.freq[i] = p.freq[i];
+  ex.qscale = p.qscale;
+  ex.G = p.G;
+  ex.ring_stride = (int)(((long)p.W * p.Tpf + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile);
+  ex.stage_stride = (p.Nq + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile;
+  ExpandedLayout L;
+  L.dense = dense_layout(ex);
+  L.wext = L.dense.cache_total + L.dense.ws_total;
+  L.total = L.wext + align256((size_t)p.nh * p.dh * p.D * 2);
+  return L;
+}
 }  // namespace vmla
 
 namespace {
@@ -251,6 +282,8 @@ VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* ca
   c->cache = cache;
   c->workspace = workspace;
   c->n = 0;
+  c->expanded = nullptr;
+  c->expanded_n = -1;
   if (rope_freqs) {
     for (int i = 0; i < npairs; ++i) c->freq[i] = rope_freqs[i];
   } else {
@@ -335,7 +368,76 @@ VMLA_API int vmla_cache_state(const vmla_ctx* ctx, int64_t* frames_appended, int
 VMLA_API int vmla_reset(vmla_ctx* ctx) {
   if (!ctx) return VMLA_ERR_NULL;
   ctx->n = 0;
+  ctx->expanded = nullptr;
+  ctx->expanded_n = -1;
   return VMLA_OK;
+}
+
+/* ------------------------------------------------------- expanded latent path */
+
+static bool expanded_ok(const vmla_config* cfg) {
+  return check_config(cfg) == VMLA_OK && vmla::expanded_supported(geometry(cfg));
+}
+
+VMLA_API size_t vmla_expanded_bytes(const vmla_config* cfg) {
+  if (!expanded_ok(cfg)) return 0;
+  DensePlan ex;
+  return vmla::expanded_layout(geometry(cfg), ex).total;
+}
+
+// Expanded-buffer view of a ctx: dense regions and the key lift.
+static DensePlan make_expanded_plan(const Plan& p, void* buf, void** wext) {
+  DensePlan ex;
+  const vmla::ExpandedLayout L = vmla::expanded_layout(p, ex);
+  char* b = static_cast<char*>(buf);
+  char* ws = b + L.dense.cache_total;
+  ex.kring = b + L.dense.kring;
+  ex.vring = b + L.dense.vring;
+  ex.q = ws + L.dense.q;
+  ex.kstage = ws + L.dense.kstage;
+  ex.vstage = ws + L.dense.vstage;
+  ex.o = ws + L.dense.o;
+  ex.part_o = reinterpret_cast<float*>(ws + L.dense.part_o);
+  ex.part_ml = reinterpret_cast<float*>(ws + L.dense.part_ml);
+  *wext = b + L.wext;
+  return ex;
+}
+
+VMLA_API int vmla_expand(vmla_ctx* ctx, void* expanded, hipStream_t stream) {
+  if (!ctx || !expanded) return VMLA_ERR_NULL;
+  if (!aligned16(expanded)) return VMLA_ERR_ALIGN;
+  if (!expanded_ok(&ctx->cfg)) return VMLA_ERR_UNSUPPORTED;
+  Plan p = make_plan(ctx);
+  void* wext;
+  DensePlan ex = make_expanded_plan(p, expanded, &wext);
+  if (vmla::run_expand(p, ex, wext, ctx->n, stream) != hipSuccess) return VMLA_ERR_HIP;
+  ctx->expanded = expanded;
+  ctx->expanded_n = ctx->n;
+  return VMLA_OK;
+}
+
+static int attend_expanded(vmla_ctx* ctx, const void* expanded, const void* x, void* out, hipEvent_t e0,
+                           hipEvent_t e1, hipStream_t stream) {
+  if (!aligned16(expanded) || !aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (!expanded_ok(&ctx->cfg)) return VMLA_ERR_UNSUPPORTED;
+  if (ctx->expanded != expanded || ctx->expanded_n != ctx->n) return VMLA_ERR_STATE;
+  Plan p = make_plan(ctx);
+  void* wext;
+  DensePlan ex = make_expanded_plan(p, const_cast<void*>(expanded), &wext);
+  if (vmla::run_attend_expanded(p, ex, wext, ctx->n, x, out, stream, e0, e1) != hipSuccess) return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_attend_expanded(vmla_ctx* ctx, const void* expanded, const void* x, void* out,
+                                  hipStream_t stream) {
+  if (!ctx || !expanded || !x || !out) return VMLA_ERR_NULL;
+  return attend_expanded(ctx, expanded, x, out, nullptr, nullptr, stream);
+}
+
+VMLA_API int vmla_attend_expanded_profiled(vmla_ctx* ctx, const void* expanded, const void* x, void* out,
+                                           hipEvent_t attn_start, hipEvent_t attn_stop, hipStream_t stream) {
+  if (!ctx || !expanded || !x || !out || !attn_start || !attn_stop) return VMLA_ERR_NULL;
+  return attend_expanded(ctx, expanded, x, out, attn_start, attn_stop, stream);
 }
 
 VMLA_API void vmla_destroy(vmla_ctx* ctx) { delete ctx; }

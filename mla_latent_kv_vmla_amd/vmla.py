@@ -89,6 +89,15 @@ def lib():
         L.vmla_reset.restype = c_int
         L.vmla_destroy.argtypes = [c_void_p]
         L.vmla_destroy.restype = None
+        L.vmla_expanded_bytes.argtypes = [POINTER(vmla_config)]
+        L.vmla_expanded_bytes.restype = c_size_t
+        L.vmla_expand.argtypes = [c_void_p, c_void_p, c_void_p]
+        L.vmla_expand.restype = c_int
+        L.vmla_attend_expanded.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.vmla_attend_expanded.restype = c_int
+        L.vmla_attend_expanded_profiled.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_void_p]
+        L.vmla_attend_expanded_profiled.restype = c_int
         L.vmla_dense_cache_bytes.argtypes = [POINTER(vmla_config)]
         L.vmla_dense_cache_bytes.restype = c_size_t
         L.vmla_dense_workspace_bytes.argtypes = [POINTER(vmla_config)]
@@ -182,6 +191,24 @@ def vmla_reset(ctx) -> None:
 
 def vmla_destroy(ctx) -> None:
     lib().vmla_destroy(ctx)
+
+
+def vmla_expanded_bytes(cfg: vmla_config) -> int:
+    return lib().vmla_expanded_bytes(byref(cfg))
+
+
+def vmla_expand(ctx, expanded, stream=None) -> None:
+    _check(lib().vmla_expand(ctx, _ptr(expanded), _stream(stream)), "vmla_expand")
+
+
+def vmla_attend_expanded(ctx, expanded, x, out, stream=None) -> None:
+    _check(lib().vmla_attend_expanded(ctx, _ptr(expanded), _ptr(x), _ptr(out), _stream(stream)),
+           "vmla_attend_expanded")
+
+
+def vmla_attend_expanded_profiled(ctx, expanded, x, out, attn_start: int, attn_stop: int, stream=None) -> None:
+    _check(lib().vmla_attend_expanded_profiled(ctx, _ptr(expanded), _ptr(x), _ptr(out), attn_start, attn_stop,
+                                               _stream(stream)), "vmla_attend_expanded_profiled")
 
 
 def _freq_array(rope_freqs):
@@ -313,6 +340,25 @@ class LatentAttention:
 
     def reset(self):
         vmla_reset(self.ctx)
+
+    def expand(self, stream=None):
+        """Up-project the window to per-head keys/values (expanded path) into an
+        owned buffer, allocated on first use."""
+        import torch
+        if getattr(self, "expanded", None) is None:
+            nbytes = vmla_expanded_bytes(self.cfg)
+            if nbytes == 0:
+                raise ValueError(f"geometry {self.g.name} has no expanded path")
+            self.expanded = torch.empty(nbytes, dtype=torch.uint8, device=self.cache.device)
+        vmla_expand(self.ctx, self.expanded, stream)
+
+    def attend_expanded(self, x, out=None, stream=None):
+        import torch
+        self._check_x(x)
+        if out is None:
+            out = torch.empty_like(x)
+        vmla_attend_expanded(self.ctx, getattr(self, "expanded", None), x, out, stream)
+        return out
 
     def close(self):
         if self.ctx:

@@ -145,11 +145,11 @@ def test_null_ctx_rejected():
 # ----------------------------------------------------------------------------- dense baseline
 def test_dense_cache_and_workspace_bytes():
     g = wl.WAN_DENSE
-    P = (21 * 1560 + 63) // 64 * 64  # ring keys per (stream, head), padded to the 64-key tile
+    P = (21 * 1560 + 127) // 128 * 128  # ring keys per (stream, head), padded to the 128-key tile
     assert P == 32768
     assert vmla.vmla_dense_cache_bytes(_cfg(g)) == 12 * P * (128 + 128) * 2  # 201.3 MB: keys + values, 16-bit
     ws = vmla.vmla_dense_workspace_bytes(_cfg(g))
-    S = (4680 + 63) // 64 * 64
+    S = (4680 + 127) // 128 * 128
     assert ws >= 12 * (4680 * 128 + 2 * S * 128) * 2 + 4680 * 1536 * 2
     # the latent entry points refuse the dense geometry and vice versa
     assert vmla.vmla_cache_bytes(_cfg(g)) == 0
@@ -191,3 +191,35 @@ def test_dense_create_and_argument_checks():
         assert vmla.vmla_dense_cache_state(ctx) == (0, 0, 0)
     finally:
         vmla.vmla_dense_destroy(ctx)
+
+
+# ----------------------------------------------------------------------------- expanded latent path
+def test_expanded_bytes_and_state_checks():
+    g = wl.WAN_LAYER
+    nb = vmla.vmla_expanded_bytes(_cfg(g))
+    P = (21 * 1560 + 127) // 128 * 128
+    assert nb >= 12 * P * 256 * 2  # per-head keys and values of the window
+    assert vmla.vmla_expanded_bytes(_cfg(wl.TINY)) == 0          # fp32 / 16-wide heads: no expanded kernel
+    assert vmla.vmla_expanded_bytes(_cfg(g, d_v=64)) == 0        # value width != 128
+    ctx = vmla.vmla_create(_cfg(g), _fake_weights(), FAKE, FAKE)
+    try:
+        # attend before any expand, or with another buffer: rejected before launch
+        for f, code in [(lambda: vmla.vmla_attend_expanded(ctx, FAKE, FAKE, FAKE, 0), "VMLA_ERR_STATE"),
+                        (lambda: vmla.vmla_attend_expanded(ctx, 0, FAKE, FAKE, 0), "VMLA_ERR_NULL"),
+                        (lambda: vmla.vmla_attend_expanded(ctx, FAKE + 4, FAKE, FAKE, 0), "VMLA_ERR_ALIGN"),
+                        (lambda: vmla.vmla_expand(ctx, 0, 0), "VMLA_ERR_NULL"),
+                        (lambda: vmla.vmla_expand(ctx, FAKE + 2, 0), "VMLA_ERR_ALIGN"),
+                        (lambda: vmla.vmla_attend_expanded_profiled(ctx, FAKE, FAKE, FAKE, 0, 0, 0),
+                         "VMLA_ERR_NULL")]:
+            with pytest.raises(vmla.VmlaError) as e:
+                f()
+            assert e.value.code == vmla.STATUS[code]
+    finally:
+        vmla.vmla_destroy(ctx)
+    tiny = vmla.vmla_create(_cfg(wl.TINY), _fake_weights(), FAKE, FAKE)
+    try:
+        with pytest.raises(vmla.VmlaError) as e:
+            vmla.vmla_expand(tiny, FAKE, 0)
+        assert e.value.code == vmla.STATUS["VMLA_ERR_UNSUPPORTED"]
+    finally:
+        vmla.vmla_destroy(tiny)
