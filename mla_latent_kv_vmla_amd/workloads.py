@@ -54,6 +54,7 @@ class LayerGeometry:
     chunks: int = 1
     steps: int = 1
     prefill_chunks: int = 0  # seeded appends before the measured attend
+    sink_frames: int = 0     # pinned sink frames ahead of the window (long-horizon cache)
 
     @property
     def head_dim(self) -> int:
@@ -71,8 +72,12 @@ class LayerGeometry:
     def latent_width(self) -> int:
         return self.d_c + self.d_rope
 
+    def cached_frames(self, frames_appended: int) -> int:
+        n, S = frames_appended, self.sink_frames
+        return min(n, S) + max(0, min(n - S, self.window_frames))
+
     def n_k(self, frames_appended: int) -> int:
-        return min(frames_appended, self.window_frames) * self.tokens_per_frame + self.n_q
+        return self.cached_frames(frames_appended) * self.tokens_per_frame + self.n_q
 
     def replace(self, **kw) -> "LayerGeometry":
         return dataclasses.replace(self, **kw)

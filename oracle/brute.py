@@ -41,14 +41,17 @@ def attend(g, wts, history, n, chunk_x):
     T = g.grid_h * g.grid_w
     W, C = g.window_frames, g.chunk_frames
     tolist = lambda a: [[float(v) for v in row] for row in a]
-    first = n - W if n > W else 0
-    # visible tokens with window-local (t, h, w)
+    # visible frames in context order: pinned sink frames, the recent window, the
+    # chunk; a frame's local temporal coordinate is its index in that list
+    S = getattr(g, "sink_frames", 0)
+    frames = [f for f in range(n) if f < S or f >= max(S, n - W)] + list(range(n, n + C))
     keys_x, keys_pos = [], []
-    for fr in list(range(first, n)) + list(range(n, n + C)):
+    for tau, fr in enumerate(frames):
         rows = tolist(history[fr]) if fr < n else tolist(chunk_x)[(fr - n) * T:(fr - n + 1) * T]
         for s in range(T):
             keys_x.append(rows[s])
-            keys_pos.append((fr - first, s // g.grid_w, s % g.grid_w))
+            keys_pos.append((tau, s // g.grid_w, s % g.grid_w))
+    n_cached = len(frames) - C
     w_dkv, w_kr, w_dq, w_uq, w_o = (tolist(getattr(wts, k)) for k in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_o"))
     w_uk = [tolist(m) for m in wts.w_uk]
     w_uv = [tolist(m) for m in wts.w_uv]
@@ -65,7 +68,7 @@ def attend(g, wts, history, n, chunk_x):
     out = []
     chunk_rows = tolist(chunk_x)
     for i, xi in enumerate(chunk_rows):
-        pos = (n + i // T - first, (i % T) // g.grid_w, (i % T) % g.grid_w)
+        pos = (n_cached + i // T, (i % T) // g.grid_w, (i % T) % g.grid_w)
         cq = _mat_vec(w_dq, xi)
         qall = _mat_vec(w_uq, cq)
         o = []
@@ -87,13 +90,17 @@ def attend_dense(g, wts, history, n, chunk_x):
     T = g.grid_h * g.grid_w
     W, C = g.window_frames, g.chunk_frames
     tolist = lambda a: [[float(v) for v in row] for row in a]
-    first = n - W if n > W else 0
+    # visible frames in context order: pinned sink frames, the recent window, the
+    # chunk; a frame's local temporal coordinate is its index in that list
+    S = getattr(g, "sink_frames", 0)
+    frames = [f for f in range(n) if f < S or f >= max(S, n - W)] + list(range(n, n + C))
     keys_x, keys_pos = [], []
-    for fr in list(range(first, n)) + list(range(n, n + C)):
+    for tau, fr in enumerate(frames):
         rows = tolist(history[fr]) if fr < n else tolist(chunk_x)[(fr - n) * T:(fr - n + 1) * T]
         for s in range(T):
             keys_x.append(rows[s])
-            keys_pos.append((fr - first, s // g.grid_w, s % g.grid_w))
+            keys_pos.append((tau, s // g.grid_w, s % g.grid_w))
+    n_cached = len(frames) - C
     w_q, w_k, w_v, w_o = (tolist(getattr(wts, k)) for k in ("w_q", "w_k", "w_v", "w_o"))
     dh = g.d_nope + g.d_rope
     K, V = [], []
@@ -103,7 +110,7 @@ def attend_dense(g, wts, history, n, chunk_x):
         V.append([vall[h * g.d_v:(h + 1) * g.d_v] for h in range(g.n_heads)])
     out = []
     for i, xi in enumerate(tolist(chunk_x)):
-        pos = (n + i // T - first, (i % T) // g.grid_w, (i % T) % g.grid_w)
+        pos = (n_cached + i // T, (i % T) // g.grid_w, (i % T) % g.grid_w)
         qall = _mat_vec(w_q, xi)
         o = []
         for h in range(g.n_heads):

@@ -11,11 +11,14 @@ sections 3, 3.1-3.3, appendices C.1, D.1, D.4, D.5):
     latent c_j = W_DKV x_j (d_c) and the decoupled positional key
     k^_j = W_KR x_j (d_r), kept before rotation (section 3.3 and D.5 store the
     positional key un-rotated and rotate it when the window is assembled).
- 2. Visible keys (D.4, chunk-causal): the cached frames [max(0, n-W), n) plus
-    the chunk's own frames [n, n+C); every query of the chunk sees all of them.
+ 2. Visible keys (D.4, chunk-causal): the cached frames -- the S pinned sink
+    frames [0, min(n, S)) (S = 0 unless a geometry sets sink_frames) and the
+    recent window [max(S, n-W), n) -- plus the chunk's own frames [n, n+C);
+    every query of the chunk sees all of them.
  3. Positions (C.1, D.5): token s of a frame sits at row s // grid_w, column
-    s % grid_w; the temporal coordinate is window-local, tau = f - first
-    visible frame, for keys and queries alike.
+    s % grid_w; the temporal coordinate is local: a frame's index in the
+    visible context [sink frames, window frames, chunk frames], for keys and
+    queries alike (D.5 re-indexing; without a sink this is f - first frame).
  4. 3D-RoPE (section 3.2, 4.1, C.1): the d_r channels are complex pairs
     (2p, 2p+1); the first p_t pairs turn with tau, the next p_h with the row,
     the last p_w with the column; pair p turns by angle pos * omega_p.
@@ -101,10 +104,13 @@ def query_heads(x: np.ndarray, w_dq: np.ndarray, w_uq: np.ndarray, n_heads: int,
 
 
 # ----------------------------------------------------------------------------- window
-def visible_frames(n: int, window_frames: int, chunk_frames: int):
-    """(first, cached frames, chunk frames): cached [max(0, n-W), n), chunk [n, n+C)."""
-    first = max(0, n - window_frames)
-    return first, list(range(first, n)), list(range(n, n + chunk_frames))
+def visible_frames(n: int, window_frames: int, chunk_frames: int, sink_frames: int = 0):
+    """(cached frames, chunk frames) in context order: sink frames [0, min(n, S)),
+    then the window [max(S, n-W), n); chunk [n, n+C).  A frame's local temporal
+    coordinate is its index in cached + chunk (appendix D.4, D.5)."""
+    sink = list(range(min(n, sink_frames)))
+    window = list(range(max(sink_frames, n - window_frames), n))
+    return sink + window, list(range(n, n + chunk_frames))
 
 
 class _Assembled:
@@ -115,21 +121,22 @@ def _assemble(g, wts, history, n, chunk_x, query_tokens, dtype):
     """Everything attention needs, for one stream: rotated keys/queries, latents."""
     f = lambda a: np.asarray(a, dtype=dtype)
     T = g.grid_h * g.grid_w
-    first, cached, chunk = visible_frames(n, g.window_frames, g.chunk_frames)
+    cached, chunk = visible_frames(n, g.window_frames, g.chunk_frames, getattr(g, "sink_frames", 0))
     xk = [f(history[fr]).reshape(T, g.hidden) for fr in cached]
     xk.append(f(chunk_x).reshape(g.chunk_frames * T, g.hidden))
     xk = np.concatenate(xk, axis=0)
     freqs = rope_frequencies(g.rope_pairs, g.rope_theta)
+    local = np.arange(len(cached) + len(chunk))  # local temporal coordinate of each visible frame
 
     A = _Assembled()
     A.c, kr_hat = latents(xk, f(wts.w_dkv), f(wts.w_kr))
-    kcoords = token_coordinates(np.array(cached + chunk) - first, g.grid_h, g.grid_w)
+    kcoords = token_coordinates(local, g.grid_h, g.grid_w)
     A.kr = rope_rotate(kr_hat, kcoords, g.rope_pairs, freqs)
 
     qi = np.arange(g.chunk_frames * T) if query_tokens is None else np.asarray(query_tokens)
     xq = f(chunk_x).reshape(g.chunk_frames * T, g.hidden)[qi]
     A.q_nope, qr_hat = query_heads(xq, f(wts.w_dq), f(wts.w_uq), g.n_heads, g.d_nope, g.d_rope)
-    qcoords = token_coordinates(np.array(chunk) - first, g.grid_h, g.grid_w)[qi]
+    qcoords = token_coordinates(local[len(cached):], g.grid_h, g.grid_w)[qi]
     A.qr = rope_rotate(qr_hat, qcoords, g.rope_pairs, freqs)
     A.scale = 1.0 / np.sqrt(g.d_nope + g.d_rope)
     return A
@@ -221,17 +228,18 @@ def attend_dense(g, wts, history, n: int, chunk_x, query_tokens=None, dtype=np.f
     With return_scores, also the pre-softmax scores [n_heads, Nq, Nk]."""
     f = lambda a: np.asarray(a, dtype=dtype)
     T = g.grid_h * g.grid_w
-    first, cached, chunk = visible_frames(n, g.window_frames, g.chunk_frames)
+    cached, chunk = visible_frames(n, g.window_frames, g.chunk_frames, getattr(g, "sink_frames", 0))
     xk = np.concatenate([f(history[fr]).reshape(T, g.hidden) for fr in cached]
                         + [f(chunk_x).reshape(-1, g.hidden)], axis=0)
     dh = g.head_dim
     freqs = rope_frequencies(g.rope_pairs, g.rope_theta)
-    kc = token_coordinates(np.array(cached + chunk) - first, g.grid_h, g.grid_w)
+    local = np.arange(len(cached) + len(chunk))
+    kc = token_coordinates(local, g.grid_h, g.grid_w)
     k = rope_rotate((xk @ f(wts.w_k).T).reshape(-1, g.n_heads, dh), kc, g.rope_pairs, freqs)
     v = (xk @ f(wts.w_v).T).reshape(-1, g.n_heads, g.d_v)
     qi = np.arange(g.chunk_frames * T) if query_tokens is None else np.asarray(query_tokens)
     xq = f(chunk_x).reshape(-1, g.hidden)[qi]
-    qc = token_coordinates(np.array(chunk) - first, g.grid_h, g.grid_w)[qi]
+    qc = token_coordinates(local[len(cached):], g.grid_h, g.grid_w)[qi]
     q = rope_rotate((xq @ f(wts.w_q).T).reshape(-1, g.n_heads, dh), qc, g.rope_pairs, freqs)
     o = np.empty((len(qi), g.n_heads, g.d_v), dtype=dtype)
     sc = []

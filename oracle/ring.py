@@ -3,30 +3,35 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 VideoMLA paper, section 1 and appendix D.4: the cache is a fixed-size sliding
-window of latent frames; the oldest frame leaves when a new one arrives.
-Reading taken here: eviction is per frame and first-in first-out, and frame f
-lives in slot f mod W of a W-slot ring, so the frame written into a slot is
+window of latent frames; the oldest frame leaves when a new one arrives, and
+the long-horizon cache also pins sink frames.  Readings taken here: eviction is
+per frame and first-in first-out; the first S frames (S = sink_frames, 0 by
+default) stay in slots 0..S-1 for good; frame f >= S lives in slot
+S + (f - S) mod W of the W-slot ring, so the frame written into a slot is
 exactly the one that evicts the slot's previous occupant (f - W).
 """
 from __future__ import annotations
 
 
 class RingModel:
-    def __init__(self, window_frames: int, tokens_per_frame: int):
-        if window_frames <= 0 or tokens_per_frame <= 0:
+    def __init__(self, window_frames: int, tokens_per_frame: int, sink_frames: int = 0):
+        if window_frames <= 0 or tokens_per_frame <= 0 or sink_frames < 0:
             raise ValueError("window and frame size must be positive")
         self.W = window_frames
+        self.S = sink_frames
         self.T = tokens_per_frame
         self.n = 0  # frames appended so far
 
     def slot(self, frame: int) -> int:
-        return frame % self.W
+        return frame if frame < self.S else self.S + (frame - self.S) % self.W
 
     def row(self, frame: int, token: int) -> int:
         return self.slot(frame) * self.T + token
 
-    def valid_frames(self) -> range:
-        return range(max(0, self.n - self.W), self.n)
+    def valid_frames(self) -> list:
+        """Frames held, in context order: sink frames, then the window (oldest first)."""
+        sink = list(range(min(self.n, self.S)))
+        return sink + list(range(max(self.S, self.n - self.W), self.n))
 
     def valid_rows(self) -> int:
         return len(self.valid_frames()) * self.T

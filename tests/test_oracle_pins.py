@@ -341,3 +341,59 @@ def test_dense_window_excludes_evicted_frames():
     h3 = dict(hist)
     h3[3] = hist[0] * 3.0  # oldest visible frame
     assert np.abs(mla.attend_dense(g, w, h3, 5, chunk) - u).max() > 1e-6 * np.abs(u).max()
+
+
+
+# ----------------------------------------------------------------------------- sink frame + re-indexing
+TINY_SINK = wl.TINY.replace(name="tiny-sink", sink_frames=1)
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 4, 6])
+def test_sink_brute_force_matches_numpy(n):
+    """One pinned sink frame ahead of the 2-frame window: both formulations agree
+    at every window state (empty, sink only, partial, full, evicted)."""
+    g = TINY_SINK
+    w, hist, chunk = _tiny_inputs(n, "sharp", g=g)
+    u = mla.attend(g, w, hist, n, chunk)
+    ub = np.array(brute.attend(g, w, hist, n, chunk))
+    np.testing.assert_allclose(u, ub, rtol=1e-12, atol=1e-14 * np.abs(ub).max())
+
+
+def test_sink_visible_frames_and_local_coordinates():
+    # S = 1, W = 2, C = 1: the sink stays, the window slides, the gap collapses
+    assert mla.visible_frames(0, 2, 1, 1) == ([], [0])
+    assert mla.visible_frames(1, 2, 1, 1) == ([0], [1])
+    assert mla.visible_frames(3, 2, 1, 1) == ([0, 1, 2], [3])
+    assert mla.visible_frames(7, 2, 1, 1) == ([0, 5, 6], [7])
+    assert mla.visible_frames(7, 2, 1, 0) == ([5, 6], [7])
+
+
+def test_reindexing_makes_output_independent_of_absolute_time():
+    """With the sink and the window re-indexed (appendix D.5), an attend depends
+    only on the visible content: the same sink, window and chunk at frame 4 and at
+    frame 9 give the same output, to the last bit."""
+    g = TINY_SINK
+    w = wl.latent_weights(g, mode="sharp")
+    frame = lambda k: wl.hidden_states(g, chunk=k, mode="unit")[0]
+    chunk = wl.hidden_states(g, chunk=77, mode="unit")[0]
+    h1 = {0: frame(0), 2: frame(1), 3: frame(2)}     # n = 4: sink 0, window 2..3
+    h2 = {0: frame(0), 7: frame(1), 8: frame(2)}     # n = 9: sink 0, window 7..8
+    np.testing.assert_array_equal(mla.attend(g, w, h1, 4, chunk), mla.attend(g, w, h2, 9, chunk))
+    # the sink context is the plain window that holds the same frames in the same order
+    g0 = g.replace(sink_frames=0, window_frames=3)
+    a = mla.attend(g0, w, {1: frame(0), 2: frame(1), 3: frame(2)}, 4, chunk)
+    b = mla.attend(g, w, {0: frame(0), 2: frame(1), 3: frame(2)}, 4, chunk)
+    np.testing.assert_array_equal(a, b)  # same local frame order -> same result
+
+
+@pytest.mark.parametrize("S,W,C", [(1, 6, 3), (1, 2, 1), (2, 4, 2), (1, 5, 2)])
+def test_ring_model_with_sink(S, W, C):
+    r = ring.RingModel(W, 10, sink_frames=S)
+    for k in range(12):
+        r.append(C)
+        occ = r.slot_map()
+        assert len(occ) == len(r.valid_frames()) == min(r.n, S) + max(0, min(r.n - S, W))
+        assert all(occ[f] == f for f in range(min(r.n, S)))            # sinks pinned in slots 0..S-1
+        window = [f for f in r.valid_frames() if f >= S]
+        assert window == list(range(max(S, r.n - W), r.n))              # FIFO window
+        assert sorted(occ) == list(range(len(occ)))                      # occupied slots are a prefix
