@@ -219,7 +219,7 @@ def main():
 
     attn_ms = [ev.elapsed_ms(a, b) for a, b in ev_pairs[args.warmup * args.steps_per_chunk:]]
     attn_avg = float(np.mean(attn_ms))
-    n_frames = min(layer.state()[0], g.window_frames)  # window full for every timed step
+    n_frames = layer.state()[0]  # frames appended; n_k counts the visible ones (sinks + window)
     flops_attn = attention_flops(g, n_frames, expanded=args.path == "expanded")
     achieved = flops_attn / (attn_avg * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if g.dtype == wl.F32 else PEAK_BF16_TFLOPS

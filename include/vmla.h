@@ -66,9 +66,20 @@ enum { VMLA_DTYPE_BF16 = 0, VMLA_DTYPE_F32 = 1 };
  *   batch: independent streams advanced in lockstep (one frame counter).
  *   attn_workgroups: persistent attention workgroups (0 = 256, one per MI355X
  *     compute unit); it sizes part of the workspace.
- * Constraints (else VMLA_ERR_CONFIG): all sizes > 0;
+ *   sink_frames: S >= 0 pinned sink frames (appendix D.4: the long-horizon cache
+ *     keeps one sink latent frame ahead of a six-frame window).  The first S
+ *     frames appended stay in slots 0..S-1; later frames slide through the
+ *     window_frames FIFO slots.  The visible cache is sink frames [0, min(n, S))
+ *     plus window frames [max(S, n - window_frames), n).
+ *   rope_at_use: 0 rotates the decoupled key with its absolute frame index when
+ *     it is appended; 1 stores it un-rotated and rotates every visible key, and
+ *     the chunk's keys and queries, with local temporal coordinates: a frame's
+ *     index in [sink frames, window frames, chunk frames] (appendix D.5
+ *     re-indexing).  Without sinks both give the same scores (rotary relative
+ *     invariance); sink_frames > 0 requires rope_at_use = 1.
+ * Constraints (else VMLA_ERR_CONFIG): all sizes > 0 (sink_frames >= 0);
  *   1 <= chunk_frames <= window_frames; d_nope, d_rope, d_c, d_v, d_q and hidden
- *   multiples of 8; rope_theta > 0.
+ *   multiples of 8; rope_theta > 0; rope_at_use in {0, 1}.
  * Built kernels (else VMLA_ERR_UNSUPPORTED): (dtype, d_c, d_rope) in
  *   {(f32, 24, 8), (bf16, 24, 8), (bf16, 96, 32), (bf16, 192, 32), (bf16, 448, 32)}.
  */
@@ -88,6 +99,8 @@ typedef struct vmla_config {
   int32_t chunk_frames;
   int32_t dtype;
   int32_t attn_workgroups;
+  int32_t sink_frames;
+  int32_t rope_at_use;
 } vmla_config;
 
 /*
@@ -106,10 +119,12 @@ typedef struct vmla_weights {
 
 typedef struct vmla_ctx vmla_ctx; /* opaque; holds host-side metadata only */
 
-/* Bytes of the ring cache: batch * window_frames * T * (d_c + d_rope) elements.
- * Row (slot*T + s) of stream b holds [c (d_c) | k_r rotated (d_rope)] of token s
- * of the frame in that slot; frame f lives in slot f % window_frames.
- * Returns 0 for an invalid config. */
+/* Bytes of the ring cache: batch * (sink_frames + window_frames) * T *
+ * (d_c + d_rope) elements.  Row (slot*T + s) of stream b holds [c (d_c) | k_r
+ * (d_rope)] of token s of the frame in that slot, k_r rotated with the absolute
+ * frame index (rope_at_use = 0) or un-rotated (rope_at_use = 1); frame f lives
+ * in slot f if f < S, else in slot S + (f - S) % window_frames.  Occupied slots
+ * are always 0..(visible frames - 1).  Returns 0 for an invalid config. */
 VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg);
 
 /* Bytes of scratch device memory a ctx needs (chunk latents, absorbed queries,
@@ -154,8 +169,9 @@ VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEv
 VMLA_API int vmla_compress(vmla_ctx* ctx, const void* x, int64_t frame0, void* latents_out,
                            hipStream_t stream);
 
-/* Host metadata: frames appended n, first valid frame max(0, n-W), and the
- * number of valid frames min(n, W).  Any output pointer may be NULL. */
+/* Host metadata: frames appended n, the first window frame min(n, max(S, n-W))
+ * (= max(0, n-W) without sinks), and the number of visible cached frames
+ * min(n, S) + max(0, min(n - S, W)).  Any output pointer may be NULL. */
 VMLA_API int vmla_cache_state(const vmla_ctx* ctx, int64_t* frames_appended,
                               int64_t* first_valid_frame, int32_t* n_valid_frames);
 
@@ -206,7 +222,8 @@ VMLA_API int vmla_attend_expanded_profiled(vmla_ctx* ctx, const void* expanded, 
  * It takes the same vmla_config, read this way: d_rope = d_h (the rotated
  * per-head width; rope_pairs_* split its d_h/2 pairs), d_v = value width, and
  * d_nope = d_c = d_q = 0 (else VMLA_ERR_CONFIG).  Built kernels (else
- * VMLA_ERR_UNSUPPORTED): bf16 with d_rope = d_v = 128.
+ * VMLA_ERR_UNSUPPORTED): bf16 with d_rope = d_v = 128, sink_frames = 0 and
+ * rope_at_use = 0.
  *
  * Weights (Linear layout, bf16):
  *   w_q, w_k [n_heads*d_rope, hidden]; w_v [n_heads*d_v, hidden];

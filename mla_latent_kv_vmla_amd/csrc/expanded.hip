@@ -134,16 +134,19 @@ hipError_t run_expand(const Plan& p, const DensePlan& ex, void* wext_buf, int64_
   const long total = (long)p.nh * p.dh * p.D;
   build_key_lift<<<(int)((total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024), 256, 0, s>>>(
       wext, static_cast<const bf16*>(p.w_uk), p.nh, p.d_nope, p.dc, p.dr);
-  const int n_ring = (int)((n < p.W ? n : p.W) * p.Tpf);
-  up_project(p, ex, wext, p.cache, (long)p.W * p.Tpf * p.D, n_ring, static_cast<bf16*>(ex.kring),
-             static_cast<f16*>(ex.vring), ex.ring_stride, s);
+  const int n_ring = (int)(cached_frames(p, n) * p.Tpf);
+  // rope_at_use: up-project the window with k^ rotated at local coordinates
+  if (p.rope_at_use) run_assemble(p, n, s);
+  up_project(p, ex, wext, p.rope_at_use ? p.assembled : p.cache, (long)(p.S + p.W) * p.Tpf * p.D, n_ring,
+             static_cast<bf16*>(ex.kring), static_cast<f16*>(ex.vring), ex.ring_stride, s);
   return hipGetLastError();
 }
 
 hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* wext, int64_t n, const void* x,
                                void* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int M = p.B * p.Nq;
-  hipError_t err = run_compress(p, x, n, p.stage, false, s);
+  const int64_t tq = p.rope_at_use ? cached_frames(p, n) : n;  // temporal coordinate of the chunk's first frame
+  hipError_t err = run_compress(p, x, tq, p.stage, false, s);
   if (err != hipSuccess) return err;
   {  // c^Q = W_DQ x
     EpiStore<bf16> e{static_cast<bf16*>(p.cq), p.dq, 0};
@@ -157,7 +160,7 @@ hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* w
     e.dh = p.dh;
     e.d_nope = p.d_nope;
     e.qscale = p.qscale;
-    e.frame0 = n;
+    e.frame0 = tq;
     e.rope = latent_rope(p);
     gemm<bf16, false>(gops(p.w_uq, p.dq, 0, p.cq, p.dq, 0, p.nh * p.dh, M, p.dq), 1, e, s);
   }
@@ -181,7 +184,7 @@ hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* w
     a.B = p.B;
     a.H = p.nh;
     a.Nq = p.Nq;
-    a.n_ring = (int)((n < p.W ? n : p.W) * p.Tpf);
+    a.n_ring = (int)(cached_frames(p, n) * p.Tpf);
     a.ring_stride = ex.ring_stride;
     a.stage_stride = ex.stage_stride;
     a.G = ex.G;

@@ -24,6 +24,7 @@ struct Plan {
   DType dtype;
   int B, d, nh, d_nope, dr, dv, dc, dq, D, dh;  // D = dc + dr, dh = d_nope + dr
   int Tpf, grid_w, W, C, Nq;                    // tokens/frame, window and chunk frames
+  int S, rope_at_use;                           // sink frames; rotate k_r at use (local coordinates)
   int pairs_t, pairs_h, pairs_w;
   float freq[kMaxRopePairs];
   float qscale;  // log2(e) / sqrt(dh): softmax scale folded into the absorbed query
@@ -40,19 +41,32 @@ struct Plan {
   float *part_o; // [2G][kAttnMaxRows][dc] unnormalised partial outputs
   float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
   void *vtiles;  // transposed value-tile images of the visible keys (per call)
+  void *assembled;  // rope_at_use: the visible cache rows with k_r rotated at local coordinates
 };
 
+// Visible cached frames after n appends: sinks [0, min(n, S)) + window [max(S, n-W), n).
+inline int64_t cached_frames(const Plan& p, int64_t n) {
+  const int64_t sink = n < p.S ? n : p.S;
+  const int64_t win = n - p.S < p.W ? n - p.S : p.W;
+  return sink + (win > 0 ? win : 0);
+}
+
 struct WorkspaceLayout {
-  size_t stage, cq, qnope, qt, olat, o, part_o, part_ml, vtiles, total;
+  size_t stage, cq, qnope, qt, olat, o, part_o, part_ml, vtiles, assembled, total;
 };
 
 WorkspaceLayout workspace_layout(const Plan& p);
 
 // Kernel pipelines.  Each returns hipSuccess or the first launch error.
 // compress: rows [c | RoPE(k^)] of x for frames frame0.. into dst; ring != 0
-// writes row (frame % W)*Tpf + s of each stream's cache, else row t of dst.
+// writes the frame's ring slot row (slot*Tpf + s; sinks pinned) of each
+// stream's cache, else row t of dst.  k^ is rotated with frame index frame0 + i
+// unless the rows go to the ring of a rope_at_use layer (stored un-rotated).
 hipError_t run_compress(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring,
                         hipStream_t s);
+// rope_at_use: the visible cache rows after n appends, k^ rotated with each
+// frame's local coordinate, into p.assembled.
+hipError_t run_assemble(const Plan& p, int64_t n, hipStream_t s);
 // attend: full chunk attention against the ring holding n frames.
 hipError_t run_attend(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s,
                       hipEvent_t attn_start = nullptr, hipEvent_t attn_stop = nullptr);

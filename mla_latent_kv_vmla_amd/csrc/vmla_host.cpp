@@ -48,9 +48,11 @@ size_t elem_bytes(const vmla_config* c) { return c->dtype == VMLA_DTYPE_F32 ? 4 
 int check_common(const vmla_config* c) {
   if (c->batch <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->d_rope <= 0 || c->d_v <= 0 ||
       c->d_nope < 0 || c->d_c < 0 || c->d_q < 0 || c->grid_h <= 0 || c->grid_w <= 0 ||
-      c->window_frames <= 0 || c->chunk_frames <= 0 || c->attn_workgroups < 0)
+      c->window_frames <= 0 || c->chunk_frames <= 0 || c->attn_workgroups < 0 || c->sink_frames < 0)
     return VMLA_ERR_CONFIG;
   if (c->chunk_frames > c->window_frames) return VMLA_ERR_CONFIG;
+  if (c->rope_at_use != 0 && c->rope_at_use != 1) return VMLA_ERR_CONFIG;
+  if (c->sink_frames > 0 && !c->rope_at_use) return VMLA_ERR_CONFIG;
   if (c->rope_pairs_t < 0 || c->rope_pairs_h < 0 || c->rope_pairs_w < 0 ||
       2 * (c->rope_pairs_t + c->rope_pairs_h + c->rope_pairs_w) != c->d_rope ||
       c->d_rope / 2 > vmla::kMaxRopePairs)
@@ -61,7 +63,7 @@ int check_common(const vmla_config* c) {
   if (c->dtype != VMLA_DTYPE_BF16 && c->dtype != VMLA_DTYPE_F32) return VMLA_ERR_CONFIG;
   // sizes must fit the 32-bit row counters the kernels use
   const long long T = (long long)c->grid_h * c->grid_w;
-  const long long rows = T * c->window_frames + T * c->chunk_frames;
+  const long long rows = T * ((long long)c->sink_frames + c->window_frames) + T * c->chunk_frames;
   if (rows * c->n_heads > (1LL << 30) || (long long)c->batch * T * c->chunk_frames > (1LL << 30))
     return VMLA_ERR_CONFIG;
   return VMLA_OK;
@@ -74,7 +76,8 @@ int check_config(const vmla_config* c) {
   if (c->d_nope <= 0 || c->d_c <= 0 || c->d_q <= 0) return VMLA_ERR_CONFIG;
   // one stream's ring rows are addressed with 32-bit byte offsets
   const long long T = (long long)c->grid_h * c->grid_w;
-  if (T * c->window_frames * (c->d_c + c->d_rope) * (long long)elem_bytes(c) >= (1LL << 31))
+  if (T * ((long long)c->sink_frames + c->window_frames) * (c->d_c + c->d_rope) * (long long)elem_bytes(c) >=
+      (1LL << 31))
     return VMLA_ERR_CONFIG;
   if (!vmla::latent_attention_supported(static_cast<DType>(c->dtype), c->d_c, c->d_rope))
     return VMLA_ERR_UNSUPPORTED;
@@ -94,6 +97,7 @@ int check_dense_config(const vmla_config* c) {
   int st = check_common(c);
   if (st != VMLA_OK) return st;
   if (c->d_nope != 0 || c->d_c != 0 || c->d_q != 0) return VMLA_ERR_CONFIG;
+  if (c->sink_frames != 0 || c->rope_at_use != 0) return VMLA_ERR_UNSUPPORTED;
   // one (stream, head)'s keys and values are addressed with 32-bit byte offsets
   const int wmax = c->d_rope > c->d_v ? c->d_rope : c->d_v;
   if (dense_ring_stride(c) * wmax * 2 >= (1LL << 31)) return VMLA_ERR_CONFIG;
@@ -131,6 +135,8 @@ Plan geometry(const vmla_config* c) {
   p.W = c->window_frames;
   p.C = c->chunk_frames;
   p.Nq = c->chunk_frames * p.Tpf;
+  p.S = c->sink_frames;
+  p.rope_at_use = c->rope_at_use;
   p.pairs_t = c->rope_pairs_t;
   p.pairs_h = c->rope_pairs_h;
   p.pairs_w = c->rope_pairs_w;
@@ -162,7 +168,8 @@ WorkspaceLayout workspace_layout(const Plan& p) {
   L.o = take(M * p.nh * (size_t)p.dv * es);
   L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * sizeof(float));
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
-  L.vtiles = take(latent_value_tiles_bytes(p.dtype, p.dc, p.dr, p.B, p.W * p.Tpf, p.Nq));
+  L.vtiles = take(latent_value_tiles_bytes(p.dtype, p.dc, p.dr, p.B, (p.S + p.W) * p.Tpf, p.Nq));
+  L.assembled = take(p.rope_at_use ? (size_t)p.B * (p.S + p.W) * p.Tpf * p.D * es : 0);
   L.total = off;
   return L;
 }
@@ -208,7 +215,7 @@ ExpandedLayout expanded_layout(const Plan& p, DensePlan& ex) {
   for (int i = 0; i < kMaxRopePairs; ++i) ex.freq[i] = p.freq[i];
   ex.qscale = p.qscale;
   ex.G = p.G;
-  ex.ring_stride = (int)(((long)p.W * p.Tpf + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile);
+  ex.ring_stride = (int)(((long)(p.S + p.W) * p.Tpf + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile);
   ex.stage_stride = (p.Nq + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile;
   ExpandedLayout L;
   L.dense = dense_layout(ex);
@@ -247,7 +254,7 @@ extern "C" {
 
 VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg) {
   if (check_config(cfg) != VMLA_OK) return 0;
-  return (size_t)cfg->batch * cfg->window_frames * cfg->grid_h * cfg->grid_w *
+  return (size_t)cfg->batch * (cfg->sink_frames + cfg->window_frames) * cfg->grid_h * cfg->grid_w *
          (size_t)(cfg->d_c + cfg->d_rope) * elem_bytes(cfg);
 }
 
@@ -315,6 +322,7 @@ static Plan make_plan(const vmla_ctx* c) {
   p.part_o = reinterpret_cast<float*>(ws + L.part_o);
   p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
   p.vtiles = ws + L.vtiles;
+  p.assembled = ws + L.assembled;
   return p;
 }
 
@@ -358,10 +366,11 @@ VMLA_API int vmla_compress(vmla_ctx* ctx, const void* x, int64_t frame0, void* l
 VMLA_API int vmla_cache_state(const vmla_ctx* ctx, int64_t* frames_appended, int64_t* first_valid_frame,
                               int32_t* n_valid_frames) {
   if (!ctx) return VMLA_ERR_NULL;
-  const int64_t W = ctx->cfg.window_frames;
-  if (frames_appended) *frames_appended = ctx->n;
-  if (first_valid_frame) *first_valid_frame = ctx->n > W ? ctx->n - W : 0;
-  if (n_valid_frames) *n_valid_frames = (int32_t)(ctx->n < W ? ctx->n : W);
+  const int64_t W = ctx->cfg.window_frames, S = ctx->cfg.sink_frames, n = ctx->n;
+  const int64_t first_window = n - W > S ? n - W : S;
+  if (frames_appended) *frames_appended = n;
+  if (first_valid_frame) *first_valid_frame = first_window < n ? first_window : n;
+  if (n_valid_frames) *n_valid_frames = (int32_t)vmla::cached_frames(geometry(&ctx->cfg), n);
   return VMLA_OK;
 }
 

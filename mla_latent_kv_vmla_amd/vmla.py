@@ -38,7 +38,7 @@ class vmla_config(ctypes.Structure):
                 ("rope_pairs_t", c_int32), ("rope_pairs_h", c_int32), ("rope_pairs_w", c_int32),
                 ("rope_theta", c_float), ("grid_h", c_int32), ("grid_w", c_int32),
                 ("window_frames", c_int32), ("chunk_frames", c_int32), ("dtype", c_int32),
-                ("attn_workgroups", c_int32)]
+                ("attn_workgroups", c_int32), ("sink_frames", c_int32), ("rope_at_use", c_int32)]
 
 
 class vmla_weights(ctypes.Structure):
@@ -273,7 +273,8 @@ def config_from_geometry(g, attn_workgroups: int = 0) -> vmla_config:
                        rope_theta=g.rope_theta, grid_h=g.grid_h, grid_w=g.grid_w,
                        window_frames=g.window_frames, chunk_frames=g.chunk_frames,
                        dtype=VMLA_DTYPE_F32 if g.dtype == "f32" else VMLA_DTYPE_BF16,
-                       attn_workgroups=attn_workgroups)
+                       attn_workgroups=attn_workgroups, sink_frames=getattr(g, "sink_frames", 0),
+                       rope_at_use=1 if getattr(g, "sink_frames", 0) > 0 or getattr(g, "rope_at_use", False) else 0)
 
 
 def torch_dtype(g):
@@ -303,7 +304,7 @@ class LatentAttention:
             self.w[n] = t.to(device=device, dtype=self.dtype).contiguous()
         es = 4 if g.dtype == "f32" else 2
         self.cache = torch.empty(cb // es, dtype=self.dtype, device=device).view(
-            g.batch, g.window_frames * g.tokens_per_frame, g.latent_width)
+            g.batch, (getattr(g, "sink_frames", 0) + g.window_frames) * g.tokens_per_frame, g.latent_width)
         if cache_fill is not None:
             self.cache.fill_(cache_fill)
         self.workspace = torch.empty(wb, dtype=torch.uint8, device=device)

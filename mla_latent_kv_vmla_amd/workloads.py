@@ -55,6 +55,7 @@ class LayerGeometry:
     steps: int = 1
     prefill_chunks: int = 0  # seeded appends before the measured attend
     sink_frames: int = 0     # pinned sink frames ahead of the window (long-horizon cache)
+    rope_at_use: bool = False  # GPU layout choice: store k_r un-rotated, rotate per call (implied by sinks)
 
     @property
     def head_dim(self) -> int:
@@ -117,7 +118,11 @@ STRESS = {dc: WAN_LAYER.replace(name=f"stress-b4-w42-dc{dc}", batch=4, window_fr
 WAN_SMALL_GRID = WAN_LAYER.replace(name="wan-widths-grid6x10", grid_h=6, grid_w=10,
                                    window_frames=5, prefill_chunks=2)
 
-GEOMETRIES = {g.name: g for g in (TINY, TINY_DENSE, WAN_LAYER, WAN_ROLLOUT, WAN_DENSE, WAN_DENSE_SMALL_GRID,
+# The long-horizon cache of the pages' rollouts: one sink frame and a six-frame
+# window (10,920 cached keys), with re-indexed temporal coordinates.
+WAN_SINK = WAN_LAYER.replace(name="wan1.3b-sink1-w6", sink_frames=1, window_frames=6, prefill_chunks=7)
+
+GEOMETRIES = {g.name: g for g in (TINY, TINY_DENSE, WAN_LAYER, WAN_ROLLOUT, WAN_DENSE, WAN_DENSE_SMALL_GRID, WAN_SINK,
                                   WAN_SMALL_GRID,
                                   *STRESS.values())}
 

@@ -223,3 +223,25 @@ def test_expanded_bytes_and_state_checks():
         assert e.value.code == vmla.STATUS["VMLA_ERR_UNSUPPORTED"]
     finally:
         vmla.vmla_destroy(tiny)
+
+
+# ----------------------------------------------------------------------------- sink frames / rope at use
+def test_sink_config_rules():
+    g = wl.WAN_SINK
+    assert vmla.vmla_cache_bytes(_cfg(g)) == (1 + 6) * 1560 * 224 * 2  # one sink slot + six window slots
+    assert vmla.vmla_cache_bytes(_cfg(g, rope_at_use=0)) == 0           # a sink needs rotation at use
+    assert vmla.vmla_cache_bytes(_cfg(g, rope_at_use=2)) == 0
+    assert vmla.vmla_cache_bytes(_cfg(g, sink_frames=-1)) == 0
+    # rope at use without sinks is a valid layout choice
+    assert vmla.vmla_cache_bytes(_cfg(wl.WAN_LAYER, rope_at_use=1)) == vmla.vmla_cache_bytes(_cfg(wl.WAN_LAYER))
+    # the dense baseline has no sink / rotate-at-use kernel
+    c = _cfg(wl.WAN_DENSE, sink_frames=1, rope_at_use=1)
+    w = vmla.vmla_dense_weights(w_q=FAKE, w_k=FAKE + 256, w_v=FAKE + 512, w_o=FAKE + 768)
+    with pytest.raises(vmla.VmlaError) as e:
+        vmla.vmla_dense_create(c, w, FAKE, FAKE)
+    assert e.value.code == vmla.STATUS["VMLA_ERR_UNSUPPORTED"]
+    ctx = vmla.vmla_create(_cfg(g), _fake_weights(), FAKE, FAKE)
+    try:
+        assert vmla.vmla_cache_state(ctx) == (0, 0, 0)
+    finally:
+        vmla.vmla_destroy(ctx)
