@@ -47,6 +47,18 @@ def attention_flops(g, n_frames: int, expanded: bool = False) -> float:
     return rows * g.n_k(n_frames) * per
 
 
+def clip_attention_flops(g) -> float:
+    """Algorithmic FLOPs of one block-causal clip launch: block q's rows against
+    the keys of blocks 0..q."""
+    T, C, F = g.tokens_per_frame, g.chunk_frames, g.window_frames
+    per = 2.0 * (g.d_c + g.d_rope) + 2.0 * g.d_c
+    tot = 0.0
+    for q0 in range(0, F, C):
+        c = min(C, F - q0)
+        tot += g.batch * c * T * g.n_heads * (q0 + c) * T * per
+    return tot
+
+
 def attend_call_flops(g, n_frames: int, expanded: bool = False) -> float:
     """All algorithmic FLOPs of one attend call (projections + attention); for the
     expanded path the chunk's own keys/values are up-projected in the call (the
@@ -134,8 +146,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan1.3b-layer")
     ap.add_argument("--steps-per-chunk", type=int, default=4)
-    ap.add_argument("--path", choices=("absorbed", "expanded"), default="absorbed",
-                    help="latent layer: absorbed queries (default) or the window up-projected once per chunk")
+    ap.add_argument("--path", choices=("absorbed", "expanded", "clip"), default="absorbed",
+                    help="latent layer: absorbed queries (default), the window up-projected once per chunk, "
+                         "or one block-causal attend over a whole window-length clip per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="query tokens the CPU oracle baseline times (0 = the whole attend call)")
@@ -168,6 +181,9 @@ def main():
         layer = vmla.LatentAttention(g, {k: torch.from_numpy(v) for k, v in w.as_dict().items()})
         attend_profiled, append = vmla.vmla_attend_profiled, vmla.vmla_compress_append
         kernel = "flash_attn_kernel (latent, absorbed)"
+        if args.path == "clip":
+            clip_ws = torch.empty(vmla.vmla_clip_workspace_bytes(layer.cfg), dtype=torch.uint8, device=dev)
+            kernel = "flash_attn_kernel (latent, block-causal clip)"
         if args.path == "expanded":
             expanded = torch.empty(vmla.vmla_expanded_bytes(layer.cfg), dtype=torch.uint8, device=dev)
             attend_profiled = lambda ctx, x, o, a, b, st: vmla.vmla_attend_expanded_profiled(ctx, expanded, x, o, a,
@@ -183,6 +199,14 @@ def main():
     xs_np = [wl.hidden_states(g, chunk=g.prefill_chunks, step=s) for s in range(args.steps_per_chunk)]
     xs = [torch.from_numpy(a).to(dev, dt) for a in xs_np]
     out = torch.empty_like(xs[0])
+    if args.path == "clip":  # one whole window-length clip per step, no cache
+        if is_dense(g):
+            raise SystemExit("--path clip runs the latent layer")
+        args.steps_per_chunk = 1
+        gc = g.replace(chunk_frames=g.window_frames)
+        xs_np = [wl.hidden_states(gc, chunk=999)]
+        xs = [torch.from_numpy(xs_np[0]).to(dev, dt)]
+        out = torch.empty_like(xs[0])
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -193,6 +217,10 @@ def main():
                for _ in range(args.warmup + args.steps)]
 
     def step(i):
+        if args.path == "clip":
+            a, b = ev_pairs[i]
+            vmla.vmla_attend_clip_profiled(layer.ctx, xs[0], clip_ws, out, a, b, sh)
+            return
         if args.path == "expanded" and not is_dense(g):
             vmla.vmla_expand(layer.ctx, expanded, sh)  # once per chunk: the frozen window's per-head K/V
         for s in range(args.steps_per_chunk):
@@ -220,12 +248,16 @@ def main():
     attn_ms = [ev.elapsed_ms(a, b) for a, b in ev_pairs[args.warmup * args.steps_per_chunk:]]
     attn_avg = float(np.mean(attn_ms))
     n_frames = layer.state()[0]  # frames appended; n_k counts the visible ones (sinks + window)
-    flops_attn = attention_flops(g, n_frames, expanded=args.path == "expanded")
+    flops_attn = (clip_attention_flops(g) if args.path == "clip"
+                  else attention_flops(g, n_frames, expanded=args.path == "expanded"))
     achieved = flops_attn / (attn_avg * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if g.dtype == wl.F32 else PEAK_BF16_TFLOPS
-    tokens_per_step = g.batch * g.n_q * args.steps_per_chunk
+    tokens_per_step = (g.batch * g.window_frames * g.tokens_per_frame if args.path == "clip"
+                       else g.batch * g.n_q * args.steps_per_chunk)
     value = tokens_per_step / (ms_per_step * 1e-3)
     call_flops = attend_call_flops(g, n_frames, expanded=args.path == "expanded")
+    if args.path == "clip":
+        call_flops = flops_attn
 
     if args.calibrate_copy_mb > 0:
         nbytes = args.calibrate_copy_mb << 20
@@ -248,12 +280,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if g.dtype == wl.F32 else "bf16",
         "data": "synthetic (seeded N(0,1)/sqrt(fan_in) weights and hidden states)",
-        "config": {"workload": g.name if args.path == "absorbed" else f"{g.name}-expanded", "batch": g.batch, "query_tokens_per_call": g.n_q,
-                   "keys_per_call": g.n_k(n_frames), "heads": g.n_heads, "head_dim": g.head_dim,
+        "config": {"workload": g.name if args.path == "absorbed" else f"{g.name}-{args.path}", "batch": g.batch,
+                   "query_tokens_per_call": g.window_frames * g.tokens_per_frame if args.path == "clip" else g.n_q,
+                   "keys_per_call": (g.window_frames * g.tokens_per_frame if args.path == "clip"
+                                     else g.n_k(n_frames)),
+                   "heads": g.n_heads, "head_dim": g.head_dim,
                    "d_c": g.d_c, "d_rope": g.d_rope,
                    "window_frames": g.window_frames, "chunk_frames": g.chunk_frames,
                    "attends_per_step": args.steps_per_chunk, "appends_per_step": 1,
-                   "expands_per_step": 1 if args.path == "expanded" else 0},
+                   "expands_per_step": 1 if args.path == "expanded" else 0, "sink_frames": g.sink_frames},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_from_counters(g) if args.path == "absorbed" else None,
                      "kernel": kernel,
@@ -261,7 +296,7 @@ def main():
         "attend_call_tflops": call_flops * args.steps_per_chunk / (ms_per_step * 1e-3) / 1e12,
         "wall_s_timed_region": wall,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.path != "clip":
         res["cpu_baseline"] = cpu_baseline(g, w, hist, n_prefill, xs_np[0][0], args.cpu_sample_tokens or g.n_q)
     for a, b in ev_pairs:
         ev.destroy(a)

@@ -182,6 +182,27 @@ VMLA_API int vmla_reset(vmla_ctx* ctx);
 VMLA_API void vmla_destroy(vmla_ctx* ctx);
 
 /*
+ * Block-causal clip (the training-time form of the layer, appendix D.4): all
+ * window_frames frames of one clip attend at once, tokens of chunk q (frames
+ * [q*C, (q+1)*C)) seeing every token of chunks 0..q; the ring cache is neither
+ * read nor written and the frame counter is unchanged.  Temporal coordinates
+ * are the clip's frame indices 0..window_frames-1.  Key tiles above the block
+ * diagonal are skipped.
+ * vmla_clip_workspace_bytes: bytes of the caller-owned clip workspace (the
+ *   per-call buffers of vmla_attend sized for window_frames*T query tokens).
+ * vmla_attend_clip: x and out are [batch, window_frames*T, hidden]; same rules
+ *   as vmla_attend (window_frames must be a multiple of chunk_frames for whole
+ *   blocks; a shorter last block is allowed).
+ */
+VMLA_API size_t vmla_clip_workspace_bytes(const vmla_config* cfg);
+VMLA_API int vmla_attend_clip(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out,
+                              hipStream_t stream);
+/* vmla_attend_clip plus caller-made events recorded right before and after the
+ * attention kernel (NULL -> VMLA_ERR_NULL). */
+VMLA_API int vmla_attend_clip_profiled(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out,
+                                       hipEvent_t attn_start, hipEvent_t attn_stop, hipStream_t stream);
+
+/*
  * Expanded (non-absorbed) latent path (paper section 3.3: the cached latents
  * are up-projected to per-head keys and values, which are then attended like a
  * dense layer).  Same result as vmla_attend up to rounding; for the

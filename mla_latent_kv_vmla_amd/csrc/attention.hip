@@ -77,6 +77,10 @@ template <typename T> struct FlashArgs {
   float* part_ml;           // [2G][kAttnMaxRows][2]
   int len0, len1, tiles0;   // keys per segment, key tiles of segment 0
   int R, RB, KT, S, G;      // rows per stream, row blocks per stream, key tiles, streams, workgroups
+  // Block-causal mode (causal_tokens > 0; keys in segment 1 only): row r sees
+  // keys [0, (t / causal_tokens + 1) * causal_tokens) with t = r / row_div its
+  // token.  One workgroup per row block, longest rows first, no split.
+  int causal_tokens, row_div;
 };
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
@@ -264,6 +268,12 @@ void flash_attn_kernel(FlashArgs<T> p) {
     }
   };
 
+  const bool causal = p.causal_tokens > 0;
+  // token limit (exclusive) of the keys row r may see in block-causal mode
+  auto row_limit = [&](int r) {
+    const int lim = (r / p.row_div / p.causal_tokens + 1) * p.causal_tokens;
+    return lim < p.len1 ? lim : p.len1;
+  };
   const long I = (long)p.S * p.RB * p.KT;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2); the virtual index gives the workgroups of one XCD one contiguous share
@@ -275,17 +285,30 @@ void flash_attn_kernel(FlashArgs<T> p) {
   // the last may end inside a row block.  The last piece (which starts at key
   // tile 0) is processed first, so every workgroup sweeps the key tiles in
   // increasing order from near tile 0 and the workgroups sharing an L2 stay
-  // within a few dozen tiles of one another.
-  const long u_first = it0 / p.KT;
-  const int npieces = (int)((it1 - 1) / p.KT - u_first + 1);
+  // within a few dozen tiles of one another.  Block-causal mode: one whole row
+  // block per workgroup, the longest (last) row blocks first.
+  const long u_first = causal ? (long)p.S * p.RB - 1 - blockIdx.x : it0 / p.KT;
+  const int npieces = causal ? 1 : (int)((it1 - 1) / p.KT - u_first + 1);
   for (int k = 0; k < npieces; ++k) {
     const int piece = npieces > 1 ? (k == 0 ? npieces - 1 : k - 1) : 0;
     const long unit = u_first + piece;
-    const int kt0 = piece == 0 ? (int)(it0 % p.KT) : 0;
-    const int kt1 = piece == npieces - 1 ? (int)((it1 - 1) % p.KT) + 1 : p.KT;
     const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
+    int kt0, kt1;
+    if (causal) {  // tiles up to the last row's limit; the tiles above the block diagonal are skipped
+      const int last_row = min((rb + 1) * (NW * RW), p.R) - 1;
+      kt0 = 0;
+      kt1 = p.tiles0 + (row_limit(last_row) + KTILE - 1) / KTILE;
+    } else {
+      kt0 = piece == 0 ? (int)(it0 % p.KT) : 0;
+      kt1 = piece == npieces - 1 ? (int)((it1 - 1) % p.KT) + 1 : p.KT;
+    }
     const bool first_piece = piece == 0;
     const int row0 = rb * (NW * RW) + wave * RW;
+    // keys from which this workgroup's rows (uniform) / this lane's rows need masking
+    const int mask_from_wg = causal ? row_limit(rb * (NW * RW)) : 0x7fffffff;
+    int mask_from[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) mask_from[nb] = causal ? row_limit(row0 + 32 * nb + l32) : 0x7fffffff;
 
     typename MF::Frag qf[NB][NKS];
 #pragma unroll
@@ -345,14 +368,17 @@ void flash_attn_kernel(FlashArgs<T> p) {
           }
         }
         // the tail mask and the rescale below are rare: the empty volatile asm
-        // keeps each a real (uniform) branch instead of code run on every block
-        if (kbase + 32 * kb + 32 > len) {
+        // keeps each a real (uniform) branch instead of code run on every block.
+        // Keys past the segment's end, or (block-causal) past a row's limit, are masked.
+        if (kbase + 32 * kb + 32 > min(len, mask_from_wg)) {
           asm volatile("");
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            if (kbase + 32 * kb + 8 * (rr >> 2) + 4 * h32 + (rr & 3) >= len)
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = kbase + 32 * kb + 8 * (rr >> 2) + 4 * h32 + (rr & 3);
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) sc[nb][rr] = NEG_INF;
+            for (int nb = 0; nb < NB; ++nb)
+              if (key >= len || key >= mask_from[nb]) sc[nb][rr] = NEG_INF;
+          }
         }
         // online softmax per query row (lane pair); every piece's first block
         // holds a valid key, so m_run is finite before any all-masked block
@@ -450,7 +476,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
       if (t + 1 < kt1) step(t + 1, lds1, lds0);
     }
 
-    const bool full = (kt0 == 0 && kt1 == p.KT);
+    const bool full = causal || (kt0 == 0 && kt1 == p.KT);
     T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -544,13 +570,16 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   a.tiles0 = (a.len0 + KTILE - 1) / KTILE;
   a.KT = a.tiles0 + (a.len1 + KTILE - 1) / KTILE;
   const long I = (long)a.S * a.RB * a.KT;
-  a.G = (int)(G < I ? G : I);
+  const bool causal = a.causal_tokens > 0;
+  a.G = causal ? a.S * a.RB : (int)(G < I ? G : I);  // block-causal: one workgroup per row block
+  if (a.row_div <= 0) a.row_div = 1;
   if constexpr (!VROWS) latent_value_tiles<T, D, DV, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
   hipError_t err;
   if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
   flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS><<<a.G, NW * 64, 0, s>>>(a);
   if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
-  if (I != (long)a.G * a.KT) flash_attn_combine<T, DV, ROWS><<<a.S * a.RB * (ROWS / 16), 256, 0, s>>>(a);
+  if (!causal && I != (long)a.G * a.KT)
+    flash_attn_combine<T, DV, ROWS><<<a.S * a.RB * (ROWS / 16), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -607,6 +636,8 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
   a.len1 = c.n_stage;
   a.R = c.R;
   a.S = c.B;
+  a.causal_tokens = c.causal_tokens;
+  a.row_div = c.R / c.n_stage;  // rows are (token, head) pairs
   if constexpr (std::is_same<T, float>::value) {
     if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     return hipErrorInvalidValue;

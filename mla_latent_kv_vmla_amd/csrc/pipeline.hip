@@ -235,6 +235,7 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
     a.G = p.G;
     a.ev_start = ev0;
     a.ev_stop = ev1;
+    a.causal_tokens = p.causal_tokens;
     err = run_latent_attention(a, s);
     if (err != hipSuccess) return err;
   }

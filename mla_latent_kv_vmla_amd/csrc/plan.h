@@ -25,6 +25,7 @@ struct Plan {
   int B, d, nh, d_nope, dr, dv, dc, dq, D, dh;  // D = dc + dr, dh = d_nope + dr
   int Tpf, grid_w, W, C, Nq;                    // tokens/frame, window and chunk frames
   int S, rope_at_use;                           // sink frames; rotate k_r at use (local coordinates)
+  int causal_tokens;  // > 0: a whole clip of Nq tokens, block-causal in blocks of this many tokens
   int pairs_t, pairs_h, pairs_w;
   float freq[kMaxRopePairs];
   float qscale;  // log2(e) / sqrt(dh): softmax scale folded into the absorbed query
@@ -87,6 +88,7 @@ struct AttnCall {
   long cache_bstride, stage_bstride;  // elements
   int B, R, n_ring, n_stage;
   int G;
+  int causal_tokens;  // > 0: block-causal over the staged keys only (n_ring = 0), blocks of this many tokens
 };
 hipError_t run_latent_attention(const AttnCall& a, hipStream_t s);
 bool latent_attention_supported(DType dt, int dc, int dr);

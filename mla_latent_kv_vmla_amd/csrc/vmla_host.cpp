@@ -382,6 +382,65 @@ VMLA_API int vmla_reset(vmla_ctx* ctx) {
   return VMLA_OK;
 }
 
+/* ------------------------------------------------------- block-causal clip */
+
+// Plan of a whole clip of window_frames frames: W*T query tokens, no ring,
+// block-causal in chunk_frames*T token blocks.
+static Plan clip_geometry(const vmla_config* cfg) {
+  Plan p = geometry(cfg);
+  p.causal_tokens = p.C * p.Tpf;
+  p.C = p.W;
+  p.Nq = p.W * p.Tpf;
+  return p;
+}
+
+VMLA_API size_t vmla_clip_workspace_bytes(const vmla_config* cfg) {
+  if (check_config(cfg) != VMLA_OK) return 0;
+  return vmla::workspace_layout(clip_geometry(cfg)).total;
+}
+
+static int attend_clip(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out, hipEvent_t e0, hipEvent_t e1,
+                       hipStream_t stream) {
+  if (!aligned16(x) || !aligned16(clip_workspace) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  Plan p = clip_geometry(&ctx->cfg);
+  for (int i = 0; i < vmla::kMaxRopePairs; ++i) p.freq[i] = ctx->freq[i];
+  const Plan base = make_plan(ctx);  // weights and cache pointers
+  p.w_dkv = base.w_dkv;
+  p.w_kr = base.w_kr;
+  p.w_dq = base.w_dq;
+  p.w_uq = base.w_uq;
+  p.w_uk = base.w_uk;
+  p.w_uv = base.w_uv;
+  p.w_o = base.w_o;
+  p.cache = base.cache;
+  const vmla::WorkspaceLayout L = vmla::workspace_layout(p);
+  char* ws = static_cast<char*>(clip_workspace);
+  p.stage = ws + L.stage;
+  p.cq = ws + L.cq;
+  p.qnope = ws + L.qnope;
+  p.qt = ws + L.qt;
+  p.olat = ws + L.olat;
+  p.o = ws + L.o;
+  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  p.vtiles = ws + L.vtiles;
+  p.assembled = ws + L.assembled;
+  // the clip's frames are 0..W-1 and nothing is cached: attend at n = 0
+  if (vmla::run_attend(p, 0, x, out, stream, e0, e1) != hipSuccess) return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_attend_clip(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out, hipStream_t stream) {
+  if (!ctx || !x || !clip_workspace || !out) return VMLA_ERR_NULL;
+  return attend_clip(ctx, x, clip_workspace, out, nullptr, nullptr, stream);
+}
+
+VMLA_API int vmla_attend_clip_profiled(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out,
+                                       hipEvent_t attn_start, hipEvent_t attn_stop, hipStream_t stream) {
+  if (!ctx || !x || !clip_workspace || !out || !attn_start || !attn_stop) return VMLA_ERR_NULL;
+  return attend_clip(ctx, x, clip_workspace, out, attn_start, attn_stop, stream);
+}
+
 /* ------------------------------------------------------- expanded latent path */
 
 static bool expanded_ok(const vmla_config* cfg) {

@@ -89,6 +89,13 @@ def lib():
         L.vmla_reset.restype = c_int
         L.vmla_destroy.argtypes = [c_void_p]
         L.vmla_destroy.restype = None
+        L.vmla_clip_workspace_bytes.argtypes = [POINTER(vmla_config)]
+        L.vmla_clip_workspace_bytes.restype = c_size_t
+        L.vmla_attend_clip.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.vmla_attend_clip.restype = c_int
+        L.vmla_attend_clip_profiled.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                c_void_p]
+        L.vmla_attend_clip_profiled.restype = c_int
         L.vmla_expanded_bytes.argtypes = [POINTER(vmla_config)]
         L.vmla_expanded_bytes.restype = c_size_t
         L.vmla_expand.argtypes = [c_void_p, c_void_p, c_void_p]
@@ -191,6 +198,20 @@ def vmla_reset(ctx) -> None:
 
 def vmla_destroy(ctx) -> None:
     lib().vmla_destroy(ctx)
+
+
+def vmla_clip_workspace_bytes(cfg: vmla_config) -> int:
+    return lib().vmla_clip_workspace_bytes(byref(cfg))
+
+
+def vmla_attend_clip(ctx, x, clip_workspace, out, stream=None) -> None:
+    _check(lib().vmla_attend_clip(ctx, _ptr(x), _ptr(clip_workspace), _ptr(out), _stream(stream)),
+           "vmla_attend_clip")
+
+
+def vmla_attend_clip_profiled(ctx, x, clip_workspace, out, attn_start: int, attn_stop: int, stream=None) -> None:
+    _check(lib().vmla_attend_clip_profiled(ctx, _ptr(x), _ptr(clip_workspace), _ptr(out), attn_start, attn_stop,
+                                           _stream(stream)), "vmla_attend_clip_profiled")
 
 
 def vmla_expanded_bytes(cfg: vmla_config) -> int:
@@ -341,6 +362,21 @@ class LatentAttention:
 
     def reset(self):
         vmla_reset(self.ctx)
+
+    def attend_clip(self, x, out=None, stream=None):
+        """Block-causal attention over a whole clip x [batch, window_frames*T, hidden]."""
+        import torch
+        g = self.g
+        shape = (g.batch, g.window_frames * g.tokens_per_frame, g.hidden)
+        if tuple(x.shape) != shape or x.dtype != self.dtype or not x.is_contiguous():
+            raise ValueError(f"x must be contiguous {self.dtype} of shape {shape}")
+        if getattr(self, "clip_workspace", None) is None:
+            self.clip_workspace = torch.empty(vmla_clip_workspace_bytes(self.cfg), dtype=torch.uint8,
+                                              device=self.cache.device)
+        if out is None:
+            out = torch.empty_like(x)
+        vmla_attend_clip(self.ctx, x, self.clip_workspace, out, stream)
+        return out
 
     def expand(self, stream=None):
         """Up-project the window to per-head keys/values (expanded path) into an

@@ -178,6 +178,24 @@ def attend(g, wts, history, n: int, chunk_x, query_tokens=None, dtype=np.float64
     return (u, probs) if return_probs else u
 
 
+def attend_clip(g, wts, clip_x, dtype=np.float64):
+    """Block-causal attention over a whole clip of window_frames frames (the
+    training-time form, appendix D.4): tokens of chunk q (frames [qC, (q+1)C),
+    the last chunk possibly shorter) attend to every token of chunks 0..q, with
+    the clip's frame indices as temporal coordinates.  Written as the definition
+    composes: chunk q is an attend() whose cached frames are all earlier frames."""
+    T = g.grid_h * g.grid_w
+    F, C = g.window_frames, g.chunk_frames
+    frames = np.asarray(clip_x).reshape(F, T, g.hidden)
+    out = []
+    for q0 in range(0, F, C):
+        c = min(C, F - q0)
+        gq = g.replace(chunk_frames=c, sink_frames=0) if hasattr(g, "replace") else g
+        hist = {f: frames[f] for f in range(q0)}
+        out.append(attend(gq, wts, hist, q0, frames[q0:q0 + c].reshape(c * T, g.hidden), dtype=dtype))
+    return np.concatenate(out, axis=0)
+
+
 def attend_absorbed(g, wts, history, n: int, chunk_x, query_tokens=None, dtype=np.float64):
     """Same attention with W_UK folded into the query and W_UV applied after the
     probability-weighted sum of latents (the MLA absorption identity).  Kept only

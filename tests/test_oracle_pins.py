@@ -397,3 +397,36 @@ def test_ring_model_with_sink(S, W, C):
         window = [f for f in r.valid_frames() if f >= S]
         assert window == list(range(max(S, r.n - W), r.n))              # FIFO window
         assert sorted(occ) == list(range(len(occ)))                      # occupied slots are a prefix
+
+
+
+# ----------------------------------------------------------------------------- block-causal clip
+def test_clip_matches_masked_full_attention():
+    """attend_clip (chunk by chunk) against the masked formulation: one score
+    matrix over the whole clip with key j hidden from query i when j's chunk is
+    later than i's (-inf before the softmax)."""
+    g = wl.TINY.replace(name="tiny-clip", window_frames=5, chunk_frames=2)   # chunks of 2, 2, 1 frames
+    w = wl.latent_weights(g, mode="sharp")
+    T, F = 16, 5
+    x = wl.hidden_states(g.replace(chunk_frames=F), chunk=3, mode="unit")[0].astype(np.float64)
+    u = mla.attend_clip(g, w, x)
+    # independent assembly over the full clip
+    c, kr_hat = mla.latents(x, w.w_dkv, w.w_kr)
+    freqs = mla.rope_frequencies(g.rope_pairs, g.rope_theta)
+    coords = mla.token_coordinates(np.arange(F), 4, 4)
+    kr = mla.rope_rotate(kr_hat, coords, g.rope_pairs, freqs)
+    q_nope, qr_hat = mla.query_heads(x, w.w_dq, w.w_uq, g.n_heads, g.d_nope, g.d_rope)
+    qr = mla.rope_rotate(qr_hat, coords, g.rope_pairs, freqs)
+    chunk = np.arange(F * T) // T // 2
+    hidden = chunk[None, :] > chunk[:, None]
+    o = []
+    for h in range(g.n_heads):
+        s_ = (q_nope[:, h] @ (c @ w.w_uk[h].T).T + qr[:, h] @ kr.T) / np.sqrt(g.d_nope + g.d_rope)
+        s_[hidden] = -np.inf
+        p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        p_ /= p_.sum(axis=1, keepdims=True)
+        o.append(p_ @ (c @ w.w_uv[h].T))
+    ref = np.concatenate(o, axis=1) @ w.w_o.T
+    np.testing.assert_allclose(u, ref, rtol=1e-10, atol=1e-13)
+    # the first chunk sees only itself; the second does see the first
+    np.testing.assert_allclose(u[:2 * T], mla.attend(g, w, {}, 0, x[:2 * T]), rtol=1e-12)
