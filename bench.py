@@ -139,6 +139,69 @@ def cpu_baseline(g, w, hist, n, x, sample_tokens: int):
                        f"against the full {g.n_k(n)} keys, float64 numpy; {dt:.1f} s")}
 
 
+def capacity_run(args):
+    """Memory-headroom sweep: the largest batch of independent streams whose
+    30-layer caches stay resident on this GPU, for the latent layer at several
+    d_c and for the dense baseline (arithmetic from the library's layouts, priced
+    against this GPU's free memory).  Then, for the latent layer at d_c = 192 and
+    for the dense layer, allocate exactly that: 30 layers' caches and weights plus
+    one layer's per-call buffers, fill the first layer's window (7 chunk appends)
+    and time one more append and one attend at that batch.  Inputs are seeded and
+    generated on the device; only the first layer's ring is read, the others
+    stand for the resident caches of a 30-layer model."""
+    import torch
+    from mla_latent_kv_vmla_amd import capacity as cap, vmla, workloads as wl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    free, total = torch.cuda.mem_get_info()
+    budget = free - (6 << 30)  # runtime, code objects and allocator rounding
+    layers = 30
+    sweep = []
+    for dc in (64, 128, 192, 256, 512):
+        c = cap.capacity(wl.WAN_LAYER.replace(d_c=dc), layers, budget)
+        sweep.append({"d_c": dc, "per_stream_gb": round(c.per_stream_bytes / 1e9, 4), "max_batch": int(c.max_batch)})
+    d = cap.capacity(wl.WAN_DENSE, layers, budget, dense=True)
+    dense = {"per_stream_gb": round(d.per_stream_bytes / 1e9, 4), "max_batch": int(d.max_batch)}
+    runs = {}
+    gen = torch.Generator(device=dev).manual_seed(11)
+    for name, g0, B, is_dense in (("latent_dc192", wl.WAN_LAYER, sweep[2]["max_batch"], False),
+                                  ("dense", wl.WAN_DENSE, dense["max_batch"], True)):
+        g = g0.replace(batch=B)
+        print(f"capacity: {name} batch {B}", file=sys.stderr, flush=True)
+        w = (wl.dense_weights if is_dense else wl.latent_weights)(g).__dict__
+        lay = (vmla.DenseAttention if is_dense else vmla.LatentAttention)(g, w, device=dev)
+        wbytes = sum(t.numel() * t.element_size() for t in lay.w.values())
+        others = [torch.empty(lay.cache.numel() * lay.cache.element_size() + wbytes, dtype=torch.uint8, device=dev)
+                  for _ in range(layers - 1)]
+        x = torch.randn(B, g.n_q, g.hidden, generator=gen, device=dev, dtype=torch.bfloat16).mul_(g.hidden ** -0.5)
+        out = torch.empty_like(x)
+        allocated = torch.cuda.memory_allocated(dev)
+        for _ in range(g.window_frames // g.chunk_frames):
+            lay.append(x)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        lay.attend(x, out=out)
+        e[1].record()
+        lay.append(x)
+        e[2].record()
+        torch.cuda.synchronize()
+        attend_ms = e[0].elapsed_time(e[1])
+        runs[name] = {"batch": B, "allocated_gb": round(allocated / 1e9, 2), "frames_cached": lay.state()[2],
+                      "attend_ms": round(attend_ms, 2), "append_ms": round(e[1].elapsed_time(e[2]), 2),
+                      "attend_tokens_per_s": round(B * g.n_q / (attend_ms / 1e3)),
+                      "output_finite": all(bool(torch.isfinite(out[i:i + 8]).all().item()) for i in range(0, B, 8))}
+        lay.close()
+        del lay, others, x, out
+        torch.cuda.empty_cache()
+    res = {"metric": "streams with 30-layer caches resident on one GPU (memory-headroom sweep)",
+           "budget_gb": round(budget / 1e9, 2), "device_total_gb": round(total / 1e9, 2), "layers": layers,
+           "workload": f"{wl.WAN_LAYER.name} chunk, {wl.WAN_LAYER.window_frames}-frame window",
+           "latent": sweep, "dense": dense,
+           "headroom_x": {str(r["d_c"]): round(r["max_batch"] / max(1, dense["max_batch"]), 2) for r in sweep},
+           "run": runs}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +217,8 @@ def main():
                     help="query tokens the CPU oracle baseline times (0 = the whole attend call)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after timing, run plain device copies of this size (counter calibration)")
+    ap.add_argument("--capacity", action="store_true",
+                    help="instead of the throughput step: the memory-headroom batch sweep (see capacity_run)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -162,6 +227,10 @@ def main():
               "(see the sharding paragraph of the design notes); --gpus above 1 is not supported.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.capacity:
+        capacity_run(args)
+        return
 
     import numpy as np
     import torch

@@ -1,0 +1,95 @@
+"""Serving capacity of one GPU: how many independent streams fit.
+
+Per stream, a rollout keeps every layer's cache resident (latent rows
+[c | k_r] per token, or per-head K and V for the dense baseline), while the
+per-call buffers (workspace, hidden states in and out) exist for one layer at
+a time and scale with the batch; the layers' weights are a fixed cost.  The
+layouts are the library's: `vmla_cache_bytes` / `vmla_workspace_bytes` (latent)
+and `vmla_dense_cache_bytes` / `vmla_dense_workspace_bytes` (dense); the
+formulas below restate them so that latent widths without a built kernel can be
+priced too, and a test checks them against the library for every built shape
+(VideoMLA paper, section 4.3 "Batch Scaling Under Fixed Memory" runs the same
+sweep on its own hardware).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+ALIGN = 256
+ATTN_MAX_ROWS = 256
+DEFAULT_WORKGROUPS = 256
+DENSE_KEY_TILE = 128
+
+
+def _al(x: int) -> int:
+    return (x + ALIGN - 1) // ALIGN * ALIGN
+
+
+def latent_cache_bytes(g, batch: int = 1, es: int = 2) -> int:
+    return batch * (g.sink_frames + g.window_frames) * g.tokens_per_frame * (g.d_c + g.d_rope) * es
+
+
+def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
+                           workgroups: int = DEFAULT_WORKGROUPS) -> int:
+    """Mirror of the library's latent workspace layout for `batch` streams."""
+    M = batch * g.n_q
+    D, nh = g.d_c + g.d_rope, g.n_heads
+    dcp = (g.d_c + 31) // 32 * 32
+    tiles = (-(-(g.sink_frames + g.window_frames) * g.tokens_per_frame // key_tile)
+             + -(-g.n_q // key_tile))
+    parts = [M * D * es, M * g.d_q * es, M * nh * g.d_nope * es, M * nh * D * es, M * nh * g.d_c * es,
+             M * nh * g.d_v * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * 4, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
+             batch * tiles * dcp * (key_tile + 16 // es) * es,
+             batch * (g.sink_frames + g.window_frames) * g.tokens_per_frame * D * es if g.rope_at_use or g.sink_frames
+             else 0]
+    return sum(_al(x) for x in parts)
+
+
+def dense_cache_bytes(g, batch: int = 1) -> int:
+    P = -(-g.window_frames * g.tokens_per_frame // DENSE_KEY_TILE) * DENSE_KEY_TILE
+    heads = batch * g.n_heads
+    return _al(heads * P * g.head_dim * 2) + _al(heads * P * g.d_v * 2)
+
+
+def dense_workspace_bytes(g, batch: int = 1, workgroups: int = DEFAULT_WORKGROUPS) -> int:
+    S = -(-g.n_q // DENSE_KEY_TILE) * DENSE_KEY_TILE
+    heads = batch * g.n_heads
+    parts = [heads * g.n_q * g.head_dim * 2, heads * S * g.head_dim * 2, heads * S * g.d_v * 2,
+             batch * g.n_q * g.n_heads * g.d_v * 2, 2 * workgroups * ATTN_MAX_ROWS * g.d_v * 4,
+             2 * workgroups * ATTN_MAX_ROWS * 2 * 4]
+    return sum(_al(x) for x in parts)
+
+
+def latent_weight_bytes(g, es: int = 2) -> int:
+    d, nh = g.hidden, g.n_heads
+    return es * (g.d_c * d + g.d_rope * d + g.d_q * d + nh * g.head_dim * g.d_q + nh * g.d_nope * g.d_c
+                 + nh * g.d_v * g.d_c + d * nh * g.d_v)
+
+
+def dense_weight_bytes(g, es: int = 2) -> int:
+    d, nh = g.hidden, g.n_heads
+    return es * (nh * g.head_dim * d * 2 + nh * g.d_v * d + d * nh * g.d_v)
+
+
+@dataclass
+class Capacity:
+    per_stream_bytes: int   # all layers' caches + this stream's share of one call's buffers
+    fixed_bytes: int        # all layers' weights
+    max_batch: int
+
+
+def capacity(g, layers: int, budget_bytes: int, dense: bool = False) -> Capacity:
+    """Largest batch whose caches (all layers), one layer's per-call buffers and
+    all weights fit in budget_bytes.  Per-call buffers are linear in the batch
+    except the stream-K partial states, which are charged once."""
+    io = 2 * g.n_q * g.hidden * 2  # x and out of one call, per stream
+    if dense:
+        cache, fixed = dense_cache_bytes(g) * layers, dense_weight_bytes(g) * layers
+        ws1, ws2 = dense_workspace_bytes(g, 1), dense_workspace_bytes(g, 2)
+    else:
+        cache, fixed = latent_cache_bytes(g) * layers, latent_weight_bytes(g) * layers
+        ws1, ws2 = latent_workspace_bytes(g, 1), latent_workspace_bytes(g, 2)
+    slope = ws2 - ws1
+    fixed += ws1 - slope  # the batch-independent part of the workspace
+    per = cache + slope + io
+    return Capacity(per, fixed, max(0, (budget_bytes - fixed) // per))

@@ -77,6 +77,10 @@ template <typename T> struct FlashArgs {
   float* part_ml;           // [2G][kAttnMaxRows][2]
   int len0, len1, tiles0;   // keys per segment, key tiles of segment 0
   int R, RB, KT, S, G;      // rows per stream, row blocks per stream, key tiles, streams, workgroups
+  // Units (stream, row block) 0..dp_units-1 go whole to workgroups round-robin
+  // (unit j*G + w to workgroup w); the rest are split into key-tile pieces
+  // (stream-K).  dp_units is a multiple of G.
+  long dp_units;
   // Block-causal mode (causal_tokens > 0; keys in segment 1 only): row r sees
   // keys [0, (t / causal_tokens + 1) * causal_tokens) with t = r / row_div its
   // token.  One workgroup per row block, longest rows first, no split.
@@ -274,30 +278,39 @@ void flash_attn_kernel(FlashArgs<T> p) {
     const int lim = (r / p.row_div / p.causal_tokens + 1) * p.causal_tokens;
     return lim < p.len1 ? lim : p.len1;
   };
-  const long I = (long)p.S * p.RB * p.KT;
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-  // L2); the virtual index gives the workgroups of one XCD one contiguous share
-  // of the work, so they stream the same streams' keys.
+  // L2); the virtual index gives the workgroups of one XCD consecutive numbers,
+  // so that they work on neighbouring row blocks of the same streams and share
+  // those streams' keys in L2.
   const int vw = p.G % 8 == 0 ? (int)(blockIdx.x % 8) * (p.G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const long it0 = (long)vw * I / p.G, it1 = (long)(vw + 1) * I / p.G;
-
-  // The range covers pieces of consecutive row blocks: the first may start and
-  // the last may end inside a row block.  The last piece (which starts at key
-  // tile 0) is processed first, so every workgroup sweeps the key tiles in
+  // Whole units first: unit j*G + vw in round j, so in every round the
+  // workgroups of one XCD hold consecutive row blocks, mostly of one stream.
+  const int n_whole = causal ? 0 : (int)(p.dp_units / p.G);
+  // Then this workgroup's share [it0, it1) of the key-tile pieces of the
+  // remaining units: pieces of consecutive row blocks, where the first may start
+  // and the last may end inside a row block.  The last piece (which starts at
+  // key tile 0) is processed first, so every workgroup sweeps the key tiles in
   // increasing order from near tile 0 and the workgroups sharing an L2 stay
   // within a few dozen tiles of one another.  Block-causal mode: one whole row
   // block per workgroup, the longest (last) row blocks first.
-  const long u_first = causal ? (long)p.S * p.RB - 1 - blockIdx.x : it0 / p.KT;
-  const int npieces = causal ? 1 : (int)((it1 - 1) / p.KT - u_first + 1);
-  for (int k = 0; k < npieces; ++k) {
-    const int piece = npieces > 1 ? (k == 0 ? npieces - 1 : k - 1) : 0;
-    const long unit = u_first + piece;
+  const long I = ((long)p.S * p.RB - (causal ? 0 : p.dp_units)) * p.KT;
+  const long it0 = (long)vw * I / p.G, it1 = (long)(vw + 1) * I / p.G;
+  const long u_first = causal ? (long)p.S * p.RB - 1 - blockIdx.x : p.dp_units + it0 / p.KT;
+  const int npieces = causal ? 1 : (int)((it1 - 1) / p.KT - it0 / p.KT + 1);
+  for (int job = 0; job < n_whole + npieces; ++job) {
+    const bool whole = job < n_whole;
+    const int k = job - n_whole;
+    const int piece = whole ? 0 : npieces > 1 ? (k == 0 ? npieces - 1 : k - 1) : 0;
+    const long unit = whole ? (long)job * p.G + vw : u_first + piece;
     const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
     int kt0, kt1;
     if (causal) {  // tiles up to the last row's limit; the tiles above the block diagonal are skipped
       const int last_row = min((rb + 1) * (NW * RW), p.R) - 1;
       kt0 = 0;
       kt1 = p.tiles0 + (row_limit(last_row) + KTILE - 1) / KTILE;
+    } else if (whole) {
+      kt0 = 0;
+      kt1 = p.KT;
     } else {
       kt0 = piece == 0 ? (int)(it0 % p.KT) : 0;
       kt1 = piece == npieces - 1 ? (int)((it1 - 1) % p.KT) + 1 : p.KT;
@@ -518,17 +531,18 @@ void flash_attn_kernel(FlashArgs<T> p) {
   }
 }
 
-// Merge the partial states of every row block that was split across workgroups.
-// Workgroups w0..w1 (virtual indices) hold the pieces of row block `unit`;
+// Merge the partial states of every row block that was split across workgroups
+// (units past dp_units).  Workgroups w0..w1 (virtual indices) hold the pieces of
+// row block `unit`;
 // every piece is its workgroup's first (slot 2w) except possibly w0's, which is
 // its second (slot 2w0+1) when w0 started inside an earlier row block.
 template <typename T, int DV, int ROWS>
 __global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
   constexpr int SLICE = 16;  // rows per workgroup: many small workgroups hide load latency
-  const long unit = blockIdx.x / (ROWS / SLICE);
+  const long unit = p.dp_units + blockIdx.x / (ROWS / SLICE);
   const int r0 = (int)(blockIdx.x % (ROWS / SLICE)) * SLICE;
-  const long I = (long)p.S * p.RB * p.KT;
-  const long i0 = unit * p.KT, i1 = i0 + p.KT;
+  const long I = ((long)p.S * p.RB - p.dp_units) * p.KT;
+  const long i0 = (unit - p.dp_units) * p.KT, i1 = i0 + p.KT;
   auto start = [&](long w) { return w * I / p.G; };
   long w0 = i0 * p.G / I;
   while (w0 + 1 < p.G && start(w0 + 1) <= i0) ++w0;
@@ -569,9 +583,13 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   a.RB = (a.R + ROWS - 1) / ROWS;
   a.tiles0 = (a.len0 + KTILE - 1) / KTILE;
   a.KT = a.tiles0 + (a.len1 + KTILE - 1) / KTILE;
-  const long I = (long)a.S * a.RB * a.KT;
+  const long U = (long)a.S * a.RB;
   const bool causal = a.causal_tokens > 0;
-  a.G = causal ? a.S * a.RB : (int)(G < I ? G : I);  // block-causal: one workgroup per row block
+  a.G = causal ? (int)U : (int)(G < U * a.KT ? G : U * a.KT);  // block-causal: one workgroup per row block
+  // With at least two units per workgroup, all but the last one to two rounds
+  // of units go whole (no partial states, no combine); stream-K balances the rest.
+  a.dp_units = !causal && U >= 2L * a.G ? (U / a.G - 1) * a.G : 0;
+  const long I = (U - a.dp_units) * a.KT;
   if (a.row_div <= 0) a.row_div = 1;
   if constexpr (!VROWS) latent_value_tiles<T, D, DV, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
   hipError_t err;
@@ -579,7 +597,7 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS><<<a.G, NW * 64, 0, s>>>(a);
   if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
   if (!causal && I != (long)a.G * a.KT)
-    flash_attn_combine<T, DV, ROWS><<<a.S * a.RB * (ROWS / 16), 256, 0, s>>>(a);
+    flash_attn_combine<T, DV, ROWS><<<(U - a.dp_units) * (ROWS / 16), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -136,7 +136,10 @@ hipError_t run_expand(const Plan& p, const DensePlan& ex, void* wext_buf, int64_
       wext, static_cast<const bf16*>(p.w_uk), p.nh, p.d_nope, p.dc, p.dr);
   const int n_ring = (int)(cached_frames(p, n) * p.Tpf);
   // rope_at_use: up-project the window with k^ rotated at local coordinates
-  if (p.rope_at_use) run_assemble(p, n, s);
+  if (p.rope_at_use) {
+    const hipError_t err = run_assemble(p, n, s);
+    if (err != hipSuccess) return err;
+  }
   up_project(p, ex, wext, p.rope_at_use ? p.assembled : p.cache, (long)(p.S + p.W) * p.Tpf * p.D, n_ring,
              static_cast<bf16*>(ex.kring), static_cast<f16*>(ex.vring), ex.ring_stride, s);
   return hipGetLastError();

@@ -245,3 +245,33 @@ def test_sink_config_rules():
         assert vmla.vmla_cache_state(ctx) == (0, 0, 0)
     finally:
         vmla.vmla_destroy(ctx)
+
+
+# ----------------------------------------------------------------------------- capacity arithmetic
+def test_capacity_formulas_match_the_library():
+    from mla_latent_kv_vmla_amd import capacity as cap
+    cases = [(wl.WAN_LAYER, 64), (wl.WAN_SINK, 64), (wl.STRESS[96], 64), (wl.STRESS[192], 64), (wl.STRESS[448], 32),
+             (wl.WAN_SMALL_GRID, 64)]
+    for g, kt in cases:
+        assert cap.latent_cache_bytes(g, g.batch) == vmla.vmla_cache_bytes(_cfg(g)), g.name
+        assert cap.latent_workspace_bytes(g, g.batch, key_tile=kt) == vmla.vmla_workspace_bytes(_cfg(g)), g.name
+    for g in (wl.WAN_DENSE, wl.WAN_DENSE_SMALL_GRID):
+        assert cap.dense_cache_bytes(g, g.batch) == vmla.vmla_dense_cache_bytes(_cfg(g))
+        assert cap.dense_workspace_bytes(g, g.batch) == vmla.vmla_dense_workspace_bytes(_cfg(g))
+
+
+def test_capacity_sweep_orders_as_the_cache_sizes():
+    from mla_latent_kv_vmla_amd import capacity as cap
+    budget = 288 * 10**9
+    dense = cap.capacity(wl.WAN_DENSE, 30, budget, dense=True)
+    prev = None
+    for dc in (64, 128, 192, 256, 512):
+        c = cap.capacity(wl.WAN_LAYER.replace(d_c=dc), 30, budget)
+        assert c.max_batch > dense.max_batch
+        if prev is not None:
+            assert c.max_batch <= prev
+        prev = c.max_batch
+        assert (c.max_batch + 1) * c.per_stream_bytes + c.fixed_bytes > budget >= c.max_batch * c.per_stream_bytes + c.fixed_bytes
+    # the latent caches alone are 224 / 3,072 of the dense ones at d_c = 192
+    assert cap.latent_cache_bytes(wl.WAN_LAYER) * 3072 == pytest.approx(
+        cap.dense_cache_bytes(wl.WAN_DENSE) * 224, rel=1e-3)  # dense rows padded to 128 keys
