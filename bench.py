@@ -336,6 +336,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    traffic = traffic_from_counters(g) if args.path == "absorbed" else None
     res = {
         "metric": METRIC,
         "value": value,
@@ -359,7 +360,10 @@ def main():
                    "attends_per_step": args.steps_per_chunk, "appends_per_step": 1,
                    "expands_per_step": 1 if args.path == "expanded" else 0, "sink_frames": g.sink_frames},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_from_counters(g) if args.path == "absorbed" else None,
+                     "frac": achieved / peak, "traffic": traffic,
+                     # counter bytes over the live launch time, against the 8 TB/s HBM peak
+                     "hbm_gb_per_s": traffic / (attn_avg * 1e-3) / 1e9 if traffic else None,
+                     "hbm_frac": traffic / (attn_avg * 1e-3) / 1e9 / PEAK_HBM_GBS if traffic else None,
                      "kernel": kernel,
                      "flops_per_launch": flops_attn, "avg_launch_ms": attn_avg},
         "attend_call_tflops": call_flops * args.steps_per_chunk / (ms_per_step * 1e-3) / 1e12,
