@@ -36,8 +36,12 @@ def _rotate(vec, coord, pairs, theta):
     return out
 
 
-def attend(g, wts, history, n, chunk_x):
-    """u for every query token of the chunk, as nested lists [C*T][hidden]."""
+def attend(g, wts, history, n, chunk_x, key_order=None):
+    """u for every query token of the chunk, as nested lists [C*T][hidden].
+
+    key_order: optional permutation (indices into the visible keys in context
+    order) in which the keys, each with its own position, are processed; softmax
+    attention does not depend on it (e.g. a ring cache's slot order)."""
     T = g.grid_h * g.grid_w
     W, C = g.window_frames, g.chunk_frames
     tolist = lambda a: [[float(v) for v in row] for row in a]
@@ -52,6 +56,10 @@ def attend(g, wts, history, n, chunk_x):
             keys_x.append(rows[s])
             keys_pos.append((tau, s // g.grid_w, s % g.grid_w))
     n_cached = len(frames) - C
+    if key_order is not None:
+        assert sorted(key_order) == list(range(len(keys_x))), "key_order must be a permutation"
+        keys_x = [keys_x[j] for j in key_order]
+        keys_pos = [keys_pos[j] for j in key_order]
     w_dkv, w_kr, w_dq, w_uq, w_o = (tolist(getattr(wts, k)) for k in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_o"))
     w_uk = [tolist(m) for m in wts.w_uk]
     w_uv = [tolist(m) for m in wts.w_uv]

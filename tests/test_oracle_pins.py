@@ -248,6 +248,29 @@ def test_single_key_returns_its_value():
     np.testing.assert_allclose(u, o @ w.w_o.T, rtol=1e-12)
 
 
+def test_key_order_does_not_matter():
+    """Softmax attention is invariant under a joint permutation of the keys (each
+    key keeps its own position), which is why a ring cache may hold the window in
+    slot order.  The brute force processed in ring-slot order and in a random order
+    matches the oracle's context order.  Negative control: moving keys to other
+    positions (the two cached frames' contents swapped) does change the output."""
+    g, n = wl.TINY, 5                       # W = 2, C = 1: frames 3, 4 cached, 4 in slot 0 (wrapped)
+    w, hist, chunk = _tiny_inputs(n, "sharp")
+    u = mla.attend(g, w, hist, n, chunk)
+    T = g.grid_h * g.grid_w
+    cached = [3, 4]
+    slot_of = {f: f % g.window_frames for f in cached}
+    ring_order = [cached.index(f) * T + s for f in sorted(cached, key=lambda f: slot_of[f]) for s in range(T)]
+    ring_order += [len(cached) * T + s for s in range(g.n_q)]
+    assert ring_order[:T] == list(range(T, 2 * T))   # the newer frame comes first in slot order
+    for order in (ring_order, list(np.random.default_rng(3).permutation(len(ring_order)))):
+        ub = np.array(brute.attend(g, w, hist, n, chunk, key_order=[int(j) for j in order]))
+        np.testing.assert_allclose(ub, u, rtol=1e-11, atol=1e-14)
+    swapped = dict(hist)
+    swapped[3], swapped[4] = hist[4], hist[3]
+    assert np.abs(mla.attend(g, w, swapped, n, chunk) - u).max() > 1e-3 * np.abs(u).max()
+
+
 def test_window_excludes_evicted_frames():
     g, n = wl.TINY, 5
     w, hist, chunk = _tiny_inputs(n, "sharp")
