@@ -8,6 +8,9 @@ followed by one vmla_compress_append that writes the chunk into the
 21-frame ring and evicts the oldest frames.  The window is full (32,760 cached
 keys + 4,680 chunk keys) for every timed step.  Inputs are seeded synthetic
 tensors already resident in HBM; weights are random N(0,1)/sqrt(fan_in).
+With the 30-layer rollout workload a step is that chunk for every layer in turn
+(each with its own weights, ring and inputs), so the layers' caches (440 MB)
+cycle through the GPU's last-level cache as they do in a rollout.
 
 Prints one JSON line.  `value` = query tokens attended per second.
 `roofline` describes the dominant kernel (latent attention) timed live with
@@ -104,17 +107,22 @@ def pmc_summary_path(g) -> str:
     return os.path.join(ROOT, "profiles", f"flash_attn_{g.name}_pmc.json")
 
 
-def traffic_from_counters(g):
-    """HBM bytes per launch of the attention kernel from the committed rocprofv3
-    counter summary of this workload, if it was taken on the current kernel source."""
+def counter_summary(g) -> dict:
+    """The committed rocprofv3 counter summary of this workload's attention kernel,
+    if it was taken on the current kernel source (else empty)."""
     try:
         s = json.load(open(pmc_summary_path(g)))
         sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
         if s.get("attention_source_sha256") == sha:
-            return s.get("hbm_bytes_per_launch")
+            return s
     except (OSError, ValueError):
         pass
-    return None
+    return {}
+
+
+def traffic_from_counters(g):
+    """HBM bytes per launch of the attention kernel (calibrated FETCH_SIZE + WRITE_SIZE)."""
+    return counter_summary(g).get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(g, w, hist, n, x, sample_tokens: int):
@@ -248,6 +256,11 @@ def main():
     else:
         w = wl.latent_weights(g, mode="literal")
         layer = vmla.LatentAttention(g, {k: torch.from_numpy(v) for k, v in w.as_dict().items()})
+        # a multi-layer geometry (the streaming rollout) runs every layer per step, each
+        # with its own seeded weights, ring cache and inputs
+        extra_layers = [vmla.LatentAttention(g, {k: torch.from_numpy(v) for k, v in
+                                                 wl.latent_weights(g, layer=l, mode="literal").as_dict().items()})
+                        for l in range(1, g.layers if args.path == "absorbed" else 1)]
         attend_profiled, append = vmla.vmla_attend_profiled, vmla.vmla_compress_append
         kernel = "flash_attn_kernel (latent, absorbed)"
         if args.path == "clip":
@@ -258,15 +271,24 @@ def main():
             attend_profiled = lambda ctx, x, o, a, b, st: vmla.vmla_attend_expanded_profiled(ctx, expanded, x, o, a,
                                                                                             b, st)
             kernel = "flash_attn_kernel (latent window expanded to per-head K/V)"
+    if is_dense(g):
+        extra_layers = []
+    layers = [layer] + extra_layers
     hist = {}
-    for k in range(g.prefill_chunks):
+    # the window is full for every timed step: geometries without a prefill get one window's worth
+    prefill_chunks = g.prefill_chunks or -(-g.window_frames // g.chunk_frames)
+    for k in range(prefill_chunks):
         xk = wl.hidden_states(g, chunk=k)
-        layer.append(torch.from_numpy(xk).to(dev, dt))
+        xkd = torch.from_numpy(xk).to(dev, dt)
+        for l, lay in enumerate(layers):  # layer l's hidden states: layer 0's rolled by 37 l tokens
+            lay.append(torch.roll(xkd, shifts=37 * l, dims=1).contiguous() if l else xkd)
         for i in range(g.chunk_frames):
             hist[k * g.chunk_frames + i] = xk[0].reshape(g.chunk_frames, g.tokens_per_frame, g.hidden)[i]
     n_prefill = layer.state()[0]
-    xs_np = [wl.hidden_states(g, chunk=g.prefill_chunks, step=s) for s in range(args.steps_per_chunk)]
+    xs_np = [wl.hidden_states(g, chunk=prefill_chunks, step=s) for s in range(args.steps_per_chunk)]
     xs = [torch.from_numpy(a).to(dev, dt) for a in xs_np]
+    xs_layers = [xs] + [[torch.roll(x, shifts=37 * l, dims=1).contiguous() for x in xs]
+                        for l in range(1, len(layers))]
     out = torch.empty_like(xs[0])
     if args.path == "clip":  # one whole window-length clip per step, no cache
         if is_dense(g):
@@ -280,7 +302,8 @@ def main():
     sh = stream.cuda_stream
 
     ev = HipEvents()
-    n_att = (args.warmup + args.steps) * args.steps_per_chunk
+    L = len(layers)
+    n_att = (args.warmup + args.steps) * args.steps_per_chunk * L
     ev_pairs = [(ev.create(), ev.create()) for _ in range(n_att)]
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.warmup + args.steps)]
@@ -292,10 +315,12 @@ def main():
             return
         if args.path == "expanded" and not is_dense(g):
             vmla.vmla_expand(layer.ctx, expanded, sh)  # once per chunk: the frozen window's per-head K/V
-        for s in range(args.steps_per_chunk):
-            a, b = ev_pairs[i * args.steps_per_chunk + s]
-            attend_profiled(layer.ctx, xs[s], out, a, b, sh)
-        append(layer.ctx, xs[-1], sh)
+        for l, lay in enumerate(layers):
+            xl = xs_layers[l]
+            for s in range(args.steps_per_chunk):
+                a, b = ev_pairs[(i * L + l) * args.steps_per_chunk + s]
+                attend_profiled(lay.ctx, xl[s], out, a, b, sh)
+            append(lay.ctx, xl[-1], sh)
 
     for i in range(args.warmup):
         step(i)
@@ -314,7 +339,7 @@ def main():
     ms_region = region0.elapsed_time(region1)
     ms_per_step = ms_region / args.steps
 
-    attn_ms = [ev.elapsed_ms(a, b) for a, b in ev_pairs[args.warmup * args.steps_per_chunk:]]
+    attn_ms = [ev.elapsed_ms(a, b) for a, b in ev_pairs[args.warmup * args.steps_per_chunk * L:]]
     attn_avg = float(np.mean(attn_ms))
     n_frames = layer.state()[0]  # frames appended; n_k counts the visible ones (sinks + window)
     flops_attn = (clip_attention_flops(g) if args.path == "clip"
@@ -322,7 +347,7 @@ def main():
     achieved = flops_attn / (attn_avg * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if g.dtype == wl.F32 else PEAK_BF16_TFLOPS
     tokens_per_step = (g.batch * g.window_frames * g.tokens_per_frame if args.path == "clip"
-                       else g.batch * g.n_q * args.steps_per_chunk)
+                       else g.batch * g.n_q * args.steps_per_chunk * L)
     value = tokens_per_step / (ms_per_step * 1e-3)
     call_flops = attend_call_flops(g, n_frames, expanded=args.path == "expanded")
     if args.path == "clip":
@@ -357,7 +382,7 @@ def main():
                    "heads": g.n_heads, "head_dim": g.head_dim,
                    "d_c": g.d_c, "d_rope": g.d_rope,
                    "window_frames": g.window_frames, "chunk_frames": g.chunk_frames,
-                   "attends_per_step": args.steps_per_chunk, "appends_per_step": 1,
+                   "layers": L, "attends_per_step": args.steps_per_chunk * L, "appends_per_step": L,
                    "expands_per_step": 1 if args.path == "expanded" else 0, "sink_frames": g.sink_frames},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
@@ -365,16 +390,21 @@ def main():
                      "hbm_gb_per_s": traffic / (attn_avg * 1e-3) / 1e9 if traffic else None,
                      "hbm_frac": traffic / (attn_avg * 1e-3) / 1e9 / PEAK_HBM_GBS if traffic else None,
                      "kernel": kernel,
-                     "flops_per_launch": flops_attn, "avg_launch_ms": attn_avg},
+                     "flops_per_launch": flops_attn, "avg_launch_ms": attn_avg,
+                     # MFMA work the counters saw (padding included) and the matrix cores' busy share
+                     "mfma_counter_flops_per_launch": (counter_summary(g).get("mfma_flops_per_launch")
+                                                       if args.path == "absorbed" else None),
+                     "mfma_busy_frac": counter_summary(g).get("mfma_busy_frac") if args.path == "absorbed" else None},
         "attend_call_tflops": call_flops * args.steps_per_chunk / (ms_per_step * 1e-3) / 1e12,
         "wall_s_timed_region": wall,
     }
-    if not args.no_cpu_baseline and args.path != "clip":
+    if not args.no_cpu_baseline and args.path != "clip" and L == 1:
         res["cpu_baseline"] = cpu_baseline(g, w, hist, n_prefill, xs_np[0][0], args.cpu_sample_tokens or g.n_q)
     for a, b in ev_pairs:
         ev.destroy(a)
         ev.destroy(b)
-    layer.close()
+    for lay in layers:
+        lay.close()
     print(json.dumps(res), flush=True)
 
 
