@@ -20,17 +20,21 @@ template <typename T> struct GemmOps {
   int N, M, K, n_split;
 };
 
-constexpr int GEMM_BK = 32;
+#ifndef VMLA_GEMM_BK
+#define VMLA_GEMM_BK 64
+#endif
+constexpr int GEMM_BK = VMLA_GEMM_BK;  // k-values per pipeline stage (16-bit storage)
 
 template <typename T, int BN, int BM, bool W_KN, class Epi>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
   using MF = Mfma<T>;
+  constexpr int BK = sizeof(T) == 2 ? GEMM_BK : 32;  // fp32 tiles keep 32 (LDS)
   constexpr int KPL = MF::KPL;
   constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int STRIDE = GEMM_BK + VEC;          // LDS row: 32 k-values + 16 B pad
+  constexpr int STRIDE = BK + VEC;          // LDS row: BK k-values + 16 B pad
   constexpr int FN = BN / 64, FM = BM / 64;      // 32x32 tiles per wave (2x2 waves)
-  constexpr int WV = BN * GEMM_BK / VEC / 256;   // 16-B vectors per thread, W tile
-  constexpr int XV = BM * GEMM_BK / VEC / 256;
+  constexpr int WV = BN * BK / VEC / 256;   // 16-B vectors per thread, W tile
+  constexpr int XV = BM * BK / VEC / 256;
   static_assert(FN >= 1 && FM >= 1 && WV >= 1 && XV >= 1, "tile too small");
 
   __shared__ __attribute__((aligned(16))) T Ws[2][BN * STRIDE];
@@ -52,7 +56,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
       int v = tid + i * 256;
       u32x4 val = {0, 0, 0, 0};
       if constexpr (!W_KN) {
-        int row = v / (GEMM_BK / VEC), cv = v % (GEMM_BK / VEC);
+        int row = v / (BK / VEC), cv = v % (BK / VEC);
         int n = n0 + row, k = k0 + cv * VEC;
         if (n < op.N && k < op.K) {
           const T* src = n < op.n_split ? wbase + (long)n * op.ldw : wbase2 + (long)(n - op.n_split) * op.ldw;
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
       int v = tid + i * 256;
-      int row = v / (GEMM_BK / VEC), cv = v % (GEMM_BK / VEC);
+      int row = v / (BK / VEC), cv = v % (BK / VEC);
       int m = m0 + row, k = k0 + cv * VEC;
       u32x4 val = {0, 0, 0, 0};
       if (m < op.M && k < op.K) val = ld16(xbase + (long)m * op.ldx + k);
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
     for (int i = 0; i < WV; ++i) {
       int v = tid + i * 256;
       if constexpr (!W_KN) {
-        int row = v / (GEMM_BK / VEC), cv = v % (GEMM_BK / VEC);
+        int row = v / (BK / VEC), cv = v % (BK / VEC);
         *reinterpret_cast<u32x4*>(&Ws[buf][row * STRIDE + cv * VEC]) = wr[i];
       } else {
         int krow = v / (BN / VEC), nv = v % (BN / VEC);
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
       int v = tid + i * 256;
-      int row = v / (GEMM_BK / VEC), cv = v % (GEMM_BK / VEC);
+      int row = v / (BK / VEC), cv = v % (BK / VEC);
       *reinterpret_cast<u32x4*>(&Xs[buf][row * STRIDE + cv * VEC]) = xr[i];
     }
   };
@@ -104,15 +108,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
 
-  const int KT = (op.K + GEMM_BK - 1) / GEMM_BK;
+  const int KT = (op.K + BK - 1) / BK;
   load_tiles(0);
   store_tiles(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) load_tiles((kt + 1) * GEMM_BK);
+    if (kt + 1 < KT) load_tiles((kt + 1) * BK);
 #pragma unroll
-    for (int ks = 0; ks < GEMM_BK / (2 * KPL); ++ks) {
+    for (int ks = 0; ks < BK / (2 * KPL); ++ks) {
       typename MF::Frag a[FN], b[FM];
       const int koff = ks * 2 * KPL + KPL * h32;
 #pragma unroll
