@@ -79,7 +79,9 @@ enum { VMLA_DTYPE_BF16 = 0, VMLA_DTYPE_F32 = 1 };
  *     invariance); sink_frames > 0 requires rope_at_use = 1.
  * Constraints (else VMLA_ERR_CONFIG): all sizes > 0 (sink_frames >= 0);
  *   1 <= chunk_frames <= window_frames; d_nope, d_rope, d_c, d_v, d_q and hidden
- *   multiples of 8; rope_theta > 0; rope_at_use in {0, 1}.
+ *   multiples of 8; rope_theta > 0; rope_at_use in {0, 1}; batch <= 65,535 and
+ *   batch * chunk_frames * grid_h * grid_w <= 64 * 65,535 query tokens per call
+ *   (launch-grid limits).
  * Built kernels (else VMLA_ERR_UNSUPPORTED): (dtype, d_c, d_rope) in
  *   {(f32, 24, 8), (bf16, 24, 8), (bf16, 96, 32), (bf16, 192, 32), (bf16, 448, 32)}.
  */
@@ -189,7 +191,9 @@ VMLA_API void vmla_destroy(vmla_ctx* ctx);
  * are the clip's frame indices 0..window_frames-1.  Key tiles above the block
  * diagonal are skipped.
  * vmla_clip_workspace_bytes: bytes of the caller-owned clip workspace (the
- *   per-call buffers of vmla_attend sized for window_frames*T query tokens).
+ *   per-call buffers of vmla_attend sized for window_frames*T query tokens);
+ *   0 if the config is invalid or batch * window_frames * T exceeds 64 * 65,535
+ *   (launch-grid limit; vmla_attend_clip then returns VMLA_ERR_CONFIG).
  * vmla_attend_clip: x and out are [batch, window_frames*T, hidden]; same rules
  *   as vmla_attend (window_frames must be a multiple of chunk_frames for whole
  *   blocks; a shorter last block is allowed).

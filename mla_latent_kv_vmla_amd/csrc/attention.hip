@@ -22,8 +22,10 @@
 //
 // Staging.  A key tile lives in LDS twice: row-major [key][D] (storage type) for
 // the score product, and transposed [channel][key] for the value product.  Both
-// are copied with LDS-DMA loads (global_load_lds_dwordx4: lane L's 16 bytes land
-// at M0 + 16 L), so staging needs no registers and no VALU.  The transposed tile
+// are copied with LDS-DMA loads through a buffer resource (buffer_load_dwordx4
+// ... lds: lane L's 16 bytes land at M0 + 16 L), so staging needs no registers
+// and no VALU, and the resource's range check reads rows past a segment's end as
+// zero.  The transposed tile
 // comes either from images a pre-pass builds once per call in the workspace,
 // already in LDS layout (latent: the value is the key's first DV channels), or
 // straight from value rows [f][key] that the dense cache stores transposed.
@@ -43,13 +45,17 @@
 // where bf16's spacing (2^-8) exceeds the spread of the probabilities
 // themselves; fp16's spacing there is 2^-11, at the same MFMA rate.
 //
-// Scheduling is stream-K over (stream, row block, key tile): workgroup w owns
-// iterations [w*I/G, (w+1)*I/G).  A row block finished by one workgroup is
-// written directly; a row block split across workgroups leaves unnormalised
-// partial states (at most two per workgroup) that the combine kernel merges
-// with the usual log-sum-exp rule.  Scores are in log2 units (log2(e) is
-// folded into the query), and the running maximum is only moved when a block
-// exceeds it by more than 2^8, which keeps rescaling of the accumulator rare.
+// Scheduling.  G persistent workgroups.  With at least two (stream, row block)
+// units per workgroup, whole units go round-robin first; the remaining units
+// are split stream-K over their key tiles: workgroup w owns pieces
+// [w*I/G, (w+1)*I/G).  A row block finished by one workgroup is written
+// directly; a row block split across workgroups leaves unnormalised partial
+// states (at most two per workgroup) that the combine kernel merges with the
+// usual log-sum-exp rule.  Block-causal mode (a whole clip) runs one workgroup
+// per row block and skips the key tiles above its diagonal.  Scores are in log2
+// units (log2(e) is folded into the query), and the running maximum is only
+// moved when a block exceeds it by more than 8 (a factor 2^8), which keeps
+// rescaling of the accumulator rare.
 #include <type_traits>
 
 #include "device_common.h"

@@ -44,6 +44,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elem_bytes(const vmla_config* c) { return c->dtype == VMLA_DTYPE_F32 ? 4 : 2; }
 
+constexpr long long kMaxGridY = 65535;  // launch-grid limit along y
+
 // Checks common to both layer types.
 int check_common(const vmla_config* c) {
   if (c->batch <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->d_rope <= 0 || c->d_v <= 0 ||
@@ -65,6 +67,9 @@ int check_common(const vmla_config* c) {
   const long long T = (long long)c->grid_h * c->grid_w;
   const long long rows = T * ((long long)c->sink_frames + c->window_frames) + T * c->chunk_frames;
   if (rows * c->n_heads > (1LL << 30) || (long long)c->batch * T * c->chunk_frames > (1LL << 30))
+    return VMLA_ERR_CONFIG;
+  // launch grids: streams and 64-token GEMM tiles of one call along grid y (at most 65,535)
+  if (c->batch > kMaxGridY || (long long)c->batch * T * c->chunk_frames > 64LL * kMaxGridY)
     return VMLA_ERR_CONFIG;
   return VMLA_OK;
 }
@@ -394,13 +399,20 @@ static Plan clip_geometry(const vmla_config* cfg) {
   return p;
 }
 
+// A clip call runs window_frames*T query tokens per stream: the same launch-grid
+// limit as a chunk call, for that token count.
+static bool clip_fits(const vmla_config* cfg) {
+  return (long long)cfg->batch * cfg->window_frames * cfg->grid_h * cfg->grid_w <= 64LL * kMaxGridY;
+}
+
 VMLA_API size_t vmla_clip_workspace_bytes(const vmla_config* cfg) {
-  if (check_config(cfg) != VMLA_OK) return 0;
+  if (check_config(cfg) != VMLA_OK || !clip_fits(cfg)) return 0;
   return vmla::workspace_layout(clip_geometry(cfg)).total;
 }
 
 static int attend_clip(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out, hipEvent_t e0, hipEvent_t e1,
                        hipStream_t stream) {
+  if (!clip_fits(&ctx->cfg)) return VMLA_ERR_CONFIG;
   if (!aligned16(x) || !aligned16(clip_workspace) || !aligned16(out)) return VMLA_ERR_ALIGN;
   Plan p = clip_geometry(&ctx->cfg);
   for (int i = 0; i < vmla::kMaxRopePairs; ++i) p.freq[i] = ctx->freq[i];

@@ -65,13 +65,31 @@ def test_cache_and_workspace_bytes():
     assert vmla.vmla_cache_bytes(_cfg(b4)) == 4 * 42 * 1560 * 224 * 2
 
 
-@pytest.mark.parametrize("field,value,code", [
+PARAMS_INVALID = [
     ("batch", 0, "VMLA_ERR_CONFIG"), ("hidden", 12, "VMLA_ERR_CONFIG"), ("d_nope", 0, "VMLA_ERR_CONFIG"),
     ("chunk_frames", 22, "VMLA_ERR_CONFIG"), ("rope_pairs_t", 5, "VMLA_ERR_CONFIG"),
     ("rope_theta", 0.0, "VMLA_ERR_CONFIG"), ("dtype", 7, "VMLA_ERR_CONFIG"), ("grid_w", 0, "VMLA_ERR_CONFIG"),
     ("attn_workgroups", -1, "VMLA_ERR_CONFIG"),
     ("d_c", 200, "VMLA_ERR_UNSUPPORTED"), ("dtype", vmla.VMLA_DTYPE_F32, "VMLA_ERR_UNSUPPORTED"),
-])
+]
+
+
+def test_launch_grid_limits():
+    """Streams and 64-token GEMM tiles of one call run along grid y (at most
+    65,535): the Wan layer accepts 896 streams (4,193,280 query tokens) and
+    rejects 897; a tiny frame caps the batch itself at 65,535."""
+    assert vmla.vmla_cache_bytes(_cfg(batch=896)) > 0
+    assert vmla.vmla_cache_bytes(_cfg(batch=897)) == 0
+    assert vmla.vmla_dense_cache_bytes(vmla.config_from_geometry(wl.WAN_DENSE.replace(batch=897))) == 0
+    # a whole-clip call runs window_frames * T = 32,760 tokens per Wan stream: at most 128 streams
+    assert vmla.vmla_clip_workspace_bytes(_cfg(batch=128)) > 0
+    assert vmla.vmla_clip_workspace_bytes(_cfg(batch=129)) == 0
+    tiny = wl.TINY.replace(dtype=wl.BF16)
+    assert vmla.vmla_cache_bytes(vmla.config_from_geometry(tiny.replace(batch=65535))) > 0
+    assert vmla.vmla_cache_bytes(vmla.config_from_geometry(tiny.replace(batch=65536))) == 0
+
+
+@pytest.mark.parametrize("field,value,code", PARAMS_INVALID)
 def test_invalid_configs_rejected(field, value, code):
     c = _cfg(**{field: value})
     assert vmla.vmla_cache_bytes(c) == 0 and vmla.vmla_workspace_bytes(c) == 0
