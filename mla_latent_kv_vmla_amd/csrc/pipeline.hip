@@ -1,10 +1,14 @@
 // Launch sequences of the two library calls and the GEMM epilogues they use.
 //
 //   compress (VideoMLA paper, sections 3.1-3.2): one GEMM x . [W_DKV; W_KR]^T whose
-//     epilogue rotates the decoupled key channels by 3D-RoPE, rounds to the
-//     storage type and scatters each token's row to its ring slot
-//     ((frame % W) * T + s) or to a linear buffer.
-//   attend: compress the chunk into staging; c^Q = W_DQ x; q = W_UQ c^Q with the
+//     epilogue rotates the decoupled key channels by 3D-RoPE at the absolute
+//     frame (ring rows with rope_at_use stay un-rotated), rounds to the storage
+//     type and scatters each token's row to its ring slot (slot * T + s; frames
+//     f < S take sink slot f, later ones slot S + (f - S) % W) or to a linear
+//     buffer.
+//   attend: compress the chunk into staging; with rope_at_use, rotate the
+//     visible ring rows at their window-local coordinates into the workspace
+//     (assemble_window); c^Q = W_DQ x; q = W_UQ c^Q with the
 //     rotary channels turned and scaled straight into the absorbed query;
 //     absorbed query q~_h = W_UK^h^T q_nope_h (per-head GEMM on MFMA);
 //     latent attention (attention.hip); o_h = W_UV^h o~_h; out = W_O o.
