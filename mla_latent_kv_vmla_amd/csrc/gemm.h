@@ -23,12 +23,18 @@ template <typename T> struct GemmOps {
 #ifndef VMLA_GEMM_BK
 #define VMLA_GEMM_BK 64
 #endif
+#ifndef VMLA_GEMM_BK_SMALL
+#define VMLA_GEMM_BK_SMALL 128
+#endif
 constexpr int GEMM_BK = VMLA_GEMM_BK;  // k-values per pipeline stage (16-bit storage)
 
 template <typename T, int BN, int BM, bool W_KN, class Epi>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
   using MF = Mfma<T>;
-  constexpr int BK = sizeof(T) == 2 ? GEMM_BK : 32;  // fp32 tiles keep 32 (LDS)
+  // k-values per stage: deeper stages halve the global-load round trips of
+  // these latency-bound GEMMs; 64x64 tiles afford 128 (~70 KB of LDS), larger
+  // tiles 64 (two workgroups per CU); fp32 tiles keep 32 (LDS)
+  constexpr int BK = sizeof(T) != 2 ? 32 : (BN == 64 && BM == 64 ? VMLA_GEMM_BK_SMALL : GEMM_BK);
   constexpr int KPL = MF::KPL;
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int STRIDE = BK + VEC;          // LDS row: BK k-values + 16 B pad
