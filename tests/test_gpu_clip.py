@@ -2,7 +2,7 @@
 oracle's attend_clip: chunk q of the clip attends to chunks 0..q (the
 training-time form of the layer).  Cases: the tiny fp32 layer, the Wan widths
 on a 6x10 grid with a 5-frame clip in 3-frame chunks (a shorter last block,
-row blocks straddling block boundaries), and the full 21-frame Wan clip
+row blocks straddling block boundaries; d_c = 192, 96 and 448), and the full 21-frame Wan clip
 (32,760 tokens, 7 blocks) on sampled queries of three blocks.  Same bar as the
 other GPU tests (gpu_harness)."""
 import numpy as np
@@ -19,8 +19,11 @@ def _clip_x(g, mode, seed=0):
     return wl.hidden_states(g.replace(chunk_frames=g.window_frames), chunk=500, mode=mode, seed=seed)
 
 
-@pytest.mark.parametrize("g,mode", [(wl.TINY, "sharp"), (wl.WAN_SMALL_GRID, "literal"), (wl.WAN_SMALL_GRID, "sharp")],
-                         ids=["tiny-sharp", "grid6x10-literal", "grid6x10-sharp"])
+@pytest.mark.parametrize("g,mode", [(wl.TINY, "sharp"), (wl.WAN_SMALL_GRID, "literal"), (wl.WAN_SMALL_GRID, "sharp"),
+                                    (wl.WAN_SMALL_GRID.replace(name="wan-widths-grid6x10-dc96", d_c=96), "sharp"),
+                                    (wl.WAN_SMALL_GRID.replace(name="wan-widths-grid6x10-dc448", d_c=448), "sharp")],
+                         ids=["tiny-sharp", "grid6x10-literal", "grid6x10-sharp", "grid6x10-dc96-sharp",
+                              "grid6x10-dc448-sharp"])
 def test_clip_matches_oracle(g, mode):
     print("case: clip", g.name, mode, flush=True)
     r = Rollout(g, mode=mode, cache_fill=float("nan"))

@@ -6,8 +6,8 @@ window, per-head queries, dense flash kernel); the absorbed path (vmla_attend)
 is the same function up to rounding.  Same bar and tolerance derivation as the
 other GPU tests (gpu_harness).  Cases: Wan widths on a 6x10 grid over empty,
 partial, full and wrapped windows with NaN canaries in unused cache slots, three
-input scalings, stream-K cuts, batched streams, the stale-expansion guard, and
-the full Wan-1.3B layer on sampled queries.
+input scalings, stream-K cuts, d_c = 96 and 448, batched streams, the
+stale-expansion guard, and the full Wan-1.3B layer on sampled queries.
 """
 import numpy as np
 import pytest
@@ -48,6 +48,12 @@ def test_expanded_small_grid_all_window_states(mode):
 @pytest.mark.parametrize("G", [1, 7, 100000])
 def test_expanded_stream_k_splits(G):
     _expanded_rollout(SMALL, "sharp", n_chunks=3, attn_workgroups=G)
+
+
+@pytest.mark.parametrize("dc", [96, 448])
+def test_expanded_other_latent_widths(dc):
+    # the up-projection (key lift with its identity block, value GEMM) at the other built widths
+    _expanded_rollout(SMALL.replace(name=f"wan-widths-grid6x10-dc{dc}", d_c=dc), "sharp", n_chunks=3)
 
 
 def test_expanded_batched_streams():

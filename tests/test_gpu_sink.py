@@ -5,8 +5,8 @@ window and rotates every visible key, and the chunk's queries, at local
 temporal coordinates (appendix D.4, D.5).  The oracle implements exactly that
 (its pins include brute force and independence from absolute time).  Cases:
 ring placement with the sink pinned (c bit-exact, k_r stored un-rotated),
-attention at every window state (fp32 and bf16, three scalings), rotation at
-use without a sink, the expanded path with a sink, and the full-size
+attention at every window state (fp32 and bf16, three scalings; d_c = 192,
+96 and 448), rotation at use without a sink, the expanded path with a sink, and the full-size
 sink + 6-frame Wan layer.  Same bar and tolerance derivation as gpu_harness.
 """
 import numpy as np
@@ -86,6 +86,12 @@ def test_sink_tiny_all_window_states(g):
 @pytest.mark.parametrize("mode", ["literal", "unit", "sharp"])
 def test_sink_wan_widths_small_grid(mode):
     _rollout(SMALL_SINK, [mode], n_chunks=5)
+
+
+@pytest.mark.parametrize("dc", [96, 448])
+def test_sink_other_latent_widths(dc):
+    # the assembly pass and rotation at use with the other built latent widths
+    _rollout(SMALL_SINK.replace(name=f"wan-widths-grid6x10-sink1-w3-dc{dc}", d_c=dc), ["sharp"], n_chunks=5)
 
 
 def test_rope_at_use_without_sink():
