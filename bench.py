@@ -141,8 +141,14 @@ def cpu_baseline(g, w, hist, n, x, sample_tokens: int):
     t0 = time.perf_counter()
     attend(g, w, hist, n, x, query_tokens=q)
     dt = time.perf_counter() - t0
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": sample_tokens / dt, "unit": "query tokens/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle",
+            "kind": "oracle", "blas_threads": threads, "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
             "sample": (f"{sample_tokens} of {g.n_q} query tokens (all {g.n_heads} heads) of one attend call "
                        f"against the full {g.n_k(n)} keys, float64 numpy; {dt:.1f} s")}
 
