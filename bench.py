@@ -237,8 +237,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the latent-attention path on a single MI355X "
-              "(see the sharding paragraph of the design notes); --gpus above 1 is not supported.",
+        print("bench.py measures one GPU: the latent-attention path runs on a single MI355X (how it would "
+              "shard is described in the design notes, not implemented); --gpus above 1 is not supported.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    """GPU tests are skipped (not failed) when no GPU is visible; a GPU machine with a
-    missing library fails them loudly instead."""
+    """GPU tests are skipped (not failed) when no GPU is visible; on a machine with
+    a GPU, a missing library fails them loudly instead."""
     try:
         import torch
         has_gpu = torch.cuda.is_available()
