@@ -205,6 +205,11 @@ void flash_attn_kernel(FlashArgs<T> p) {
   constexpr int NI = G::KI + G::CI;         // 1-KB loads per stage, spread over the waves
   constexpr int NI_W = (NI + NW - 1) / NW;
   static_assert(NW * RW <= kAttnMaxRows, "row block too large");
+  // Score widths up to 128 (d_c 24 and 96, the dense layer) are VALU-bound: a
+  // block's softmax outweighs its MFMAs.  There the running max is folded into
+  // the score MFMAs and the row sums use v_dot2; wider kernels have no register
+  // room for the folded accumulators and keep the plain form.
+  constexpr bool FOLD = HALF && D <= 128;
   static_assert(!VROWS || DV % 32 == 0, "value rows need whole 32-channel blocks");
 
   __shared__ __attribute__((aligned(16))) T lds0[G::BUF_EL];
@@ -339,10 +344,19 @@ void flash_attn_kernel(FlashArgs<T> p) {
     }
     f32x16 o[NB][NFB];
     float m_run[NB], l_run[NB];
+    // FOLD: each lane's 16 scores of a block belong to one query row, so the
+    // row's running maximum can enter the score MFMAs as their starting
+    // accumulator (the splat -m_fold): they produce s - m_fold directly.
+    // m_fold follows m_run at every rescale; it is 0 only before the first
+    // block, whose rescale is always taken.
+    f32x16 negm[NB];
+    float m_fold[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       m_run[nb] = NEG_INF;
       l_run[nb] = 0.f;
+      negm[nb] = f32x16{};
+      m_fold[nb] = 0.f;
 #pragma unroll
       for (int fb = 0; fb < NFB; ++fb) o[nb][fb] = f32x16{};
     }
@@ -358,7 +372,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
         // S^T for 32 keys x RW query rows; each K fragment feeds NB MFMAs
         f32x16 sc[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
+        for (int nb = 0; nb < NB; ++nb) sc[nb] = FOLD ? negm[nb] : f32x16{};
         const int r = 32 * kb + l32;
         if constexpr (HALF) {  // chunk 2ks+h of row r: one per-lane base, immediate offsets
           const T* kb0 = Ks + r * KS + h32 * VEC;
@@ -408,7 +422,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
           float m = sc[nb][0];
 #pragma unroll
           for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, sc[nb][rr]);
-          mx[nb] = pair_max(m);
+          mx[nb] = pair_max(m) + (FOLD ? m_fold[nb] : 0.f);  // the row max of s itself
           need[nb] = mx[nb] > m_run[nb] + kRescaleSlack;
           any_need |= need[nb];
         }
@@ -422,18 +436,31 @@ void flash_attn_kernel(FlashArgs<T> p) {
             l_run[nb] *= alpha;
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb) o[nb][fb] *= alpha;
+            if constexpr (FOLD) {  // re-base this block's scores and the next blocks' start
+              const float d = mnew - m_fold[nb];
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr) sc[nb][rr] -= d;
+              m_fold[nb] = mnew;
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr) negm[nb][rr] = -mnew;
+            }
           }
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          float lsum = 0.f;
+          if constexpr (FOLD) {  // sc already holds s - m_run; row sums below, from the fp16 operand
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const float e = __builtin_amdgcn_exp2f(sc[nb][rr] - m_run[nb]);
-            sc[nb][rr] = e;
-            lsum += e;
+            for (int rr = 0; rr < 16; ++rr) sc[nb][rr] = __builtin_amdgcn_exp2f(sc[nb][rr]);
+          } else {
+            float lsum = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const float e = __builtin_amdgcn_exp2f(sc[nb][rr] - m_run[nb]);
+              sc[nb][rr] = e;
+              lsum += e;
+            }
+            l_run[nb] += lsum;
           }
-          l_run[nb] += lsum;
         }
         // O^T += V^T[f][keys] * P^T[keys][rows]; each V^T fragment feeds NB MFMAs
         if constexpr (HALF) {
@@ -444,6 +471,19 @@ void flash_attn_kernel(FlashArgs<T> p) {
             for (int u = 0; u < 2; ++u)
 #pragma unroll
               for (int j = 0; j < 8; ++j) pf[nb][u][j] = (f16)sc[nb][8 * u + j];
+          if constexpr (FOLD) {  // row sums of the fp16 probabilities the value MFMAs use, two per v_dot2
+            const f16x2 one2 = {(f16)1.f, (f16)1.f};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              float lsum = 0.f;
+#pragma unroll
+              for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  lsum = __builtin_amdgcn_fdot2(f16x2{pf[nb][u][2 * j], pf[nb][u][2 * j + 1]}, one2, lsum, false);
+              l_run[nb] += lsum;
+            }
+          }
           constexpr int NV = 2 * NFB;
           auto vfrag = [&](int i) {
             return *reinterpret_cast<const f16x8*>(Ct + 32 * (i >> 1) * CS + 32 * kb + 16 * (i & 1) + 8 * h32);
