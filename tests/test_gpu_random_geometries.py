@@ -12,7 +12,9 @@ Each case draws:
 - 0-5 appends before the attend, so the window is empty, partial, full or
   wrapped.
 The expanded path is checked on the same state.  The sharpened query
-projection makes the softmax peaked, so online rescaling is exercised.  Same
+projection makes the softmax peaked, so online rescaling is exercised.  A
+fixed degenerate case adds the smallest geometry: one token per frame with
+one-frame windows and chunks, at every built d_c, with and without a sink.  Same
 bar and tolerance derivation as the other GPU tests (gpu_harness).
 """
 import numpy as np
@@ -54,4 +56,26 @@ def test_random_geometry(i):
         mae, mre = r.check(got_exp[b], x, b, what=f"random {i} expanded b={b}")
         print(f"  b={b}: absorbed max_abs={ma:.3e} mean_rel={mr:.3e}; expanded max_abs={mae:.3e} "
               f"mean_rel={mre:.3e}", flush=True)
+    r.dev.close()
+
+
+@pytest.mark.parametrize("dc", [96, 192, 448])
+@pytest.mark.parametrize("sink", [0, 1])
+def test_degenerate_single_token_frames(dc, sink):
+    """The smallest geometry: one token per frame, a one-frame window and a
+    one-frame chunk (12 query rows against 2 keys; with a sink, 3), two streams,
+    through empty, full and sliding windows."""
+    g = wl.WAN_LAYER.replace(name=f"one-token-dc{dc}-s{sink}", batch=2, grid_h=1, grid_w=1, window_frames=1,
+                             chunk_frames=1, d_c=dc, sink_frames=sink, rope_at_use=sink > 0)
+    print(f"case: one-token frames d_c={dc} sink={sink}", flush=True)
+    r = Rollout(g, mode="sharp", seed=dc + sink, cache_fill=float("nan"))
+    for k in range(4):
+        x = r.x(chunk=50 + k)
+        got = r.attend(x)
+        r.dev.expand()
+        got_exp = to_np(r.dev.attend_expanded(to_dev(x, g)))
+        for b in range(g.batch):
+            r.check(got[b], x, b, what=f"one-token d_c={dc} sink={sink} n={r.n} b={b}")
+            r.check(got_exp[b], x, b, what=f"one-token expanded d_c={dc} sink={sink} n={r.n} b={b}")
+        r.append(r.x(chunk=k))
     r.dev.close()
