@@ -39,7 +39,8 @@ def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
              + -(-g.n_q // key_tile))
     parts = [M * D * es, M * g.d_q * es, M * nh * g.d_nope * es, M * nh * D * es, M * nh * g.d_c * es,
              M * nh * g.d_v * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * 4, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
-             batch * tiles * dcp * (key_tile + 16 // es) * es,
+             # pre-pass tiles: fp16 key tiles (16-bit storage), transposed value images (fp32)
+             batch * tiles * key_tile * D * 2 if es == 2 else batch * tiles * dcp * (key_tile + 16 // es) * es,
              batch * (g.sink_frames + g.window_frames) * g.tokens_per_frame * D * es if g.rope_at_use or g.sink_frames
              else 0]
     return sum(_al(x) for x in parts)

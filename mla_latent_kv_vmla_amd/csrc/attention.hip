@@ -20,15 +20,21 @@
 // so softmax statistics live per lane (one query row per lane pair) and P never
 // leaves registers.
 //
-// Staging.  A key tile lives in LDS twice: row-major [key][D] (storage type) for
-// the score product, and transposed [channel][key] for the value product.  Both
-// are copied with LDS-DMA loads through a buffer resource (buffer_load_dwordx4
-// ... lds: lane L's 16 bytes land at M0 + 16 L), so staging needs no registers
-// and no VALU, and the resource's range check reads rows past a segment's end as
-// zero.  The transposed tile
-// comes either from images a pre-pass builds once per call in the workspace,
-// already in LDS layout (latent: the value is the key's first DV channels), or
-// straight from value rows [f][key] that the dense cache stores transposed.
+// Staging.  Tiles are copied into LDS with LDS-DMA loads through a buffer
+// resource (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at M0 + 16 L),
+// so staging needs no registers and no VALU, and the resource's range check
+// reads rows past a segment's end as zero.
+//   Latent attention, bf16 storage: one row-major key tile [KTILE][D] in fp16
+//     per stage, copied from the tiles a pre-pass converts once per call into
+//     the workspace.  The value is the key's first DV channels, so the value
+//     product reads its V^T fragments from that same tile with gfx950's
+//     transposing LDS read (ds_read_b64_tr_b16): one key tile serves both
+//     products.
+//   Dense attention: the row-major key tile (bf16) plus a transposed value tile
+//     [f][key] copied straight from value rows that the dense cache stores
+//     transposed.
+//   Latent attention, fp32 storage: the row-major key tile plus a transposed
+//     value tile from images a pre-pass builds once per call.
 // LDS layouts (per stage; two stages in two distinct arrays):
 //   Ks  [KTILE][D + 16 B]
 //   V^T [DVP][KTILE + 16 B]: within every 16-key group the key index has bits 2
@@ -36,14 +42,19 @@
 //       contiguous 16-B read.
 // A 128-bit LDS read is served 16 lanes at a time from 64 four-byte banks; with
 // the 16-B row pad the 16 rows one such group reads start in 16 distinct
-// 16-B bank groups, so both layouts read without bank conflicts.
+// 16-B bank groups, so both layouts read without bank conflicts.  A transposing
+// read gathers 8 bytes from each of 4 rows per 16-lane group; the pad puts
+// those rows in distinct banks too.
 //
-// Numerics.  With bf16 storage the value product runs on fp16 operands: values
-// are held as fp16 (latents converted bf16 -> fp16 by the pre-pass, exact in
-// fp16's normal range; the dense cache stores V as fp16) and P is rounded to
-// fp16.  When the softmax is nearly flat every probability sits just below 1,
-// where bf16's spacing (2^-8) exceeds the spread of the probabilities
-// themselves; fp16's spacing there is 2^-11, at the same MFMA rate.
+// Numerics.  With bf16 storage the value product runs on fp16 operands (values
+// held as fp16, P rounded to fp16).  When the softmax is nearly flat every
+// probability sits just below 1, where bf16's spacing (2^-8) exceeds the
+// spread of the probabilities themselves; fp16's spacing there is 2^-11, at
+// the same MFMA rate.  The dense cache stores V as fp16.  Latent attention
+// also takes its scores from fp16 operands, since the key tile is the value
+// tile: the bf16 -> fp16 conversion of keys and absorbed queries is exact in
+// fp16's normal range, so the scores are those of the bf16 inputs as long as
+// every key and query element stays below 65504 in magnitude.
 //
 // Scheduling.  G persistent workgroups.  With at least two (stream, row block)
 // units per workgroup, whole units go round-robin first; the remaining units
@@ -73,7 +84,7 @@ template <typename T> struct FlashArgs {
   const T* key1;            // chunk segment
   long key_ss0, key_ss1;
   const void* val0;         // value rows [f][key] (fp16 for bf16 storage) of the ring segment,
-  const void* val1;         //   of the chunk segment; or the per-call value-tile images (val0)
+  const void* val1;         //   of the chunk segment; or the per-call pre-pass tiles (val0)
   long val_ss0, val_ss1;    // elements per stream
   int val_rs0, val_rs1;     // elements per value row
   T* out;                   // row r of stream s: out + (s/heads)*out_so + (s%heads)*out_sh + r*out_rs
@@ -142,7 +153,7 @@ __device__ inline void tile_segment(const FlashArgs<T>& p, int t, int& g, int& k
   len = g ? p.len1 : p.len0;
 }
 
-// Pre-pass (latent attention): transposed value-tile images.  Image (s, t)
+// Pre-pass (latent attention, fp32 storage): transposed value-tile images.  Image (s, t)
 // holds, for the keys of tile t, rows = the first DV key channels (zero rows
 // pad DV up to a multiple of 32) in the value-operand type, keys permuted
 // within 16-key groups.  Keys past the segment's end repeat its last key
@@ -186,9 +197,37 @@ __global__ __launch_bounds__(256) void latent_value_tiles(FlashArgs<T> p) {
   for (int i = threadIdx.x; i < (G::DVP - DV) * G::CS; i += 256) img[DV * G::CS + i] = VT(0.f);
 }
 
-// VROWS = false: the transposed tile is copied from the pre-pass images (val0);
-// VROWS = true: from value rows val0/val1 ([f][key], keys permuted within
-// 16-key groups, zero past the segment's end up to the tile boundary).
+// Pre-pass (latent attention, bf16 storage): fp16 copies of the key tiles.
+// Tile (s, t) is row-major [KTILE][D] without padding; keys past the segment's
+// end repeat its last key (their probabilities are zero).
+template <typename T, int D, int KTILE>
+__global__ __launch_bounds__(256) void latent_key_tiles(FlashArgs<T> p) {
+  static_assert(std::is_same<T, bf16>::value, "the key tiles widen bf16");
+  constexpr int CV = D / 8;
+  const int t = blockIdx.x, s = blockIdx.y;
+  int g, kbase, len;
+  tile_segment<T, KTILE>(p, t, g, kbase, len);
+  const T* keys = g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0;
+  f16* img = reinterpret_cast<f16*>(const_cast<void*>(p.val0)) + ((size_t)s * p.KT + t) * (KTILE * D);
+  for (int v = threadIdx.x; v < KTILE * CV; v += 256) {
+    const int r = v / CV, c = v % CV;
+    const int key = min(kbase + r, len - 1);
+    const u32x4 k = ld16(keys + (long)key * D + c * 8);
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = k[e >> 1];
+      h[e] = (f16)((e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16));
+    }
+    *reinterpret_cast<f16x8*>(img + r * D + c * 8) = h;
+  }
+}
+
+// VROWS = false (latent): bf16 storage stages the pre-pass key tiles (val0) and
+// reads V^T from them transposed; fp32 storage stages the keys and the
+// pre-pass value images (val0).  VROWS = true (dense): the keys and value rows
+// val0/val1 ([f][key], keys permuted within 16-key groups, zero past the
+// segment's end up to the tile boundary).
 template <typename T, int D, int DV, int KTILE, int NW, int NB, bool VROWS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void flash_attn_kernel(FlashArgs<T> p) {
@@ -202,7 +241,8 @@ void flash_attn_kernel(FlashArgs<T> p) {
   constexpr int NKS = D / (2 * KPL);
   constexpr int NKB = KTILE / 32;
   constexpr int NFB = DVP / 32;
-  constexpr int NI = G::KI + G::CI;         // 1-KB loads per stage, spread over the waves
+  constexpr bool VT_FROM_K = !VROWS && HALF;  // one fp16 key tile; V^T read transposed from it
+  constexpr int NI = VT_FROM_K ? G::KI : G::KI + G::CI;  // 1-KB loads per stage, spread over the waves
   constexpr int NI_W = (NI + NW - 1) / NW;
   static_assert(NW * RW <= kAttnMaxRows, "row block too large");
   // Score widths up to 128 (d_c 24 and 96, the dense layer) are VALU-bound: a
@@ -211,9 +251,10 @@ void flash_attn_kernel(FlashArgs<T> p) {
   // room for the folded accumulators and keep the plain form.
   constexpr bool FOLD = HALF && D <= 128;
   static_assert(!VROWS || DV % 32 == 0, "value rows need whole 32-channel blocks");
+  static_assert(!VT_FROM_K || DVP <= D, "V^T fragments are read from the key tile's channels");
 
-  __shared__ __attribute__((aligned(16))) T lds0[G::BUF_EL];
-  __shared__ __attribute__((aligned(16))) T lds1[G::BUF_EL];
+  __shared__ __attribute__((aligned(16))) T lds0[VT_FROM_K ? G::KS_EL : G::BUF_EL];
+  __shared__ __attribute__((aligned(16))) T lds1[VT_FROM_K ? G::KS_EL : G::BUF_EL];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
@@ -249,8 +290,10 @@ void flash_attn_kernel(FlashArgs<T> p) {
   auto issue_tile = [&](int s, int t, T* buf) {
     int g, kbase, len;
     tile_segment<T, KTILE>(p, t, g, kbase, len);
-    const auto krs = raw_rsrc(g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0,
-                              (uint32_t)len * (uint32_t)(D * sizeof(T)));
+    const auto krs = VT_FROM_K ? raw_rsrc(static_cast<const char*>(p.val0) + ((size_t)s * p.KT + t) * (KTILE * D * 2),
+                                    (uint32_t)(KTILE * D * 2))
+                         : raw_rsrc(g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0,
+                                    (uint32_t)len * (uint32_t)(D * sizeof(T)));
     __amdgpu_buffer_rsrc_t vrs;
     uint32_t vrow = 0, vbase = 0;
     if constexpr (VROWS) {
@@ -268,7 +311,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
       if (idx < G::KI) {
         const int pos = idx * 64 + lane;
         if (G::KPOS % 64 == 0 || pos < G::KPOS) {
-          const uint32_t row = (uint32_t)kbase + (slot[k] >> 12);
+          const uint32_t row = (VT_FROM_K ? 0u : (uint32_t)kbase) + (slot[k] >> 12);
           lds_dma16(krs, (row * D + (slot[k] & 0xFFFu)) * (uint32_t)sizeof(T), buf + idx * 64 * VEC);
         }
       } else if (idx < NI) {
@@ -334,13 +377,22 @@ void flash_attn_kernel(FlashArgs<T> p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) mask_from[nb] = causal ? row_limit(row0 + 32 * nb + l32) : 0x7fffffff;
 
-    typename MF::Frag qf[NB][NKS];
+    using QFrag = typename std::conditional<VT_FROM_K, f16x8, typename MF::Frag>::type;
+    QFrag qf[NB][NKS];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int qrow = row0 + 32 * nb + l32;
       const T* qsrc = p.q + s * p.q_ss + (long)qrow * D + KPL * h32;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[nb][ks] = qrow < p.R ? MF::load(qsrc + ks * 2 * KPL) : MF::zero();
+      for (int ks = 0; ks < NKS; ++ks) {
+        const auto b = qrow < p.R ? MF::load(qsrc + ks * 2 * KPL) : MF::zero();
+        if constexpr (VT_FROM_K) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[nb][ks][e] = (f16)(float)b[e];
+        } else {
+          qf[nb][ks] = b;
+        }
+      }
     }
     f32x16 o[NB][NFB];
     float m_run[NB], l_run[NB];
@@ -378,8 +430,11 @@ void flash_attn_kernel(FlashArgs<T> p) {
           const T* kb0 = Ks + r * KS + h32 * VEC;
           // fragments are read kAhead steps before their MFMA; the scheduling
           // barriers keep the compiler from sinking each read onto its use
-          auto kfrag = [&](int ks) { return MF::load(kb0 + 2 * VEC * ks); };
-          typename MF::Frag kq[kAhead];
+          auto kfrag = [&](int ks) {
+            if constexpr (VT_FROM_K) return *reinterpret_cast<const f16x8*>(kb0 + 2 * VEC * ks);
+            else return MF::load(kb0 + 2 * VEC * ks);
+          };
+          QFrag kq[kAhead];
 #pragma unroll
           for (int i = 0; i < kAhead && i < NKS; ++i) kq[i] = kfrag(i);
 #pragma unroll
@@ -388,7 +443,10 @@ void flash_attn_kernel(FlashArgs<T> p) {
             const auto a = kq[ks % kAhead];
             if (ks + kAhead < NKS) kq[ks % kAhead] = kfrag(ks + kAhead);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) sc[nb] = MF::mma(a, qf[nb][ks], sc[nb]);
+            for (int nb = 0; nb < NB; ++nb) {
+              if constexpr (VT_FROM_K) sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[nb][ks], sc[nb], 0, 0, 0);
+              else sc[nb] = MF::mma(a, qf[nb][ks], sc[nb]);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -485,8 +543,30 @@ void flash_attn_kernel(FlashArgs<T> p) {
             }
           }
           constexpr int NV = 2 * NFB;
-          auto vfrag = [&](int i) {
-            return *reinterpret_cast<const f16x8*>(Ct + 32 * (i >> 1) * CS + 32 * kb + 16 * (i & 1) + 8 * h32);
+          auto vfrag = [&](int i) -> f16x8 {
+            if constexpr (VT_FROM_K) {
+              // Fragment i = (fb, u): element j of lane l is channel 32fb + l%32 of
+              // key 32kb + 16u + 4h32 + j%4 + 8(j/4), the key order in which the
+              // score accumulator hands over P^T.  In each 16-lane group the
+              // transposing read gives output lane m element m%4 of the 8-byte
+              // slots that source lanes m/4, m/4 + 4, m/4 + 8, m/4 + 12 address,
+              // so source lane sl addresses key 32kb + 16u + 4h32 + sl/4 at
+              // channel 32fb + 16(group%2) + 4(sl%4) (elements 0-3); the second
+              // read takes the keys 8 rows further (elements 4-7).
+              const int sl = lane & 15, gg = lane >> 4;
+              const int e = (32 * kb + 16 * (i & 1) + 4 * h32 + (sl >> 2)) * KS + 32 * (i >> 1) + 16 * (gg & 1) +
+                            4 * (sl & 3);
+              typedef short s16x4_t __attribute__((ext_vector_type(4)));
+              const s16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4_t*)(Ks + e));
+              const s16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4_t*)(Ks + e + 8 * KS));
+              typedef short s16x8_t __attribute__((ext_vector_type(8)));
+              const s16x8_t w = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+              return __builtin_bit_cast(f16x8, w);
+            } else {
+              return *reinterpret_cast<const f16x8*>(Ct + 32 * (i >> 1) * CS + 32 * kb + 16 * (i & 1) + 8 * h32);
+            }
           };
           f16x8 vq[kAhead];
 #pragma unroll
@@ -637,7 +717,10 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   a.dp_units = !causal && U >= 2L * a.G ? (U / a.G - 1) * a.G : 0;
   const long I = (U - a.dp_units) * a.KT;
   if (a.row_div <= 0) a.row_div = 1;
-  if constexpr (!VROWS) latent_value_tiles<T, D, DV, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
+  if constexpr (!VROWS) {
+    if constexpr (sizeof(T) == 2) latent_key_tiles<T, D, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
+    else latent_value_tiles<T, D, DV, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
+  }
   hipError_t err;
   if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
   flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS><<<a.G, NW * 64, 0, s>>>(a);
@@ -670,12 +753,13 @@ bool latent_attention_supported(DType dt, int dc, int dr) {
   return latent_shape(dt, dc, dr, sh);
 }
 
-size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, int stage_keys) {
+size_t latent_prepass_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, int stage_keys) {
   LatentShape sh;
   if (!latent_shape(dt, dc, dr, sh)) return 0;
   const size_t es = dt == DType::F32 ? 4 : 2;
   const size_t dcp = (size_t)(dc + 31) / 32 * 32;
   const size_t tiles = (size_t)(max_ring_keys + sh.ktile - 1) / sh.ktile + (stage_keys + sh.ktile - 1) / sh.ktile;
+  if (es == 2) return (size_t)B * tiles * sh.ktile * (size_t)(dc + dr) * 2;
   return (size_t)B * tiles * dcp * (sh.ktile + 16 / es) * es;
 }
 

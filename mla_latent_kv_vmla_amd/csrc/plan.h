@@ -41,7 +41,7 @@ struct Plan {
   void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV
   float *part_o; // [2G][kAttnMaxRows][dc] unnormalised partial outputs
   float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
-  void *vtiles;  // transposed value-tile images of the visible keys (per call)
+  void *vtiles;  // pre-pass tiles of the visible keys (per call): fp16 key tiles for bf16, value images for fp32
   void *assembled;  // rope_at_use: the visible cache rows with k_r rotated at local coordinates
 };
 
@@ -92,9 +92,10 @@ struct AttnCall {
 };
 hipError_t run_latent_attention(const AttnCall& a, hipStream_t s);
 bool latent_attention_supported(DType dt, int dc, int dr);
-// Workspace bytes of the transposed value-tile images for up to max_ring_keys
-// ring keys plus stage_keys chunk keys.
-size_t latent_value_tiles_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, int stage_keys);
+// Workspace bytes of the attention pre-pass tiles (fp16 key tiles for bf16,
+// transposed value images for fp32) for up to max_ring_keys ring keys plus
+// stage_keys chunk keys.
+size_t latent_prepass_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, int stage_keys);
 
 // ---------------------------------------------------------------- dense baseline
 // Per-head keys and values (the dense layer of the paper's section 1 and

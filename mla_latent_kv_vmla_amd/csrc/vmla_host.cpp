@@ -173,7 +173,7 @@ WorkspaceLayout workspace_layout(const Plan& p) {
   L.o = take(M * p.nh * (size_t)p.dv * es);
   L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * sizeof(float));
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
-  L.vtiles = take(latent_value_tiles_bytes(p.dtype, p.dc, p.dr, p.B, (p.S + p.W) * p.Tpf, p.Nq));
+  L.vtiles = take(latent_prepass_bytes(p.dtype, p.dc, p.dr, p.B, (p.S + p.W) * p.Tpf, p.Nq));
   L.assembled = take(p.rope_at_use ? (size_t)p.B * (p.S + p.W) * p.Tpf * p.D * es : 0);
   L.total = off;
   return L;
