@@ -27,11 +27,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
 
 SOURCES = ["vmla_host.cpp", "pipeline.hip", "dense.hip", "expanded.hip", "attention.hip"]
 
-# Per-source code generation options.  The attention kernels hold a 32*NB x DC
-# fp32 accumulator plus the absorbed query per wave; with MFMA results in the
-# VGPR form the register allocator keeps them in registers (AGPRs absorb the
-# overflow) instead of spilling to scratch memory.
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source code generation options (none at present).
+EXTRA: dict = {}
 
 
 def _hipcc() -> str:

@@ -122,6 +122,23 @@ __device__ inline float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// acc *= alpha for an accumulator held in AGPRs.  Each element passes through
+// one VGPR temporary inside the asm.  Written as plain C++ the product needs the
+// tuple in VGPRs, and the compiler then keeps a VGPR copy of every accumulator
+// live across the whole key loop (the copies are hoisted out of the rare
+// rescale branch), which at one wave per SIMD pushes the query fragments out
+// to scratch.
+__device__ inline void scale_acc_agpr(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = acc[r], t;
+    asm volatile("v_accvgpr_read_b32 %0, %1\n\tv_mul_f32_e32 %0, %2, %0\n\tv_accvgpr_write_b32 %1, %0"
+                 : "=&v"(t), "+a"(x)
+                 : "v"(alpha));
+    acc[r] = x;
+  }
+}
+
 // Compile-time geometry of one instantiation: score width D, value width DV.
 template <typename T, int D_, int DV, int KTILE> struct TileGeo {
   using VT = typename std::conditional<sizeof(T) == 2, f16, float>::type;  // value-product operand
@@ -250,6 +267,9 @@ void flash_attn_kernel(FlashArgs<T> p) {
   // the score MFMAs and the row sums use v_dot2; wider kernels have no register
   // room for the folded accumulators and keep the plain form.
   constexpr bool FOLD = HALF && D <= 128;
+  // Score widths above 256 (d_c 448) run one wave per SIMD with the value
+  // accumulators in AGPRs; their rescale must not move them to VGPRs.
+  constexpr bool ACC_AGPR = HALF && D > 256;
   static_assert(!VROWS || DV % 32 == 0, "value rows need whole 32-channel blocks");
   static_assert(!VT_FROM_K || DVP <= D, "V^T fragments are read from the key tile's channels");
 
@@ -493,7 +513,10 @@ void flash_attn_kernel(FlashArgs<T> p) {
             m_run[nb] = mnew;
             l_run[nb] *= alpha;
 #pragma unroll
-            for (int fb = 0; fb < NFB; ++fb) o[nb][fb] *= alpha;
+            for (int fb = 0; fb < NFB; ++fb) {
+              if constexpr (ACC_AGPR) scale_acc_agpr(o[nb][fb], alpha);
+              else o[nb][fb] *= alpha;
+            }
             if constexpr (FOLD) {  // re-base this block's scores and the next blocks' start
               const float d = mnew - m_fold[nb];
 #pragma unroll
@@ -744,7 +767,7 @@ static bool latent_shape(DType dt, int dc, int dr, LatentShape& sh) {
   if (dc == 24 && dr == 8) return sh = {64, 4, 1}, true;
   if (dr == 32 && dc == 96) return sh = {64, 8, 1}, true;
   if (dr == 32 && dc == 192) return sh = {64, 8, 1}, true;
-  if (dr == 32 && dc == 448) return sh = {32, 4, 1}, true;
+  if (dr == 32 && dc == 448) return sh = {64, 4, 1}, true;
   return false;
 }
 
@@ -794,7 +817,7 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
     if (c.dr == 32) {
       if (c.dc == 96) return launch_flash<T, 128, 96, 64, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
       if (c.dc == 192) return launch_flash<T, 224, 192, 64, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
-      if (c.dc == 448) return launch_flash<T, 480, 448, 32, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+      if (c.dc == 448) return launch_flash<T, 480, 448, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     }
     return hipErrorInvalidValue;
   }

@@ -268,7 +268,7 @@ def test_sink_config_rules():
 # ----------------------------------------------------------------------------- capacity arithmetic
 def test_capacity_formulas_match_the_library():
     from mla_latent_kv_vmla_amd import capacity as cap
-    cases = [(wl.WAN_LAYER, 64), (wl.WAN_SINK, 64), (wl.STRESS[96], 64), (wl.STRESS[192], 64), (wl.STRESS[448], 32),
+    cases = [(wl.WAN_LAYER, 64), (wl.WAN_SINK, 64), (wl.STRESS[96], 64), (wl.STRESS[192], 64), (wl.STRESS[448], 64),
              (wl.WAN_SMALL_GRID, 64)]
     for g, kt in cases:
         assert cap.latent_cache_bytes(g, g.batch) == vmla.vmla_cache_bytes(_cfg(g)), g.name
