@@ -154,7 +154,10 @@ VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stre
  * frames [max(0, n-W), n) and all tokens of the chunk itself (chunk-causal,
  * appendix D.4), followed by W_UV and W_O.  Leaves the cache and n unchanged:
  * the frozen-cache denoising steps of a rollout call this repeatedly, then
- * append the final step's x. */
+ * append the final step's x.  With bf16 storage the attention kernel takes its
+ * scores and values from fp16 copies of the cached rows and of the absorbed
+ * queries; the copies are exact while every element stays below 65504 in
+ * magnitude (larger elements become infinite, and the outputs NaN). */
 VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream);
 
 /* Same as vmla_attend, and additionally records attn_start on the stream right
