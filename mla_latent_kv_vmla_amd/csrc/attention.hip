@@ -18,7 +18,11 @@
 //   O^T[f][row]   += V^T[f][key] * P^T[key][row]      (the S^T accumulator is already
 //                                                      the B operand of this product)
 // so softmax statistics live per lane (one query row per lane pair) and P never
-// leaves registers.
+// leaves registers.  Two kernels share this layout: flash_attn_kernel (8 waves
+// x 32 rows, two waves per SIMD hiding each other's softmax; every width and
+// the dense layer) and flash_attn_pipe_kernel (4 waves x 64 rows, one wave per
+// SIMD that pipelines its own softmax under its MFMAs; latent d_c = 192 with
+// bf16 storage).
 //
 // Staging.  Tiles are copied into LDS with LDS-DMA loads through a buffer
 // resource (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at M0 + 16 L),
@@ -680,6 +684,459 @@ void flash_attn_kernel(FlashArgs<T> p) {
   }
 }
 
+// Software-pipelined latent attention, bf16 storage.  One workgroup = 4 waves
+// (one per SIMD) x 64 query rows (two 32-row blocks), so every K and V fragment
+// read from LDS feeds two MFMAs: half the LDS reads per FLOP of the 32-row
+// kernel.  With a single wave per SIMD no other wave hides the softmax, so each
+// wave hides its own: while the score MFMAs of 32-key block j+1 accumulate
+// (AGPRs), the softmax of block j runs on a VGPR copy of its scores, its
+// instructions placed one by one between the MFMAs; then the value MFMAs of
+// block j run.  The score MFMAs start from a splat of -m (the row's running
+// max), so they yield s - m and the softmax has no subtraction.  Three LDS
+// stages hold the tile of block j (value product), the tile of block j+1
+// (score product) and the tile two ahead (DMA in flight); one barrier per
+// tile.  Same staging (fp16 key tiles, V^T by transposing reads), scheduling
+// and numerics as flash_attn_kernel, whose comments cover them.
+template <int D, int DV, int KTILE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
+  using T = bf16;
+  using G = TileGeo<T, D, DV, KTILE>;
+  constexpr int NW = 4, NB = 2, RW = 64;
+  constexpr int KS = G::KS, VEC = G::VEC;
+  constexpr int NKS = D / 16;    // score k-steps of 16 channels
+  constexpr int NFB = G::DVP / 32;
+  constexpr int NV = 2 * NFB;    // value fragments per block
+  constexpr int NST = 3;
+  constexpr int KA = 2;          // fragment reads in flight ahead of their MFMA
+  constexpr int NI_W = (G::KI + NW - 1) / NW;
+  static_assert(KTILE == 64, "two 32-key blocks per tile");
+  static_assert(NW * RW <= kAttnMaxRows && G::DVP <= D, "bad shape");
+  static_assert(NKS == 14 && NFB == 6, "the issue-slot schedule is laid out for d_c 192 + d_r 32");
+
+  __shared__ __attribute__((aligned(16))) T lds[NST * G::KS_EL];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const float NEG_INF = -__builtin_huge_valf();
+
+  auto tile_rsrc = [&](int s, int t) __attribute__((always_inline)) {
+    return raw_rsrc(static_cast<const char*>(p.val0) + ((size_t)s * p.KT + t) * (KTILE * D * 2),
+                    (uint32_t)(KTILE * D * 2));
+  };
+  // LDS-DMA load k (0..NI_W-1) of this wave's share of a tile
+  auto issue_part = [&](__amdgpu_buffer_rsrc_t krs, T* buf, int k) __attribute__((always_inline)) {
+    const int idx = wave + k * NW;  // wave-uniform
+    const uint32_t pos = (uint32_t)(idx * 64 + lane);
+    // row pos / KCH, 16-B chunk pos % KCH of the padded row (the pad chunk loads chunk 0)
+    const uint32_t r = pos / G::KCH, c = pos % G::KCH;
+    // every wave has loads 0..NI_W-2; only the last may be past the tile
+    static_assert((NW - 1) + NW * (NI_W - 2) < G::KI && G::KPOS % 64 == 0, "tile split");
+    if (k < NI_W - 1 || idx < G::KI)
+      lds_dma16(krs, (r * D + (c < G::KCH - 1 ? c : 0) * VEC) * 2u, buf + idx * 64 * VEC);
+  };
+  auto issue_tile = [&](int s, int t, T* buf) __attribute__((always_inline)) {
+    const auto krs = tile_rsrc(s, t);
+#pragma unroll
+    for (int k = 0; k < NI_W; ++k) issue_part(krs, buf, k);
+  };
+
+  const bool causal = p.causal_tokens > 0;
+  auto row_limit = [&](int r) __attribute__((always_inline)) {
+    const int lim = (r / p.row_div / p.causal_tokens + 1) * p.causal_tokens;
+    return lim < p.len1 ? lim : p.len1;
+  };
+  const int vw = p.G % 8 == 0 ? (int)(blockIdx.x % 8) * (p.G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int n_whole = causal ? 0 : (int)(p.dp_units / p.G);
+  const long I = ((long)p.S * p.RB - (causal ? 0 : p.dp_units)) * p.KT;
+  const long it0 = (long)vw * I / p.G, it1 = (long)(vw + 1) * I / p.G;
+  const long u_first = causal ? (long)p.S * p.RB - 1 - blockIdx.x : p.dp_units + it0 / p.KT;
+  const int npieces = causal ? 1 : (int)((it1 - 1) / p.KT - it0 / p.KT + 1);
+  for (int job = 0; job < n_whole + npieces; ++job) {
+    const bool whole = job < n_whole;
+    const int k = job - n_whole;
+    const int piece = whole ? 0 : npieces > 1 ? (k == 0 ? npieces - 1 : k - 1) : 0;
+    const long unit = whole ? (long)job * p.G + vw : u_first + piece;
+    const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
+    int kt0, kt1;
+    if (causal) {
+      const int last_row = min((rb + 1) * (NW * RW), p.R) - 1;
+      kt0 = 0;
+      kt1 = p.tiles0 + (row_limit(last_row) + KTILE - 1) / KTILE;
+    } else if (whole) {
+      kt0 = 0;
+      kt1 = p.KT;
+    } else {
+      kt0 = piece == 0 ? (int)(it0 % p.KT) : 0;
+      kt1 = piece == npieces - 1 ? (int)((it1 - 1) % p.KT) + 1 : p.KT;
+    }
+    const bool first_piece = piece == 0;
+    const int row0 = rb * (NW * RW) + wave * RW;
+    const int mask_from_wg = causal ? row_limit(rb * (NW * RW)) : 0x7fffffff;
+    int mask_from[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) mask_from[nb] = causal ? row_limit(row0 + 32 * nb + l32) : 0x7fffffff;
+    const int ntiles = kt1 - kt0;
+    // element offsets of the stages of tiles i, i+1, i+2 (rotated per tile; no
+    // modulo, so LDS addresses stay provably non-negative and fragment offsets
+    // fold into the read instructions)
+    uint32_t st_cur = 0, st_nxt = G::KS_EL, st_nn = 2 * G::KS_EL;
+
+    // every wave is done with the stages of the previous job
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue_tile(s, kt0, lds + st_cur);
+    if (ntiles > 1) issue_tile(s, kt0 + 1, lds + st_nxt);
+
+    f16x8 qf[NB][NKS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int qrow = row0 + 32 * nb + l32;
+      const T* qsrc = p.q + s * p.q_ss + (long)qrow * D + 8 * h32;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 b = qrow < p.R ? *reinterpret_cast<const bf16x8*>(qsrc + 16 * ks) : bf16x8{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[nb][ks][e] = (f16)(float)b[e];
+      }
+    }
+    f32x16 o[NB][NFB];
+    float m_run[NB], l_run[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      l_run[nb] = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb) {
+        o[nb][fb] = f32x16{};
+        asm volatile("" : "+a"(o[nb][fb]));
+      }
+    }
+    f32x16 sc[NB];    // score accumulators of the next block (AGPRs)
+    f32x16 negm[NB];  // -m_run splat: the score MFMAs start from it, so they produce s - m_run
+    f32x16 d[NB];     // scores (minus m_run) of the current block, copied out of sc (VGPRs)
+    f16x8 kq[KA];     // K fragments of the next score product, read ahead
+    f16x8 pf[NB][2];
+
+    // LDS fragment readers: K rows of block kb of a stage (this lane's row and
+    // 16-B chunk), V^T fragments by transposing reads (as flash_attn_kernel).
+    auto kfrag = [&](const T* buf, int kb, int ks) __attribute__((always_inline)) {
+      return *reinterpret_cast<const f16x8*>(buf + (32 * kb + l32) * KS + h32 * VEC + 2 * VEC * ks);
+    };
+    auto vfrag = [&](const T* buf, int kb, int i) __attribute__((always_inline)) -> f16x8 {
+      const int sl = lane & 15, gg = lane >> 4;
+      const int e =
+          (32 * kb + 16 * (i & 1) + 4 * h32 + (sl >> 2)) * KS + 32 * (i >> 1) + 16 * (gg & 1) + 4 * (sl & 3);
+      typedef short s16x4_t __attribute__((ext_vector_type(4)));
+      const s16x4_t a0 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(buf + e));
+      const s16x4_t a1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(buf + e + 8 * KS));
+      return __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // Keys past the segment's end, or (block-causal) past a row's limit, -> -inf.
+    auto mask = [&](f32x16 (&sc)[NB], int t, int kb) __attribute__((always_inline)) {
+      int g, kbase, len;
+      tile_segment<T, KTILE>(p, t, g, kbase, len);
+      if (kbase + 32 * kb + 32 > min(len, mask_from_wg)) {
+        asm volatile("");
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = kbase + 32 * kb + 8 * (rr >> 2) + 4 * h32 + (rr & 3);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (key >= len || key >= mask_from[nb]) sc[nb][rr] = NEG_INF;
+        }
+      }
+    };
+    // Plain scores of block kb of `buf` into sc, no overlap (first block of a job).
+    auto qk_only = [&](f32x16 (&sc)[NB], const T* buf, int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f16x8 a = kfrag(buf, kb, ks);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[nb][ks], sc[nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(sc[nb]));
+    };
+    // Softmax work items of one block (d: VGPR copy of its scores), in the
+    // order they are issued between MFMAs.  Elements of the block are taken in
+    // two halves u: keys 16u..16u+15 of the block, i.e. rr = 8u..8u+7 of each
+    // row block; half u feeds the value MFMAs with B operand pf[.][u].
+    float mloc[NB], mx[NB], lsum[NB];
+    bool need[NB];
+    // q = 0..3: row block q/2, elements 8(q%2)..+7
+    auto max_item = [&](const f32x16 (&d)[NB], int q) __attribute__((always_inline)) {
+      const int nb = q >> 1, r0 = 8 * (q & 1);
+      float m = r0 ? mloc[nb] : d[nb][0];
+#pragma unroll
+      for (int rr = (r0 ? 0 : 1); rr < 8; ++rr) m = fmaxf(m, d[nb][r0 + rr]);
+      mloc[nb] = m;
+    };
+    auto cmp_item = [&](int nb) __attribute__((always_inline)) {
+      mx[nb] = pair_max(mloc[nb]);  // max of s - m_run over the row's keys of the block
+      need[nb] = mx[nb] > kRescaleSlack;
+    };
+    auto set_negm = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) negm[nb][rr] = -m_run[nb];
+        asm volatile("" : "+a"(negm[nb]));
+      }
+    };
+    // Rows whose block max exceeds m_run by more than the slack move m_run
+    // up; o and l follow.  Rare: a real (uniform) branch.
+    auto rescale = [&]() __attribute__((always_inline)) {
+      if (__any(need[0] || need[1])) {
+        asm volatile("");
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");  // value MFMAs still writing o
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const float dm = need[nb] ? mx[nb] : 0.f;
+          const float alpha = __builtin_amdgcn_exp2f(-dm);
+          m_run[nb] += dm;
+          l_run[nb] *= alpha;
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb) scale_acc_agpr(o[nb][fb], alpha);
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) d[nb][rr] -= dm;  // re-base this block's scores
+        }
+        set_negm();
+      }
+    };
+    // element k (0..15) of half u: row block k/8, rr = 8u + k%8
+    auto exp_item = [&](f32x16 (&d)[NB], int u, int k) __attribute__((always_inline)) {
+      const int nb = k >> 3, rr = 8 * u + (k & 7);
+      d[nb][rr] = __builtin_amdgcn_exp2f(d[nb][rr]);
+    };
+    // pair q (0..7) of half u: elements 2q, 2q+1 -> fp16 probabilities and their row sum
+    auto pack_item = [&](const f32x16 (&d)[NB], int u, int q) __attribute__((always_inline)) {
+      const int nb = q >> 2, j = 2 * (q & 3);
+      const f16x2 one2 = {(f16)1.f, (f16)1.f};
+      pf[nb][u][j] = (f16)d[nb][8 * u + j];
+      pf[nb][u][j + 1] = (f16)d[nb][8 * u + j + 1];
+      lsum[nb] = __builtin_amdgcn_fdot2(f16x2{pf[nb][u][j], pf[nb][u][j + 1]}, one2, lsum[nb], false);
+    };
+    // value fragment n in issue order: half n/NFB, 32-channel block n%NFB
+    auto vfrag_n = [&](const T* buf, int kb, int n) __attribute__((always_inline)) {
+      return vfrag(buf, kb, 2 * (n % NFB) + n / NFB);
+    };
+
+    auto copy_item = [&](int e) __attribute__((always_inline)) {  // element e (0..31) of sc -> d
+      float x = sc[e >> 4][e & 15];
+      asm volatile("" : "+v"(x));
+      d[e >> 4][e & 15] = x;
+    };
+    auto needs_mask = [&](int t, int kb) __attribute__((always_inline)) {
+      int g, kbase, len;
+      tile_segment<T, KTILE>(p, t, g, kbase, len);
+      return kbase + 32 * kb + 32 > min(len, mask_from_wg);
+    };
+
+    // One pipelined block.  On entry d holds the scores of block (t, kb) and
+    // mx/need its rescale test (both computed by the previous step, or by the
+    // prologue); masked keys are applied here (rare) and the test redone.
+    // Then 2*NKS score MFMAs of block (qbuf, qkb) into sc and 2*NV value MFMAs
+    // of block (t, kb) from pbuf run as issue slots.  A wave issues in order,
+    // and an MFMA occupies the matrix core for ~32 cycles; measured on gfx950,
+    // about four plain VALU instructions (or two with one v_exp_f32) fit
+    // behind one MFMA before they delay the next, so each slot carries about
+    // that much:
+    //   slots 0-15: exponentials of half 0; 2-16 (even): its fp16 packs and sums
+    //   slots 16-31: exponentials of half 1; 18-32 (even): its packs
+    //   slots 33-43: the next block's scores (complete since slot 27) -> d
+    //   slots 45-50: their block max and rescale test
+    //   odd slots 1-13 (dma): loads of the tile two ahead
+    // Value MFMAs of half 0 (slots 28-39) need the packs of half 0 only.
+    // prefetch: read the next step's first K fragments (nqbuf, nqkb) in the
+    // last slots.  has_next = false (last block of a job): no score product.
+    auto step = [&](const T* qbuf, int qkb, int t, int kb, const T* pbuf, bool has_next, bool kq_ready,
+                    const T* nqbuf, int nqkb, bool prefetch, bool dma, __amdgpu_buffer_rsrc_t krs,
+                    T* dbuf) __attribute__((always_inline)) {
+      if (needs_mask(t, kb)) {
+        asm volatile("");
+        mask(d, t, kb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) max_item(d, q);
+        cmp_item(0);
+        cmp_item(1);
+      }
+      rescale();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) lsum[nb] = 0.f;
+      if (!has_next) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) exp_item(d, u, k);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) pack_item(d, u, q);
+        }
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+          const f16x8 a = vfrag_n(pbuf, kb, n);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            o[nb][n % NFB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][n / NFB], o[nb][n % NFB], 0, 0, 0);
+        }
+      } else {
+        if (!kq_ready) {
+#pragma unroll
+          for (int i = 0; i < KA; ++i) kq[i] = kfrag(qbuf, qkb, i);
+        }
+        // the last load of this wave's share (some waves have none) here, the
+        // rest in slots 1, 3, ... (a wave-uniform branch would split the slots)
+        if (dma) issue_part(krs, dbuf, NI_W - 1);
+        f16x8 vq[KA];
+        constexpr int NQ = 2 * NKS, NS = NQ + 2 * NV;
+        auto slot_work = [&](int slot) __attribute__((always_inline)) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int nb = slot & 1;
+          if (slot < NQ) {  // score MFMA (k-step slot/2, row block nb); next K fragment after the last use
+            const int ks = slot >> 1;
+            sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq[ks % KA], qf[nb][ks], ks == 0 ? negm[nb] : sc[nb], 0, 0,
+                                                            0);
+            if (nb == 1 && ks + KA < NKS) kq[ks % KA] = kfrag(qbuf, qkb, ks + KA);
+            if (slot >= NQ - 2 * KA && nb == 0)
+              vq[(slot - (NQ - 2 * KA)) / 2] = vfrag_n(pbuf, kb, (slot - (NQ - 2 * KA)) / 2);
+          } else {  // value MFMA (fragment n, row block nb)
+            const int n = (slot - NQ) >> 1;
+            o[nb][n % NFB] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[n % KA], pf[nb][n / NFB], o[nb][n % NFB], 0, 0, 0);
+            if (nb == 1 && n + KA < NV) vq[n % KA] = vfrag_n(pbuf, kb, n + KA);
+          }
+          if (slot < 16) exp_item(d, 0, slot);
+          if (slot >= 2 && slot <= 16 && slot % 2 == 0) pack_item(d, 0, (slot - 2) / 2);
+          if (slot >= 16 && slot < 32) exp_item(d, 1, slot - 16);
+          if (slot >= 18 && slot <= 32 && slot % 2 == 0) pack_item(d, 1, (slot - 18) / 2);
+          if (slot >= 33 && slot < 44) {
+#pragma unroll
+            for (int e = 3 * (slot - 33); e < 3 * (slot - 33) + 3 && e < 32; ++e) copy_item(e);
+          }
+          if (slot >= 45 && slot < 49) max_item(d, slot - 45);
+          if (slot == 49 || slot == 50) cmp_item(slot - 49);
+          if (dma && slot % 2 == 1 && slot / 2 < NI_W - 1) issue_part(krs, dbuf, slot / 2);
+          if (prefetch && slot >= NS - 2 * KA && slot % 2 == 1)
+            kq[(slot - (NS - 2 * KA)) / 2] = kfrag(nqbuf, nqkb, (slot - (NS - 2 * KA)) / 2);
+        };
+        // four loops, so each stays within the compiler's full-unroll size limit
+#pragma unroll
+        for (int slot = 0; slot < 13; ++slot) slot_work(slot);
+#pragma unroll
+        for (int slot = 13; slot < 26; ++slot) slot_work(slot);
+#pragma unroll
+        for (int slot = 26; slot < 39; ++slot) slot_work(slot);
+#pragma unroll
+        for (int slot = 39; slot < NS; ++slot) slot_work(slot);
+        static_assert(NS == 52, "slot loops cover 52 slots");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(sc[nb]));
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        l_run[nb] += lsum[nb];
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb) asm volatile("" : "+a"(o[nb][fb]));
+      }
+    };
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Prologue: block 0's plain scores; their row max starts m_run (every
+    // job's first block holds a valid key for every row, so it is finite).
+    // K fragments of block 1 read ahead.
+    qk_only(sc, lds + st_cur, 0);
+#pragma unroll
+    for (int i = 0; i < KA; ++i) kq[i] = kfrag(lds + st_cur, 1, i);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) copy_item(e);
+    mask(d, kt0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) max_item(d, q);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m_run[nb] = pair_max(mloc[nb]);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) d[nb][rr] -= m_run[nb];
+      need[nb] = false;
+    }
+    set_negm();
+    for (int i = 0; i + 1 < ntiles; ++i) {
+      const int t = kt0 + i;
+      const T* cur = lds + st_cur;
+      // Tile t+1 has landed and every wave is past tile t-1 (its last reads
+      // were the value product of the previous step), whose stage takes tile
+      // t+2.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // block 0 of tile t under the scores of its block 1, with the loads of
+      // tile t+2 issued in its first slots; reads ahead the K fragments of
+      // block 0 of tile t+1
+      // (no tile t+2: an empty resource, whose loads write zeros into the free
+      // stage, keeps the slots free of branches)
+      const auto krs = i + 2 < ntiles ? tile_rsrc(s, t + 2) : raw_rsrc(p.val0, 0u);
+      step(cur, 1, t, 0, cur, true, true, lds + st_nxt, 0, true, true, krs, lds + st_nn);
+      // block 1 of tile t under the scores of block 0 of tile t+1; reads ahead
+      // the K fragments of block 1 of tile t+1
+      step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, lds + st_nn);
+      const uint32_t st_old = st_cur;
+      st_cur = st_nxt;
+      st_nxt = st_nn;
+      st_nn = st_old;
+    }
+    {  // last tile (landed: waited for at the previous tile's barrier, or in the prologue)
+      const int t = kt1 - 1;
+      const T* cur = lds + st_cur;
+      const auto krs = tile_rsrc(s, t);
+      step(cur, 1, t, 0, cur, true, true, cur, 0, false, false, krs, lds + st_nn);
+      step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, lds + st_nn);
+    }
+
+    const bool full = causal || (kt0 == 0 && kt1 == p.KT);
+    T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float l_tot = pair_sum(l_run[nb]);
+      const int qrow = row0 + 32 * nb + l32;
+      if (full) {
+        if (qrow < p.R) {
+          T* dst = out_s + (long)qrow * p.out_rs;
+          const float inv = 1.f / l_tot;
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int f = 32 * fb + 8 * q4 + 4 * h32;
+              if (f < DV)
+                store4(dst + f, o[nb][fb][4 * q4] * inv, o[nb][fb][4 * q4 + 1] * inv, o[nb][fb][4 * q4 + 2] * inv,
+                       o[nb][fb][4 * q4 + 3] * inv);
+            }
+        }
+      } else if (row0 < p.R) {
+        const long slot_row = (long)(2 * vw + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * RW + 32 * nb + l32;
+        float* po = p.part_o + slot_row * DV;
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int f = 32 * fb + 8 * q4 + 4 * h32;
+            if (f < DV)
+              *reinterpret_cast<f32x4*>(po + f) =
+                  f32x4{o[nb][fb][4 * q4], o[nb][fb][4 * q4 + 1], o[nb][fb][4 * q4 + 2], o[nb][fb][4 * q4 + 3]};
+          }
+        if (h32 == 0) {
+          p.part_ml[slot_row * 2] = m_run[nb];
+          p.part_ml[slot_row * 2 + 1] = l_tot;
+        }
+      }
+    }
+  }
+}
+
 // Merge the partial states of every row block that was split across workgroups
 // (units past dp_units).  Workgroups w0..w1 (virtual indices) hold the pieces of
 // row block `unit`;
@@ -726,7 +1183,7 @@ __global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
 }
 
 // Fill in the tiling fields, then launch: (pre-pass,) attention, (combine).
-template <typename T, int D, int DV, int KTILE, int NW, int NB, bool VROWS>
+template <typename T, int D, int DV, int KTILE, int NW, int NB, bool VROWS, bool PIPE = false>
 static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
   constexpr int ROWS = NW * 32 * NB;
   a.RB = (a.R + ROWS - 1) / ROWS;
@@ -746,7 +1203,12 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   }
   hipError_t err;
   if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
-  flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS><<<a.G, NW * 64, 0, s>>>(a);
+  if constexpr (PIPE) {
+    static_assert(NW == 4 && NB == 2 && !VROWS && sizeof(T) == 2, "pipelined kernel shape");
+    flash_attn_pipe_kernel<D, DV, KTILE><<<a.G, 256, 0, s>>>(a);
+  } else {
+    flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS><<<a.G, NW * 64, 0, s>>>(a);
+  }
   if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
   if (!causal && I != (long)a.G * a.KT)
     flash_attn_combine<T, DV, ROWS><<<(U - a.dp_units) * (ROWS / 16), 256, 0, s>>>(a);
@@ -766,7 +1228,7 @@ static bool latent_shape(DType dt, int dc, int dr, LatentShape& sh) {
   }
   if (dc == 24 && dr == 8) return sh = {64, 4, 1}, true;
   if (dr == 32 && dc == 96) return sh = {64, 8, 1}, true;
-  if (dr == 32 && dc == 192) return sh = {64, 8, 1}, true;
+  if (dr == 32 && dc == 192) return sh = {64, 4, 2}, true;
   if (dr == 32 && dc == 448) return sh = {64, 4, 1}, true;
   return false;
 }
@@ -816,7 +1278,7 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
     if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     if (c.dr == 32) {
       if (c.dc == 96) return launch_flash<T, 128, 96, 64, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
-      if (c.dc == 192) return launch_flash<T, 224, 192, 64, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+      if (c.dc == 192) return launch_flash<T, 224, 192, 64, 4, 2, false, true>(a, c.G, c.ev_start, c.ev_stop, s);
       if (c.dc == 448) return launch_flash<T, 480, 448, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     }
     return hipErrorInvalidValue;
