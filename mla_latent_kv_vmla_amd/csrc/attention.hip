@@ -703,18 +703,24 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   using T = bf16;
   using G = TileGeo<T, D, DV, KTILE>;
   constexpr int NW = 4, NB = 2, RW = 64;
-  constexpr int KS = G::KS, VEC = G::VEC;
+  // LDS key tile: rows of D elements, no pad; the 16-B chunk c of row r is
+  // stored at chunk c ^ ((r / 4) % 4).  A K-fragment read (16 lanes: 16 rows,
+  // one chunk) and a transposing V read (32 lanes: 4 rows, 4 chunks) then both
+  // touch every 16-B bank group of the 64 banks once.
+  constexpr int KS = D, VEC = 8, CH = D / 8, KS_EL = KTILE * D;
+  constexpr int KI = KTILE * CH / 64;  // 1-KB loads per tile
   constexpr int NKS = D / 16;    // score k-steps of 16 channels
   constexpr int NFB = G::DVP / 32;
   constexpr int NV = 2 * NFB;    // value fragments per block
   constexpr int NST = 3;
   constexpr int KA = 2;          // fragment reads in flight ahead of their MFMA
-  constexpr int NI_W = (G::KI + NW - 1) / NW;
+  constexpr int NI_W = KI / NW;
+  static_assert(CH % 4 == 0 && KI % NW == 0, "tile layout");
   static_assert(KTILE == 64, "two 32-key blocks per tile");
   static_assert(NW * RW <= kAttnMaxRows && G::DVP <= D, "bad shape");
   static_assert(NKS == 14 && NFB == 6, "the issue-slot schedule is laid out for d_c 192 + d_r 32");
 
-  __shared__ __attribute__((aligned(16))) T lds[NST * G::KS_EL];
+  __shared__ __attribute__((aligned(16))) T lds[NST * KS_EL];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
@@ -724,16 +730,14 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     return raw_rsrc(static_cast<const char*>(p.val0) + ((size_t)s * p.KT + t) * (KTILE * D * 2),
                     (uint32_t)(KTILE * D * 2));
   };
-  // LDS-DMA load k (0..NI_W-1) of this wave's share of a tile
+  // LDS-DMA load k (0..NI_W-1) of this wave's share of a tile: lane L of load
+  // idx fills stored chunk idx*64 + L, i.e. row r, stored chunk cs, which
+  // holds logical chunk cs ^ ((r / 4) % 4)
   auto issue_part = [&](__amdgpu_buffer_rsrc_t krs, T* buf, int k) __attribute__((always_inline)) {
     const int idx = wave + k * NW;  // wave-uniform
     const uint32_t pos = (uint32_t)(idx * 64 + lane);
-    // row pos / KCH, 16-B chunk pos % KCH of the padded row (the pad chunk loads chunk 0)
-    const uint32_t r = pos / G::KCH, c = pos % G::KCH;
-    // every wave has loads 0..NI_W-2; only the last may be past the tile
-    static_assert((NW - 1) + NW * (NI_W - 2) < G::KI && G::KPOS % 64 == 0, "tile split");
-    if (k < NI_W - 1 || idx < G::KI)
-      lds_dma16(krs, (r * D + (c < G::KCH - 1 ? c : 0) * VEC) * 2u, buf + idx * 64 * VEC);
+    const uint32_t r = pos / CH, c = (pos % CH) ^ ((r >> 2) & 3);
+    lds_dma16(krs, (r * D + c * VEC) * 2u, buf + idx * 64 * VEC);
   };
   auto issue_tile = [&](int s, int t, T* buf) __attribute__((always_inline)) {
     const auto krs = tile_rsrc(s, t);
@@ -780,7 +784,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     // element offsets of the stages of tiles i, i+1, i+2 (rotated per tile; no
     // modulo, so LDS addresses stay provably non-negative and fragment offsets
     // fold into the read instructions)
-    uint32_t st_cur = 0, st_nxt = G::KS_EL, st_nn = 2 * G::KS_EL;
+    uint32_t st_cur = 0, st_nxt = KS_EL, st_nn = 2 * KS_EL;
 
     // every wave is done with the stages of the previous job
     __builtin_amdgcn_s_waitcnt(0);
@@ -817,20 +821,25 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     f16x8 kq[KA];     // K fragments of the next score product, read ahead
     f16x8 pf[NB][2];
 
-    // LDS fragment readers: K rows of block kb of a stage (this lane's row and
-    // 16-B chunk), V^T fragments by transposing reads (as flash_attn_kernel).
+    // LDS fragment readers (swizzled tile).  K: row 32kb + l32 (so (r/4)%4 =
+    // (l32/4)%4), logical chunk 2ks + h32.  V^T (as flash_attn_kernel, by
+    // transposing reads): source lane sl of 16-lane group gg reads 8 bytes of
+    // row 32kb + 16u + 4h32 + sl/4 ((r/4)%4 = h32; + 8 rows for the second
+    // read: h32 ^ 2), logical chunk 4fb + 2(gg%2) + (sl%4)/2, half sl%2.
+    const int kq_sw = (l32 >> 2) & 3;
     auto kfrag = [&](const T* buf, int kb, int ks) __attribute__((always_inline)) {
-      return *reinterpret_cast<const f16x8*>(buf + (32 * kb + l32) * KS + h32 * VEC + 2 * VEC * ks);
+      return *reinterpret_cast<const f16x8*>(buf + (32 * kb + l32) * KS + ((2 * ks + h32) ^ kq_sw) * VEC);
     };
+    const int v_sl = lane & 15, v_c = 2 * ((lane >> 4) & 1) + ((v_sl & 3) >> 1);
+    const int v_off1 = (4 * h32 + (v_sl >> 2)) * KS + (v_c ^ h32) * VEC + 4 * (v_sl & 1);
+    const int v_off2 = (8 + 4 * h32 + (v_sl >> 2)) * KS + (v_c ^ h32 ^ 2) * VEC + 4 * (v_sl & 1);
     auto vfrag = [&](const T* buf, int kb, int i) __attribute__((always_inline)) -> f16x8 {
-      const int sl = lane & 15, gg = lane >> 4;
-      const int e =
-          (32 * kb + 16 * (i & 1) + 4 * h32 + (sl >> 2)) * KS + 32 * (i >> 1) + 16 * (gg & 1) + 4 * (sl & 3);
+      const int e0 = (32 * kb + 16 * (i & 1)) * KS + 32 * (i >> 1);  // rows of the block half, chunk group fb
       typedef short s16x4_t __attribute__((ext_vector_type(4)));
       const s16x4_t a0 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(buf + e));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(buf + e0 + v_off1));
       const s16x4_t a1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(buf + e + 8 * KS));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(buf + e0 + v_off2));
       return __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     // Keys past the segment's end, or (block-causal) past a row's limit, -> -inf.
@@ -987,9 +996,6 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
 #pragma unroll
           for (int i = 0; i < KA; ++i) kq[i] = kfrag(qbuf, qkb, i);
         }
-        // the last load of this wave's share (some waves have none) here, the
-        // rest in slots 1, 3, ... (a wave-uniform branch would split the slots)
-        if (dma) issue_part(krs, dbuf, NI_W - 1);
         f16x8 vq[KA];
         constexpr int NQ = 2 * NKS, NS = NQ + 2 * NV;
         auto slot_work = [&](int slot) __attribute__((always_inline)) {
@@ -1018,7 +1024,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           }
           if (slot >= 45 && slot < 49) max_item(d, slot - 45);
           if (slot == 49 || slot == 50) cmp_item(slot - 49);
-          if (dma && slot % 2 == 1 && slot / 2 < NI_W - 1) issue_part(krs, dbuf, slot / 2);
+          if (dma && slot % 2 == 1 && slot / 2 < NI_W) issue_part(krs, dbuf, slot / 2);
           if (prefetch && slot >= NS - 2 * KA && slot % 2 == 1)
             kq[(slot - (NS - 2 * KA)) / 2] = kfrag(nqbuf, nqkb, (slot - (NS - 2 * KA)) / 2);
         };
