@@ -268,10 +268,12 @@ def main():
                                                  wl.latent_weights(g, layer=l, mode="literal").as_dict().items()})
                         for l in range(1, g.layers if args.path == "absorbed" else 1)]
         attend_profiled, append = vmla.vmla_attend_profiled, vmla.vmla_compress_append
-        kernel = "flash_attn_kernel (latent, absorbed)"
+        # bf16 at d_c = 192 runs the software-pipelined 64-row kernel
+        lat = "flash_attn_pipe_kernel" if (g.d_c == 192 and g.dtype == "bf16") else "flash_attn_kernel"
+        kernel = f"{lat} (latent, absorbed)"
         if args.path == "clip":
             clip_ws = torch.empty(vmla.vmla_clip_workspace_bytes(layer.cfg), dtype=torch.uint8, device=dev)
-            kernel = "flash_attn_kernel (latent, block-causal clip)"
+            kernel = f"{lat} (latent, block-causal clip)"
         if args.path == "expanded":
             expanded = torch.empty(vmla.vmla_expanded_bytes(layer.cfg), dtype=torch.uint8, device=dev)
             attend_profiled = lambda ctx, x, o, a, b, st: vmla.vmla_attend_expanded_profiled(ctx, expanded, x, o, a,
