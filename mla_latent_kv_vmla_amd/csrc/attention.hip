@@ -703,11 +703,15 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   using T = bf16;
   using G = TileGeo<T, D, DV, KTILE>;
   constexpr int NW = 4, NB = 2, RW = 64;
-  // LDS key tile: rows of D elements, no pad; the 16-B chunk c of row r is
-  // stored at chunk c ^ ((r / 4) % 4).  A K-fragment read (16 lanes: 16 rows,
-  // one chunk) and a transposing V read (32 lanes: 4 rows, 4 chunks) then both
-  // touch every 16-B bank group of the 64 banks once.
-  constexpr int KS = D, VEC = 8, CH = D / 8, KS_EL = KTILE * D;
+  // LDS key tile (16-B chunk c of key row r): four regions of 16 rows (wave w
+  // loads region w), each of CH/4 blocks of 1 KB holding chunks 4k..4k+3 of
+  // its rows; within a block, chunk c sits at 256 (c % 4) + 16 ((r % 16) ^
+  // 4 (c % 4)) bytes.  A K-fragment read (16 lanes: 16 rows of one chunk) and a
+  // transposing V read (32 lanes: 4 rows, 4 chunks) both touch every 16-B bank
+  // group of the 64 banks once, and each lane's DMA source is a constant of
+  // the lane plus 64 bytes per block (no address arithmetic per load).
+  constexpr int VEC = 8, CH = D / 8, KS_EL = KTILE * D;
+  constexpr int REG_EL = 16 * D;       // elements per 16-row region
   constexpr int KI = KTILE * CH / 64;  // 1-KB loads per tile
   constexpr int NKS = D / 16;    // score k-steps of 16 channels
   constexpr int NFB = G::DVP / 32;
@@ -715,7 +719,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   constexpr int NST = 3;
   constexpr int KA = 2;          // fragment reads in flight ahead of their MFMA
   constexpr int NI_W = KI / NW;
-  static_assert(CH % 4 == 0 && KI % NW == 0, "tile layout");
+  static_assert(CH % 4 == 0 && KI % NW == 0 && KTILE == 16 * NW, "tile layout: one 16-row region per wave");
   static_assert(KTILE == 64, "two 32-key blocks per tile");
   static_assert(NW * RW <= kAttnMaxRows && G::DVP <= D, "bad shape");
   static_assert(NKS == 14 && NFB == 6, "the issue-slot schedule is laid out for d_c 192 + d_r 32");
@@ -730,14 +734,12 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     return raw_rsrc(static_cast<const char*>(p.val0) + ((size_t)s * p.KT + t) * (KTILE * D * 2),
                     (uint32_t)(KTILE * D * 2));
   };
-  // LDS-DMA load k (0..NI_W-1) of this wave's share of a tile: lane L of load
-  // idx fills stored chunk idx*64 + L, i.e. row r, stored chunk cs, which
-  // holds logical chunk cs ^ ((r / 4) % 4)
+  // LDS-DMA load k (0..NI_W-1) of this wave's share of a tile: block k of
+  // region `wave`; lane L fills slot L: chunk 4k + L/16 of row
+  // 16 wave + ((L % 16) ^ 4 (L / 16))
+  const uint32_t dma_voff = (uint32_t)(((16 * wave + ((lane & 15) ^ (4 * (lane >> 4)))) * D + 8 * (lane >> 4)) * 2);
   auto issue_part = [&](__amdgpu_buffer_rsrc_t krs, T* buf, int k) __attribute__((always_inline)) {
-    const int idx = wave + k * NW;  // wave-uniform
-    const uint32_t pos = (uint32_t)(idx * 64 + lane);
-    const uint32_t r = pos / CH, c = (pos % CH) ^ ((r >> 2) & 3);
-    lds_dma16(krs, (r * D + c * VEC) * 2u, buf + idx * 64 * VEC);
+    lds_dma16(krs, dma_voff + (uint32_t)(64 * k), buf + wave * REG_EL + k * 512);
   };
   auto issue_tile = [&](int s, int t, T* buf) __attribute__((always_inline)) {
     const auto krs = tile_rsrc(s, t);
@@ -821,20 +823,25 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     f16x8 kq[KA];     // K fragments of the next score product, read ahead
     f16x8 pf[NB][2];
 
-    // LDS fragment readers (swizzled tile).  K: row 32kb + l32 (so (r/4)%4 =
-    // (l32/4)%4), logical chunk 2ks + h32.  V^T (as flash_attn_kernel, by
-    // transposing reads): source lane sl of 16-lane group gg reads 8 bytes of
-    // row 32kb + 16u + 4h32 + sl/4 ((r/4)%4 = h32; + 8 rows for the second
-    // read: h32 ^ 2), logical chunk 4fb + 2(gg%2) + (sl%4)/2, half sl%2.
-    const int kq_sw = (l32 >> 2) & 3;
+    // LDS fragment readers (element offsets; a region is REG_EL elements, a
+    // block 512, a chunk-of-block column 128, a slot 8).  K: row 32kb + l32
+    // (region 2kb + l32/16), chunk 2ks + h32 (block ks/2, column
+    // cc = 2 (ks % 2) + h32): one lane offset for even and one for odd ks.
+    const int k_off0 = REG_EL * (l32 >> 4) + 128 * h32 + 8 * ((l32 & 15) ^ (4 * h32));
+    const int k_off1 = REG_EL * (l32 >> 4) + 128 * h32 + 8 * ((l32 & 15) ^ (8 + 4 * h32));
     auto kfrag = [&](const T* buf, int kb, int ks) __attribute__((always_inline)) {
-      return *reinterpret_cast<const f16x8*>(buf + (32 * kb + l32) * KS + ((2 * ks + h32) ^ kq_sw) * VEC);
+      return *reinterpret_cast<const f16x8*>(buf + ((ks & 1) ? k_off1 : k_off0) + 2 * REG_EL * kb + 512 * (ks >> 1) +
+                                             256 * (ks & 1));
     };
-    const int v_sl = lane & 15, v_c = 2 * ((lane >> 4) & 1) + ((v_sl & 3) >> 1);
-    const int v_off1 = (4 * h32 + (v_sl >> 2)) * KS + (v_c ^ h32) * VEC + 4 * (v_sl & 1);
-    const int v_off2 = (8 + 4 * h32 + (v_sl >> 2)) * KS + (v_c ^ h32 ^ 2) * VEC + 4 * (v_sl & 1);
+    // V^T (as flash_attn_kernel, by transposing reads): source lane sl of
+    // 16-lane group gg reads 8 bytes (half sl % 2) of row 32kb + 16u + 4h32 +
+    // sl/4 (+ 8 for the second read; region 2kb + u), chunk 4fb + i with
+    // i = 2(gg%2) + (sl%4)/2 (block fb, column i).
+    const int v_sl = lane & 15, v_i = 2 * ((lane >> 4) & 1) + ((v_sl & 3) >> 1);
+    const int v_off1 = 128 * v_i + 8 * ((4 * h32 + (v_sl >> 2)) ^ (4 * v_i)) + 4 * (v_sl & 1);
+    const int v_off2 = 128 * v_i + 8 * ((8 + 4 * h32 + (v_sl >> 2)) ^ (4 * v_i)) + 4 * (v_sl & 1);
     auto vfrag = [&](const T* buf, int kb, int i) __attribute__((always_inline)) -> f16x8 {
-      const int e0 = (32 * kb + 16 * (i & 1)) * KS + 32 * (i >> 1);  // rows of the block half, chunk group fb
+      const int e0 = REG_EL * (2 * kb + (i & 1)) + 512 * (i >> 1);  // region of the block half, block fb
       typedef short s16x4_t __attribute__((ext_vector_type(4)));
       const s16x4_t a0 =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(buf + e0 + v_off1));
@@ -958,7 +965,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     //   slots 16-31: exponentials of half 1; 18-32 (even): its packs
     //   slots 33-43: the next block's scores (complete since slot 27) -> d
     //   slots 45-50: their block max and rescale test
-    //   odd slots 1-13 (dma): loads of the tile two ahead
+    //   slots 48-51 (dma): loads of the tile two ahead, two per slot
     // Value MFMAs of half 0 (slots 28-39) need the packs of half 0 only.
     // prefetch: read the next step's first K fragments (nqbuf, nqkb) in the
     // last slots.  has_next = false (last block of a job): no score product.
@@ -1024,7 +1031,13 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           }
           if (slot >= 45 && slot < 49) max_item(d, slot - 45);
           if (slot == 49 || slot == 50) cmp_item(slot - 49);
-          if (dma && slot % 2 == 1 && slot / 2 < NI_W) issue_part(krs, dbuf, slot / 2);
+          // After the step's last transposing read: the compiler cannot tell the
+          // DMA's stage from the stages being read and waits for the DMA before
+          // any later transposing read (the next step's first, ~25 slots on).
+          if (dma && slot >= NS - 4) {
+#pragma unroll
+            for (int k = 2 * (slot - (NS - 4)); k < 2 * (slot - (NS - 4)) + 2 && k < NI_W; ++k) issue_part(krs, dbuf, k);
+          }
           if (prefetch && slot >= NS - 2 * KA && slot % 2 == 1)
             kq[(slot - (NS - 2 * KA)) / 2] = kfrag(nqbuf, nqkb, (slot - (NS - 2 * KA)) / 2);
         };
