@@ -684,6 +684,86 @@ void flash_attn_kernel(FlashArgs<T> p) {
   }
 }
 
+// Issue-slot plan of the pipelined kernel's softmax work (see step() in
+// flash_attn_pipe_kernel).  A step has NS = NQ + 2 NV slots, one MFMA each
+// (NQ score MFMAs, then 2 NV value MFMAs: half 0 of the block's keys, then
+// half 1).  Work items, in issue order, with their cost in plain-VALU units
+// (a v_exp_f32 counts 2):
+//   [0, 16)   exponential k of half 0 (row block k/8, element 8u + k%8 with u = 0)
+//   [16, 24)  fp16 pack + v_dot2 row sum of half-0 pair q (elements 2q, 2q+1)
+//   [24, 40)  exponentials of half 1;  [40, 48) packs of half 1
+//   [48, 80)  copy of score element e of the next block out of its accumulator
+//   [80, 84)  block max over 8 elements;  [84, 86) pair max and rescale test
+// Each item goes to the first slot at or after its predecessor's that has
+// room within BUDGET units and follows its inputs (a pack one slot after its
+// second exponential, copies after the last score MFMA, a max after its
+// copies, a test after its maxes).  Half-u packs must precede the first value
+// MFMA that reads them.  The plan uses the smallest budget that meets every
+// deadline: about four plain VALU instructions fit behind one MFMA on gfx950.
+struct PipeSlotPlan {
+  static constexpr int NITEM = 86, MAXS = 128, MAXPER = 8;
+  int slot_of[NITEM];
+  int lo[MAXS], hi[MAXS];  // slot s issues items pipe_item_order(lo[s] .. hi[s]-1)
+  int budget;
+  bool ok;
+};
+constexpr int pipe_item_cost(int i) { return i < 48 ? 2 : i < 80 ? 1 : 4; }
+// issue order: exponentials of each half interleaved with the packs they complete
+constexpr int pipe_item_order(int j) {
+  if (j < 48) {
+    const int h = j / 24, r = j % 24, grp = r / 3, pos = r % 3;  // per pair q: E[2q], E[2q+1], P[q]
+    return pos < 2 ? 24 * h + 2 * grp + pos : 24 * h + 16 + grp;
+  }
+  return j;
+}
+constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget) {
+  PipeSlotPlan p{};
+  p.budget = budget;
+  p.ok = true;
+  const int NS = NQ + 2 * NV;
+  int load[128] = {};
+  int cur = 0;
+  for (int j = 0; j < PipeSlotPlan::NITEM; ++j) {
+    const int i = pipe_item_order(j);
+    int earliest = cur;
+    if (i >= 16 && i < 24) earliest = p.slot_of[2 * (i - 16) + 1] + 1;
+    if (i >= 40 && i < 48) earliest = p.slot_of[24 + 2 * (i - 40) + 1] + 1;
+    if (i >= 48 && i < 80) earliest = NQ + 1;
+    if (i >= 80 && i < 84) earliest = p.slot_of[48 + 16 * ((i - 80) >> 1) + 8 * ((i - 80) & 1) + 7] + 1;
+    if (i >= 84) earliest = p.slot_of[80 + 2 * (i - 84) + 1] + 1;
+    int s = earliest > cur ? earliest : cur;
+    while (s < NS && load[s] > 0 && load[s] + pipe_item_cost(i) > budget) ++s;
+    if (s >= NS) {
+      p.ok = false;
+      return p;
+    }
+    p.slot_of[i] = s;
+    load[s] += pipe_item_cost(i);
+    cur = s;
+    int deadline = NS - 1;
+    if (i >= 16 && i < 24) deadline = NQ - 1 + ((i - 16) >= 4 ? 1 : 0);
+    if (i >= 40 && i < 48) deadline = NQ + NV - 1 + ((i - 40) >= 4 ? 1 : 0);
+    if (s > deadline) p.ok = false;
+  }
+  // items go to slots in issue order, so each slot holds a run of it
+  for (int s = 0; s < PipeSlotPlan::MAXS; ++s) p.lo[s] = p.hi[s] = PipeSlotPlan::NITEM;
+  for (int j = PipeSlotPlan::NITEM - 1; j >= 0; --j) p.lo[p.slot_of[pipe_item_order(j)]] = j;
+  for (int j = 0; j < PipeSlotPlan::NITEM; ++j) p.hi[p.slot_of[pipe_item_order(j)]] = j + 1;
+  for (int s = 0; s < NS; ++s) {
+    if (p.lo[s] == PipeSlotPlan::NITEM) p.lo[s] = p.hi[s] = 0;
+    if (p.hi[s] - p.lo[s] > PipeSlotPlan::MAXPER) p.ok = false;
+  }
+  return p;
+}
+constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV) {
+  for (int b = 3; b <= 12; ++b) {
+    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b);
+    if (p.ok) return p;
+  }
+  return pipe_slot_plan_b(NQ, NV, 0);
+}
+template <int NQ, int NV> inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV);
+
 // Software-pipelined latent attention, bf16 storage.  One workgroup = 4 waves
 // (one per SIMD) x 64 query rows (two 32-row blocks), so every K and V fragment
 // read from LDS feeds two MFMAs: half the LDS reads per FLOP of the 32-row
@@ -722,7 +802,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   static_assert(CH % 4 == 0 && KI % NW == 0 && KTILE == 16 * NW, "tile layout: one 16-row region per wave");
   static_assert(KTILE == 64, "two 32-key blocks per tile");
   static_assert(NW * RW <= kAttnMaxRows && G::DVP <= D, "bad shape");
-  static_assert(NKS == 14 && NFB == 6, "the issue-slot schedule is laid out for d_c 192 + d_r 32");
+  static_assert(NKS * 16 == D && G::DVP == DV, "whole 16-channel k-steps and 32-channel value blocks");
 
   __shared__ __attribute__((aligned(16))) T lds[NST * KS_EL];
 
@@ -961,12 +1041,10 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     // about four plain VALU instructions (or two with one v_exp_f32) fit
     // behind one MFMA before they delay the next, so each slot carries about
     // that much:
-    //   slots 0-15: exponentials of half 0; 2-16 (even): its fp16 packs and sums
-    //   slots 16-31: exponentials of half 1; 18-32 (even): its packs
-    //   slots 33-43: the next block's scores (complete since slot 27) -> d
-    //   slots 45-50: their block max and rescale test
-    //   slots 48-51 (dma): loads of the tile two ahead, two per slot
-    // Value MFMAs of half 0 (slots 28-39) need the packs of half 0 only.
+    // the softmax items placed by PipeSlotPlan (exponentials and packs of
+    // half 0 and half 1, then the next block's copy, max and rescale test; the
+    // value MFMAs of half 0 need the packs of half 0 only), and in the last
+    // four slots the loads of the tile two ahead (dma), two per slot.
     // prefetch: read the next step's first K fragments (nqbuf, nqkb) in the
     // last slots.  has_next = false (last block of a job): no score product.
     auto step = [&](const T* qbuf, int qkb, int t, int kb, const T* pbuf, bool has_next, bool kq_ready,
@@ -1005,6 +1083,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         }
         f16x8 vq[KA];
         constexpr int NQ = 2 * NKS, NS = NQ + 2 * NV;
+        static_assert(kPipeSlotPlan<NQ, NV>.ok, "no issue-slot plan meets the deadlines");
         auto slot_work = [&](int slot) __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
           const int nb = slot & 1;
@@ -1021,16 +1100,19 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
                 __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[n % KA], pf[nb][n / NFB], o[nb][n % NFB], 0, 0, 0);
             if (nb == 1 && n + KA < NV) vq[n % KA] = vfrag_n(pbuf, kb, n + KA);
           }
-          if (slot < 16) exp_item(d, 0, slot);
-          if (slot >= 2 && slot <= 16 && slot % 2 == 0) pack_item(d, 0, (slot - 2) / 2);
-          if (slot >= 16 && slot < 32) exp_item(d, 1, slot - 16);
-          if (slot >= 18 && slot <= 32 && slot % 2 == 0) pack_item(d, 1, (slot - 18) / 2);
-          if (slot >= 33 && slot < 44) {
 #pragma unroll
-            for (int e = 3 * (slot - 33); e < 3 * (slot - 33) + 3 && e < 32; ++e) copy_item(e);
+          for (int k = 0; k < PipeSlotPlan::MAXPER; ++k) {
+            const int j = kPipeSlotPlan<NQ, NV>.lo[slot] + k;
+            if (j >= kPipeSlotPlan<NQ, NV>.hi[slot]) continue;
+            const int i = pipe_item_order(j);
+            if (i < 16) exp_item(d, 0, i);
+            else if (i < 24) pack_item(d, 0, i - 16);
+            else if (i < 40) exp_item(d, 1, i - 24);
+            else if (i < 48) pack_item(d, 1, i - 40);
+            else if (i < 80) copy_item(i - 48);
+            else if (i < 84) max_item(d, i - 80);
+            else cmp_item(i - 84);
           }
-          if (slot >= 45 && slot < 49) max_item(d, slot - 45);
-          if (slot == 49 || slot == 50) cmp_item(slot - 49);
           // After the step's last transposing read: the compiler cannot tell the
           // DMA's stage from the stages being read and waits for the DMA before
           // any later transposing read (the next step's first, ~25 slots on).
@@ -1041,16 +1123,24 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           if (prefetch && slot >= NS - 2 * KA && slot % 2 == 1)
             kq[(slot - (NS - 2 * KA)) / 2] = kfrag(nqbuf, nqkb, (slot - (NS - 2 * KA)) / 2);
         };
-        // four loops, so each stays within the compiler's full-unroll size limit
+        // eight loops, so each stays within the compiler's full-unroll size limit
+        constexpr int NS8 = (NS + 7) / 8;
 #pragma unroll
-        for (int slot = 0; slot < 13; ++slot) slot_work(slot);
+        for (int slot = 0; slot < NS8; ++slot) slot_work(slot);
 #pragma unroll
-        for (int slot = 13; slot < 26; ++slot) slot_work(slot);
+        for (int slot = NS8; slot < 2 * NS8; ++slot) slot_work(slot);
 #pragma unroll
-        for (int slot = 26; slot < 39; ++slot) slot_work(slot);
+        for (int slot = 2 * NS8; slot < 3 * NS8; ++slot) slot_work(slot);
 #pragma unroll
-        for (int slot = 39; slot < NS; ++slot) slot_work(slot);
-        static_assert(NS == 52, "slot loops cover 52 slots");
+        for (int slot = 3 * NS8; slot < 4 * NS8; ++slot) slot_work(slot);
+#pragma unroll
+        for (int slot = 4 * NS8; slot < 5 * NS8; ++slot) slot_work(slot);
+#pragma unroll
+        for (int slot = 5 * NS8; slot < 6 * NS8; ++slot) slot_work(slot);
+#pragma unroll
+        for (int slot = 6 * NS8; slot < 7 * NS8; ++slot) slot_work(slot);
+#pragma unroll
+        for (int slot = 7 * NS8; slot < NS; ++slot) slot_work(slot);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(sc[nb]));
