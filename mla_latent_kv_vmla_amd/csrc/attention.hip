@@ -114,12 +114,20 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 #endif
 constexpr int kAhead = VMLA_FRAG_AHEAD;  // LDS fragment reads in flight ahead of their MFMA
 
+// Maximum of two scores in the IEEE 754-2019 sense (a NaN operand gives NaN).
+// fmaxf must first quiet a signalling NaN, so for operands the compiler cannot
+// prove canonical (copies out of the accumulators) it adds a v_max_f32 x, x
+// per operand; this form needs none, and chains of it issue as
+// v_maximum3_f32, two new operands per instruction.  A NaN score reaches the
+// output through its exponential either way.
+__device__ inline float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max and sum over the lane pair (l, l ^ 32) that shares one query row: one
 // v_permlane32_swap exchanges the two half-waves, and combining both of its
 // results gives the pair's value in either lane.
 __device__ inline float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return smax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float pair_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -503,7 +511,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
         for (int nb = 0; nb < NB; ++nb) {
           float m = sc[nb][0];
 #pragma unroll
-          for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, sc[nb][rr]);
+          for (int rr = 1; rr < 16; ++rr) m = smax(m, sc[nb][rr]);
           mx[nb] = pair_max(m) + (FOLD ? m_fold[nb] : 0.f);  // the row max of s itself
           need[nb] = mx[nb] > m_run[nb] + kRescaleSlack;
           any_need |= need[nb];
@@ -968,7 +976,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       const int nb = q >> 1, r0 = 8 * (q & 1);
       float m = r0 ? mloc[nb] : d[nb][0];
 #pragma unroll
-      for (int rr = (r0 ? 0 : 1); rr < 8; ++rr) m = fmaxf(m, d[nb][r0 + rr]);
+      for (int rr = (r0 ? 0 : 1); rr < 8; ++rr) m = smax(m, d[nb][r0 + rr]);
       mloc[nb] = m;
     };
     auto cmp_item = [&](int nb) __attribute__((always_inline)) {
