@@ -94,7 +94,7 @@ template <typename T> struct FlashArgs {
   T* out;                   // row r of stream s: out + (s/heads)*out_so + (s%heads)*out_sh + r*out_rs
   long out_so, out_sh, out_rs;
   int heads;
-  float* part_o;            // [2G][kAttnMaxRows][DV]
+  float* part_o;            // [2G][kAttnMaxRows][DV] of PartT<T> (normalised partial outputs)
   float* part_ml;           // [2G][kAttnMaxRows][2]
   int len0, len1, tiles0;   // keys per segment, key tiles of segment 0
   int R, RB, KT, S, G;      // rows per stream, row blocks per stream, key tiles, streams, workgroups
@@ -121,6 +121,24 @@ constexpr int kAhead = VMLA_FRAG_AHEAD;  // LDS fragment reads in flight ahead o
 // v_maximum3_f32, two new operands per instruction.  A NaN score reaches the
 // output through its exponential either way.
 __device__ inline float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Split-KV partial outputs are stored normalised, O / l: a convex combination
+// of value rows.  With 16-bit storage the values are fp16 copies already and
+// the result is rounded to bf16, so the partials are fp16 (half the traffic
+// of the stores and of the combine's reads); fp32 storage keeps fp32.
+template <typename T> using PartT = typename std::conditional<sizeof(T) == 2, f16, float>::type;
+template <typename T> __device__ inline void store_part4(PartT<T>* dst, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) *reinterpret_cast<f16x4*>(dst) = f16x4{(f16)a, (f16)b, (f16)c, (f16)d};
+  else *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
+}
+template <typename T> __device__ inline f32x4 load_part4(const PartT<T>* src) {
+  if constexpr (sizeof(T) == 2) {
+    const f16x4 h = *reinterpret_cast<const f16x4*>(src);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  } else {
+    return *reinterpret_cast<const f32x4*>(src);
+  }
+}
 
 // Max and sum over the lane pair (l, l ^ 32) that shares one query row: one
 // v_permlane32_swap exchanges the two half-waves, and combining both of its
@@ -673,15 +691,16 @@ void flash_attn_kernel(FlashArgs<T> p) {
       } else if (row0 < p.R) {
         const long slot_row =
             (long)(2 * vw + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * RW + 32 * nb + l32;
-        float* po = p.part_o + slot_row * DV;
+        PartT<T>* po = reinterpret_cast<PartT<T>*>(p.part_o) + slot_row * DV;
+        const float inv = 1.f / l_tot;  // >= 1: the piece's first block holds a valid key
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int f = 32 * fb + 8 * q4 + 4 * h32;
             if (f < DV)
-              *reinterpret_cast<f32x4*>(po + f) =
-                  f32x4{o[nb][fb][4 * q4], o[nb][fb][4 * q4 + 1], o[nb][fb][4 * q4 + 2], o[nb][fb][4 * q4 + 3]};
+              store_part4<T>(po + f, o[nb][fb][4 * q4] * inv, o[nb][fb][4 * q4 + 1] * inv, o[nb][fb][4 * q4 + 2] * inv,
+                             o[nb][fb][4 * q4 + 3] * inv);
           }
         if (h32 == 0) {
           p.part_ml[slot_row * 2] = m_run[nb];
@@ -1235,15 +1254,16 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         }
       } else if (row0 < p.R) {
         const long slot_row = (long)(2 * vw + (first_piece ? 0 : 1)) * kAttnMaxRows + wave * RW + 32 * nb + l32;
-        float* po = p.part_o + slot_row * DV;
+        PartT<T>* po = reinterpret_cast<PartT<T>*>(p.part_o) + slot_row * DV;
+        const float inv = 1.f / l_tot;  // >= 1: the piece's first block holds a valid key
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int f = 32 * fb + 8 * q4 + 4 * h32;
             if (f < DV)
-              *reinterpret_cast<f32x4*>(po + f) =
-                  f32x4{o[nb][fb][4 * q4], o[nb][fb][4 * q4 + 1], o[nb][fb][4 * q4 + 2], o[nb][fb][4 * q4 + 3]};
+              store_part4<T>(po + f, o[nb][fb][4 * q4] * inv, o[nb][fb][4 * q4 + 1] * inv, o[nb][fb][4 * q4 + 2] * inv,
+                             o[nb][fb][4 * q4 + 3] * inv);
           }
         if (h32 == 0) {
           p.part_ml[slot_row * 2] = m_run[nb];
@@ -1290,9 +1310,9 @@ __global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < npieces; ++k) {
       const long sr = (k == 0 ? slot0 : 2 * (w0 + k)) * kAttnMaxRows + r;
-      const float sc = __builtin_amdgcn_exp2f(p.part_ml[sr * 2] - M);
-      L += p.part_ml[sr * 2 + 1] * sc;
-      acc += sc * *reinterpret_cast<const f32x4*>(p.part_o + sr * DV + f);
+      const float w = p.part_ml[sr * 2 + 1] * __builtin_amdgcn_exp2f(p.part_ml[sr * 2] - M);  // piece weight l 2^(m-M)
+      L += w;
+      acc += w * load_part4<T>(reinterpret_cast<const PartT<T>*>(p.part_o) + sr * DV + f);
     }
     const float inv = 1.f / L;
     store4(out_s + (long)row * p.out_rs + f, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);

@@ -39,7 +39,7 @@ struct Plan {
   void *qt;      // [B][Nq][nh][D]        absorbed query [W_UK^T q_nope | q_rope] * qscale
   void *olat;    // [B][Nq][nh][dc]       attention output in latent space
   void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV
-  float *part_o; // [2G][kAttnMaxRows][dc] unnormalised partial outputs
+  float *part_o; // [2G][kAttnMaxRows][dc] normalised partial outputs (fp16 for 16-bit storage, else fp32)
   float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
   void *vtiles;  // pre-pass tiles of the visible keys (per call): fp16 key tiles for bf16, value images for fp32
   void *assembled;  // rope_at_use: the visible cache rows with k_r rotated at local coordinates
