@@ -1296,9 +1296,11 @@ __global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
   const int npieces = (int)(w1 - w0 + 1);
   const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
   T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
-  constexpr int Q = DV / 4;  // float4 columns per row
+  constexpr int CW = sizeof(PartT<T>) == 2 ? 8 : 4;  // columns per task: one 16-byte partial load per piece
+  static_assert(DV % CW == 0, "whole column groups");
+  constexpr int Q = DV / CW;  // column groups per row
   for (int task = threadIdx.x; task < SLICE * Q; task += 256) {
-    const int r = r0 + task / Q, f = (task % Q) * 4;
+    const int r = r0 + task / Q, f = (task % Q) * CW;
     const int row = rb * ROWS + r;
     if (row >= p.R) continue;
     float M = -__builtin_huge_valf();
@@ -1307,15 +1309,20 @@ __global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
       M = fmaxf(M, p.part_ml[sr * 2]);
     }
     float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[CW / 4] = {};
     for (int k = 0; k < npieces; ++k) {
       const long sr = (k == 0 ? slot0 : 2 * (w0 + k)) * kAttnMaxRows + r;
       const float w = p.part_ml[sr * 2 + 1] * __builtin_amdgcn_exp2f(p.part_ml[sr * 2] - M);  // piece weight l 2^(m-M)
       L += w;
-      acc += w * load_part4<T>(reinterpret_cast<const PartT<T>*>(p.part_o) + sr * DV + f);
+      const PartT<T>* src = reinterpret_cast<const PartT<T>*>(p.part_o) + sr * DV + f;
+#pragma unroll
+      for (int c = 0; c < CW / 4; ++c) acc[c] += w * load_part4<T>(src + 4 * c);
     }
     const float inv = 1.f / L;
-    store4(out_s + (long)row * p.out_rs + f, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+#pragma unroll
+    for (int c = 0; c < CW / 4; ++c)
+      store4(out_s + (long)row * p.out_rs + f + 4 * c, acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv,
+             acc[c][3] * inv);
   }
 }
 
