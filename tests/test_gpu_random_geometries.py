@@ -25,7 +25,7 @@ from mla_latent_kv_vmla_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 12
+N_CASES = 24
 
 
 def _draw(i):
