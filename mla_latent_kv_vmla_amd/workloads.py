@@ -56,6 +56,7 @@ class LayerGeometry:
     prefill_chunks: int = 0  # seeded appends before the measured attend
     sink_frames: int = 0     # pinned sink frames ahead of the window (long-horizon cache)
     rope_at_use: bool = False  # GPU layout choice: store k_r un-rotated, rotate per call (implied by sinks)
+    rope_freqs: tuple = None   # explicit omega per rotary pair (axis order t, h, w); None: the default table
 
     @property
     def head_dim(self) -> int:

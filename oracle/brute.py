@@ -25,9 +25,15 @@ def _freq(pairs, theta):
     return out
 
 
-def _rotate(vec, coord, pairs, theta):
-    """vec: list of 2P floats; coord: (t, h, w)."""
-    freqs = _freq(pairs, theta)
+def _table(g):
+    """The geometry's explicit rotary table (rope_freqs) if it has one, else the
+    default per-axis spectrum."""
+    t = getattr(g, "rope_freqs", None)
+    return [float(v) for v in t] if t is not None else _freq(g.rope_pairs, g.rope_theta)
+
+
+def _rotate(vec, coord, pairs, freqs):
+    """vec: list of 2P floats; coord: (t, h, w); freqs: omega per pair."""
     axis = [a for a, p in enumerate(pairs) for _ in range(p)]
     out = []
     for p, om in enumerate(freqs):
@@ -69,7 +75,7 @@ def attend(g, wts, history, n, chunk_x, key_order=None):
     K, V = [], []
     for xj, pj in zip(keys_x, keys_pos):
         c = _mat_vec(w_dkv, xj)
-        kr = _rotate(_mat_vec(w_kr, xj), pj, g.rope_pairs, g.rope_theta)
+        kr = _rotate(_mat_vec(w_kr, xj), pj, g.rope_pairs, _table(g))
         K.append([_mat_vec(w_uk[h], c) + kr for h in range(g.n_heads)])
         V.append([_mat_vec(w_uv[h], c) for h in range(g.n_heads)])
 
@@ -82,7 +88,7 @@ def attend(g, wts, history, n, chunk_x, key_order=None):
         o = []
         for h in range(g.n_heads):
             qh = qall[h * dh:(h + 1) * dh]
-            q = qh[:g.d_nope] + _rotate(qh[g.d_nope:], pos, g.rope_pairs, g.rope_theta)
+            q = qh[:g.d_nope] + _rotate(qh[g.d_nope:], pos, g.rope_pairs, _table(g))
             s = [sum(q[d] * K[j][h][d] for d in range(dh)) / math.sqrt(dh) for j in range(len(K))]
             m = max(s)
             e = [math.exp(v - m) for v in s]
@@ -114,7 +120,7 @@ def attend_dense(g, wts, history, n, chunk_x):
     K, V = [], []
     for xj, pj in zip(keys_x, keys_pos):
         kall, vall = _mat_vec(w_k, xj), _mat_vec(w_v, xj)
-        K.append([_rotate(kall[h * dh:(h + 1) * dh], pj, g.rope_pairs, g.rope_theta) for h in range(g.n_heads)])
+        K.append([_rotate(kall[h * dh:(h + 1) * dh], pj, g.rope_pairs, _table(g)) for h in range(g.n_heads)])
         V.append([vall[h * g.d_v:(h + 1) * g.d_v] for h in range(g.n_heads)])
     out = []
     for i, xi in enumerate(tolist(chunk_x)):
@@ -122,7 +128,7 @@ def attend_dense(g, wts, history, n, chunk_x):
         qall = _mat_vec(w_q, xi)
         o = []
         for h in range(g.n_heads):
-            q = _rotate(qall[h * dh:(h + 1) * dh], pos, g.rope_pairs, g.rope_theta)
+            q = _rotate(qall[h * dh:(h + 1) * dh], pos, g.rope_pairs, _table(g))
             s = [sum(q[d] * K[j][h][d] for d in range(dh)) / math.sqrt(dh) for j in range(len(K))]
             m = max(s)
             e = [math.exp(v - m) for v in s]

@@ -35,8 +35,10 @@ Readings of points the text leaves open (each is a reading, not a page fact):
   * no biases and no normalisation on c, q or k (none is mentioned);
   * softmax scale 1/sqrt(d_nope + d_r);
   * rotary bands: axis a with p_a pairs uses omega_i = theta^(-2i / (2 p_a)),
-    i = 0..p_a-1 (the standard per-axis RoPE spectrum; "highest-frequency
-    bands" read as the leading bands of each axis);
+    i = 0..p_a-1 (the standard per-axis RoPE spectrum; the high-frequency
+    bands read as the leading bands of each axis), unless the geometry carries
+    an explicit table (rope_freqs), e.g. backbone_band_frequencies: the leading
+    bands of a dense backbone's wider per-axis spectrum;
   * "complex pairs" are adjacent channels (2p, 2p+1), rotated counter-clockwise
     (multiplication by e^{i angle}).
 """
@@ -53,6 +55,33 @@ def rope_frequencies(pairs: tuple, theta: float) -> np.ndarray:
         i = np.arange(p, dtype=np.float64)
         out.append(np.power(float(theta), -2.0 * i / (2.0 * p)) if p > 0 else np.zeros(0))
     return np.concatenate(out)
+
+
+def backbone_band_frequencies(pairs: tuple, axis_dims: tuple, theta: float) -> np.ndarray:
+    """omega per complex pair when the decoupled key takes the highest-frequency
+    bands of a dense backbone's per-axis rotary spectrum (sections 3.2 and 4.1
+    allocate the decoupled key's pairs across the t, h, w axes on the
+    high-frequency bands of each axis, as the backbone does).  Axis a of the
+    backbone rotates axis_dims[a] channels with omega_i = theta^(-2i/axis_dims[a]),
+    i = 0, 1, ...; the key's p_a pairs on that axis are the first p_a of them.
+    With axis_dims = 2 * pairs this is rope_frequencies(pairs, theta)."""
+    out = []
+    for p, d in zip(pairs, axis_dims):
+        assert 0 <= p <= d // 2
+        i = np.arange(p, dtype=np.float64)
+        out.append(np.power(float(theta), -2.0 * i / float(d)))
+    return np.concatenate(out)
+
+
+def frequencies(g) -> np.ndarray:
+    """The rotary table of a geometry: its explicit per-pair table `rope_freqs`
+    when it carries one (axis order t, h, w), else rope_frequencies."""
+    table = getattr(g, "rope_freqs", None)
+    if table is not None:
+        table = np.asarray(table, dtype=np.float64)
+        assert table.shape == (sum(g.rope_pairs),)
+        return table
+    return rope_frequencies(g.rope_pairs, g.rope_theta)
 
 
 def pair_axes(pairs: tuple) -> np.ndarray:
@@ -125,7 +154,7 @@ def _assemble(g, wts, history, n, chunk_x, query_tokens, dtype):
     xk = [f(history[fr]).reshape(T, g.hidden) for fr in cached]
     xk.append(f(chunk_x).reshape(g.chunk_frames * T, g.hidden))
     xk = np.concatenate(xk, axis=0)
-    freqs = rope_frequencies(g.rope_pairs, g.rope_theta)
+    freqs = frequencies(g)
     local = np.arange(len(cached) + len(chunk))  # local temporal coordinate of each visible frame
 
     A = _Assembled()
@@ -233,7 +262,7 @@ def chunk_latents(g, wts, x, frame0: int, dtype=np.float64):
     nfr = x.shape[0] // T
     c, kr_hat = latents(x, np.asarray(wts.w_dkv, dtype=dtype), np.asarray(wts.w_kr, dtype=dtype))
     coords = token_coordinates(np.arange(frame0, frame0 + nfr), g.grid_h, g.grid_w)
-    kr = rope_rotate(kr_hat, coords, g.rope_pairs, rope_frequencies(g.rope_pairs, g.rope_theta))
+    kr = rope_rotate(kr_hat, coords, g.rope_pairs, frequencies(g))
     return np.concatenate([c, kr], axis=1)
 
 
@@ -250,7 +279,7 @@ def attend_dense(g, wts, history, n: int, chunk_x, query_tokens=None, dtype=np.f
     xk = np.concatenate([f(history[fr]).reshape(T, g.hidden) for fr in cached]
                         + [f(chunk_x).reshape(-1, g.hidden)], axis=0)
     dh = g.head_dim
-    freqs = rope_frequencies(g.rope_pairs, g.rope_theta)
+    freqs = frequencies(g)
     local = np.arange(len(cached) + len(chunk))
     kc = token_coordinates(local, g.grid_h, g.grid_w)
     k = rope_rotate((xk @ f(wts.w_k).T).reshape(-1, g.n_heads, dh), kc, g.rope_pairs, freqs)

@@ -16,7 +16,8 @@ import pytest
 from oracle import brute, mla, ring, sizes
 from mla_latent_kv_vmla_amd import workloads as wl
 
-GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+GOLD = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
 
 
 def gv(k):
@@ -79,6 +80,45 @@ def test_rope_frequencies_closed_form():
     np.testing.assert_allclose(f, [1.0, 0.1, 0.01, 0.001] + h6 + h6, rtol=1e-14)
     np.testing.assert_allclose(mla.rope_frequencies((1, 1, 2), 1e4), [1.0, 1.0, 1.0, 0.01], rtol=1e-14)
     assert list(mla.pair_axes((1, 1, 2))) == [0, 1, 2, 2]
+
+
+def test_backbone_band_frequencies_closed_form():
+    """Leading bands of a wider per-axis spectrum, written out by hand: axis
+    dims (44, 42, 42) at theta = 1e4 give omega = 10^(-8i/44) on t and
+    10^(-8i/42) on h and w."""
+    f = mla.backbone_band_frequencies((6, 5, 5), (44, 42, 42), 1e4)
+    t = [10 ** (-8 * i / 44) for i in range(6)]
+    hw = [10 ** (-8 * i / 42) for i in range(5)]
+    np.testing.assert_allclose(f, t + hw + hw, rtol=1e-14)
+    np.testing.assert_allclose(f[:2], [1.0, 0.657933224657568], rtol=1e-14)
+    # an axis spectrum exactly as wide as the key's pairs is the default table
+    np.testing.assert_array_equal(mla.backbone_band_frequencies((4, 6, 6), (8, 12, 12), 1e4),
+                                  mla.rope_frequencies((4, 6, 6), 1e4))
+    # the golden tables the GPU tests pass to the library were written from this function
+    gold = json.load(open(os.path.join(GOLDEN, "rope_bands.json")))
+    for key, table in gold["tables"].items():
+        pairs = tuple(int(v) for v in key.split(","))
+        np.testing.assert_allclose(table, mla.backbone_band_frequencies(pairs, tuple(gold["axis_dims"]),
+                                                                        gold["theta"]), rtol=1e-15)
+
+
+def test_explicit_rope_table_is_used_everywhere():
+    """A geometry's explicit table: equal to the default when it is the default
+    table, and followed identically by the numpy oracle and the brute force
+    (complex rotation per pair) when it is not."""
+    g = wl.TINY
+    for n in (0, 3):
+        w, hist, chunk = _tiny_inputs(n)
+        base = mla.attend(g, w, hist, n, chunk)
+        same = mla.attend(g.replace(rope_freqs=tuple(mla.rope_frequencies(g.rope_pairs, g.rope_theta))), w, hist, n,
+                          chunk)
+        np.testing.assert_array_equal(same, base)
+        gt = g.replace(rope_freqs=(0.9, 0.35, 0.6, 0.05))
+        ref = mla.attend(gt, w, hist, n, chunk)
+        bf = np.asarray(brute.attend(gt, w, hist, n, chunk))
+        np.testing.assert_allclose(ref, bf, rtol=1e-11, atol=1e-13)
+        if n:
+            assert np.abs(ref - base).max() > 1e-6  # the table changes the result
 
 
 def test_rope_norm_identity_and_relative_invariance():
