@@ -123,14 +123,34 @@ typedef struct vmla_ctx vmla_ctx; /* opaque; holds host-side metadata only */
 
 /* Bytes of the ring cache: batch * (sink_frames + window_frames) * T *
  * (d_c + d_rope) elements.  Row (slot*T + s) of stream b holds [c (d_c) | k_r
- * (d_rope)] of token s of the frame in that slot, k_r rotated with the absolute
- * frame index (rope_at_use = 0) or un-rotated (rope_at_use = 1); frame f lives
- * in slot f if f < S, else in slot S + (f - S) % window_frames.  Occupied slots
- * are always 0..(visible frames - 1).  Returns 0 for an invalid config. */
+ * (d_rope)] of token s of the frame in that slot -- the per-token latent entry
+ * of paper section 3.1 (content latent plus the head-shared decoupled key of
+ * section 3.2; 224 scalars at the Wan-1.3B widths) -- k_r rotated with the
+ * absolute frame index (rope_at_use = 0) or un-rotated (rope_at_use = 1, the
+ * form appendix D.5 caches).  Frame f lives in slot f if f < S, else in slot
+ * S + (f - S) % window_frames (the sink-plus-FIFO window of appendix D.4).
+ * Occupied slots are always 0..(visible frames - 1).  Returns 0 for an invalid
+ * config. */
 VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg);
 
-/* Bytes of scratch device memory a ctx needs (chunk latents, absorbed queries,
- * latent outputs, partial softmax states).  Returns 0 for an invalid config. */
+/* Bytes of device memory a ctx needs beside the cache: a persistent part
+ * written by vmla_prepare (the range flag and the weights in the activation
+ * type, below) and the per-call buffers of vmla_attend (chunk latents, c^Q,
+ * absorbed queries, latent outputs, per-head outputs, partial softmax states,
+ * key tiles).  Returns 0 for an invalid config.
+ *
+ * Operand types.  x, out, the cache and the caller's weights have the config's
+ * dtype.  What the layer computes between x and out (c^Q, absorbed queries,
+ * attention outputs, per-head outputs) is held in the activation type: fp16
+ * for bf16 storage (same 16 bits, 11 significant bits instead of 8, same MFMA
+ * rate on gfx950), fp32 for fp32 storage; so are the absorbed query weight and
+ * the copies of W_UQ, W_UV and W_O that vmla_prepare writes, and the fp16 key
+ * tiles the attention kernel reads the cached rows from.  bf16 values within
+ * fp16's normal range (2^-14 .. 65504 in magnitude) convert exactly; smaller
+ * ones become fp16 subnormals (absolute error below 2^-25).  A finite value
+ * beyond +-65504 is saturated to +-65504 -- the result then differs from
+ * full-range arithmetic -- and sets bit 0 of the ctx's range flag
+ * (vmla_range_flags).  NaN and infinite values pass through unchanged. */
 VMLA_API size_t vmla_workspace_bytes(const vmla_config* cfg);
 
 /* Create a ctx over caller-owned memory.  cache: vmla_cache_bytes(cfg) bytes;
@@ -138,26 +158,50 @@ VMLA_API size_t vmla_workspace_bytes(const vmla_config* cfg);
  * anything).  workspace: vmla_workspace_bytes(cfg) bytes.  rope_freqs: host
  * array of d_rope/2 floats giving omega per complex pair (axis order t, h, w),
  * copied at create; NULL selects theta^(-2i/(2p_a)), i = 0..p_a-1, per axis.
- * Makes no HIP call.  On success *out is a new ctx with 0 frames appended. */
+ * A non-finite entry -> VMLA_ERR_ARG.  Makes no HIP call.  On success *out is
+ * a new ctx with 0 frames appended, not yet prepared. */
 VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* cache,
                          void* workspace, const float* rope_freqs, vmla_ctx** out);
 
-/* Append one chunk: x is [batch, chunk_frames*T, hidden].  Computes
- * [c | RoPE(k^)] for frames n..n+C-1 (n = frames appended so far; the temporal
- * coordinate is the absolute frame index) and writes them into ring slots
- * (n+i) % window_frames, evicting the frames that held them (oldest first,
- * appendix D.4).  Then n += C on the host. */
+/* Enqueue the one-time set-up of a ctx: clear its range flag and write, into
+ * the persistent part of the workspace, the weights in the activation type:
+ *   absorbed query weight, per head h, the [d_c + d_rope, d_q] block
+ *     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope]  (qscale = log2(e)/sqrt(d_h)),
+ *   so one GEMM from c^Q gives the absorbed query q~_h = W_UK^h^T q^nope_h
+ *   and the un-rotated q^R_h of the MLA absorption (paper section 3.3);
+ *   qscale * W_UQ, W_UV and W_O.
+ * Must follow vmla_create before any vmla_attend*, vmla_expand or
+ * vmla_range_flags on the ctx (else those return VMLA_ERR_STATE); appends and
+ * vmla_compress do not need it.  Since it copies the weights, the caller's
+ * weights must not change afterwards (call it again if they do). */
+VMLA_API int vmla_prepare(vmla_ctx* ctx, hipStream_t stream);
+
+/* Read and clear the ctx's range flag: waits for `stream`, stores the flag in
+ * *flags (bit 0 set: since vmla_prepare or the last read, some fp16 operand
+ * copy -- a cached or chunk latent element, c^Q, an absorbed query, a per-head
+ * output, an expanded key or value, a prepared weight -- had a finite value
+ * beyond +-65504 and was saturated), then enqueues the clear on `stream`. */
+VMLA_API int vmla_range_flags(vmla_ctx* ctx, uint32_t* flags, hipStream_t stream);
+
+/* Append one chunk: x is [batch, chunk_frames*T, hidden].  Computes the cache
+ * rows [c | k_r] of frames f = n..n+C-1 (n = frames appended so far): c = W_DKV
+ * x, k_r = W_KR x rotated by 3D-RoPE at the absolute frame index (un-rotated
+ * with rope_at_use), rounded to the storage type, and writes frame f into slot
+ * f if f < S, else slot S + (f - S) % window_frames, evicting the frame that
+ * held it (oldest first; paper sections 3.1-3.2, appendix D.4).  Then n += C
+ * on the host. */
 VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stream);
 
 /* Attend one chunk: x is [batch, C*T, hidden], out is [batch, C*T, hidden].
- * Every query token of frames n..n+C-1 attends, in every head, to all cached
- * frames [max(0, n-W), n) and all tokens of the chunk itself (chunk-causal,
- * appendix D.4), followed by W_UV and W_O.  Leaves the cache and n unchanged:
+ * Every query token of frames n..n+C-1 attends, in every head, to all visible
+ * cached frames (sinks [0, min(n, S)) and the window [max(S, n-W), n)) and all
+ * tokens of the chunk itself (chunk-causal, appendix D.4), followed by W_UV and
+ * W_O (paper section 3.3, absorbed form).  Leaves the cache and n unchanged:
  * the frozen-cache denoising steps of a rollout call this repeatedly, then
- * append the final step's x.  With bf16 storage the attention kernel takes its
- * scores and values from fp16 copies of the cached rows and of the absorbed
- * queries; the copies are exact while every element stays below 65504 in
- * magnitude (larger elements become infinite, and the outputs NaN). */
+ * append the final step's x.  Needs vmla_prepare.  With bf16 storage the scores
+ * and the value sum run on fp16 operands: fp16 copies of the visible cached
+ * rows (saturating beyond +-65504, see the operand types above) and the fp16
+ * absorbed queries. */
 VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream);
 
 /* Same as vmla_attend, and additionally records attn_start on the stream right
@@ -169,14 +213,18 @@ VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEv
                                   hipEvent_t attn_stop, hipStream_t stream);
 
 /* Test hook: compute the cache rows [c | RoPE(k^)] of x ([batch, C*T, hidden])
- * as frames frame0..frame0+C-1 into latents_out ([batch, C*T, d_c+d_rope]),
- * without touching the cache or n.  frame0 >= 0 else VMLA_ERR_ARG. */
+ * as frames frame0..frame0+C-1 into latents_out ([batch, C*T, d_c+d_rope]) --
+ * the row vmla_compress_append writes (paper sections 3.1-3.2), always rotated,
+ * at the absolute coordinate frame0 + i -- without touching the cache or n.
+ * frame0 >= 0 else VMLA_ERR_ARG. */
 VMLA_API int vmla_compress(vmla_ctx* ctx, const void* x, int64_t frame0, void* latents_out,
                            hipStream_t stream);
 
-/* Host metadata: frames appended n, the first window frame min(n, max(S, n-W))
- * (= max(0, n-W) without sinks), and the number of visible cached frames
- * min(n, S) + max(0, min(n - S, W)).  Any output pointer may be NULL. */
+/* Host metadata of the sliding window (appendix D.4: sink frames ahead of a
+ * FIFO window with oldest-frame eviction): frames appended n, the first window
+ * frame min(n, max(S, n-W)) (= max(0, n-W) without sinks), and the number of
+ * visible cached frames min(n, S) + max(0, min(n - S, W)).  Any output pointer
+ * may be NULL. */
 VMLA_API int vmla_cache_state(const vmla_ctx* ctx, int64_t* frames_appended,
                               int64_t* first_valid_frame, int32_t* n_valid_frames);
 
@@ -194,12 +242,13 @@ VMLA_API void vmla_destroy(vmla_ctx* ctx);
  * are the clip's frame indices 0..window_frames-1.  Key tiles above the block
  * diagonal are skipped.
  * vmla_clip_workspace_bytes: bytes of the caller-owned clip workspace (the
- *   per-call buffers of vmla_attend sized for window_frames*T query tokens);
+ *   per-call buffers of vmla_attend sized for window_frames*T query tokens; the
+ *   prepared weights and the range flag stay in the ctx's workspace);
  *   0 if the config is invalid or batch * window_frames * T exceeds 64 * 65,535
  *   (launch-grid limit; vmla_attend_clip then returns VMLA_ERR_CONFIG).
  * vmla_attend_clip: x and out are [batch, window_frames*T, hidden]; same rules
- *   as vmla_attend (window_frames must be a multiple of chunk_frames for whole
- *   blocks; a shorter last block is allowed).
+ *   as vmla_attend, including vmla_prepare (a window_frames not divisible by
+ *   chunk_frames gives a shorter last block).
  */
 VMLA_API size_t vmla_clip_workspace_bytes(const vmla_config* cfg);
 VMLA_API int vmla_attend_clip(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out,
@@ -222,9 +271,10 @@ VMLA_API int vmla_attend_clip_profiled(vmla_ctx* ctx, const void* x, void* clip_
  *   vmla_dense_*, plus the chunk's keys/values, queries, outputs and partial
  *   states: ~260 MB at the Wan-1.3B layer).  0 if unsupported or invalid.
  * vmla_expand: per stream, head h and valid ring key j,
- *   K_h[j] = [W_UK^h c_j ; k_r_j] and V_h[j] = W_UV^h c_j into `expanded`,
- *   from the ring as it stands (n frames).  Leaves the cache and n unchanged.
- * vmla_attend_expanded: attend one chunk (x, out as vmla_attend) with per-head
+ *   K_h[j] = [W_UK^h c_j ; k_r_j] and V_h[j] = W_UV^h c_j into `expanded` (fp16,
+ *   saturating as above), from the ring as it stands (n frames).  Leaves the
+ *   cache and n unchanged.  Needs vmla_prepare.
+ * vmla_attend_expanded: attend one chunk (x, out as vmla_attend) with fp16 per-head
  *   queries [q_nope ; RoPE(q_rope)] against the expanded window and the
  *   chunk's own up-projected keys/values, then W_O.  `expanded` must be the
  *   buffer of the last vmla_expand, made after the last append (else
@@ -242,8 +292,8 @@ VMLA_API int vmla_attend_expanded_profiled(vmla_ctx* ctx, const void* expanded, 
 /*
  * Dense per-head baseline (paper section 1 and appendix C.1: the layer VideoMLA
  * replaces, whose cache holds every head's key and value, n_heads*2*d_h scalars
- * per token).  Same chunk-causal window, ring eviction and 3D-RoPE as the
- * latent layer; per head h and token x:
+ * per token, 16-bit).  Same chunk-causal window, ring eviction and 3D-RoPE as
+ * the latent layer; per head h and token x:
  *   q_h = RoPE(W_Q^h x), k_h = RoPE(W_K^h x) (all d_h channels rotated, pairs
  *   (2p, 2p+1), axis order t, h, w), v_h = W_V^h x,
  *   o_h = softmax(q_h k_h^T / sqrt(d_h)) v_h, out = W_O [o_1; ...; o_H].
@@ -259,14 +309,15 @@ VMLA_API int vmla_attend_expanded_profiled(vmla_ctx* ctx, const void* expanded, 
  *
  * Cache layout (vmla_dense_cache_bytes), P = window_frames*T rounded up to a
  * multiple of 128:
- *   keys   [batch][n_heads][P][d_rope] bf16, rotated with the absolute frame index;
+ *   keys   [batch][n_heads][P][d_rope] fp16, rotated with the absolute frame index;
  *   values [batch][n_heads][d_v][P] fp16, transposed: the value of ring key j
  *          (frame f in slot f % window_frames, key j = slot*T + s) sits in
  *          column j with bits 2 and 3 of j swapped; columns past the valid
  *          keys (up to the next multiple of 128) are kept at zero by the library.
- * The values are stored as fp16 so the value product runs on fp16 operands
- * (the bf16 rounding of probabilities near 1 is too coarse, see the latent
- * path); the cache size equals the bf16 one.
+ * Keys and values are stored as fp16 (the cache size equals a bf16 one), so
+ * both products run on fp16 operands with the fp16 queries; conversions
+ * saturate beyond +-65504 and set the dense ctx's range flag.  The attention
+ * output is fp16 and W_O runs on the fp16 copy vmla_dense_prepare writes.
  */
 typedef struct vmla_dense_weights {
   const void *w_q, *w_k, *w_v, *w_o;
@@ -285,6 +336,15 @@ VMLA_API size_t vmla_dense_workspace_bytes(const vmla_config* cfg);
  * (rope_freqs: d_rope/2 floats or NULL for theta^(-2i/(2p_a)) per axis). */
 VMLA_API int vmla_dense_create(const vmla_config* cfg, const vmla_dense_weights* w, void* cache,
                                void* workspace, const float* rope_freqs, vmla_dense_ctx** out);
+
+/* One-time set-up of a dense ctx: clear its range flag and write the fp16 copy
+ * of W_O into the workspace.  Required before vmla_dense_append,
+ * vmla_dense_attend* and vmla_dense_range_flags (else VMLA_ERR_STATE). */
+VMLA_API int vmla_dense_prepare(vmla_dense_ctx* ctx, hipStream_t stream);
+
+/* As vmla_range_flags, for a dense ctx (bit 0: a key, value, query or W_O
+ * element was saturated to +-65504). */
+VMLA_API int vmla_dense_range_flags(vmla_dense_ctx* ctx, uint32_t* flags, hipStream_t stream);
 
 /* Append one chunk (x [batch, C*T, hidden]): keys and values of frames
  * n..n+C-1 into their ring slots, evicting the oldest frames; n += C. */

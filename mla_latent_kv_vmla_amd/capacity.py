@@ -30,20 +30,26 @@ def latent_cache_bytes(g, batch: int = 1, es: int = 2) -> int:
 
 
 def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
-                           workgroups: int = DEFAULT_WORKGROUPS) -> int:
-    """Mirror of the library's latent workspace layout for `batch` streams."""
+                           workgroups: int = DEFAULT_WORKGROUPS, part: str = "total") -> int:
+    """Mirror of the library's latent workspace layout for `batch` streams:
+    part = "persistent" (range flag and the prepared weights, per layer),
+    "per_call" (the buffers of one attend) or "total".  The activation type has
+    the storage type's width (fp16 for bf16, fp32 for fp32)."""
     M = batch * g.n_q
-    D, nh = g.d_c + g.d_rope, g.n_heads
+    D, nh, dh = g.d_c + g.d_rope, g.n_heads, g.d_nope + g.d_rope
     dcp = (g.d_c + 31) // 32 * 32
     tiles = (-(-(g.sink_frames + g.window_frames) * g.tokens_per_frame // key_tile)
              + -(-g.n_q // key_tile))
-    parts = [M * D * es, M * g.d_q * es, M * nh * g.d_nope * es, M * nh * D * es, M * nh * g.d_c * es,
-             M * nh * g.d_v * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * 4, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
-             # pre-pass tiles: fp16 key tiles (16-bit storage), transposed value images (fp32)
-             batch * tiles * key_tile * D * 2 if es == 2 else batch * tiles * dcp * (key_tile + 16 // es) * es,
-             batch * (g.sink_frames + g.window_frames) * g.tokens_per_frame * D * es if g.rope_at_use or g.sink_frames
-             else 0]
-    return sum(_al(x) for x in parts)
+    persistent = [4, nh * D * g.d_q * es, nh * dh * g.d_q * es, nh * g.d_v * g.d_c * es, g.hidden * nh * g.d_v * es]
+    per_call = [M * D * es, M * g.d_q * es, M * nh * D * es, M * nh * g.d_c * es,
+                M * nh * g.d_v * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
+                # pre-pass tiles: fp16 key tiles (16-bit storage), transposed value images (fp32)
+                batch * tiles * key_tile * D * 2 if es == 2 else batch * tiles * dcp * (key_tile + 16 // es) * es,
+                # rotated copy of the visible rows: rotation at use with fp32 storage only
+                batch * (g.sink_frames + g.window_frames) * g.tokens_per_frame * D * es
+                if (g.rope_at_use or g.sink_frames) and es == 4 else 0]
+    a, b = sum(_al(x) for x in persistent), sum(_al(x) for x in per_call)
+    return {"persistent": a, "per_call": b, "total": a + b}[part]
 
 
 def dense_cache_bytes(g, batch: int = 1) -> int:
@@ -52,13 +58,16 @@ def dense_cache_bytes(g, batch: int = 1) -> int:
     return _al(heads * P * g.head_dim * 2) + _al(heads * P * g.d_v * 2)
 
 
-def dense_workspace_bytes(g, batch: int = 1, workgroups: int = DEFAULT_WORKGROUPS) -> int:
+def dense_workspace_bytes(g, batch: int = 1, workgroups: int = DEFAULT_WORKGROUPS, part: str = "total") -> int:
+    """Mirror of the dense workspace: persistent (range flag, fp16 W_O) and per call."""
     S = -(-g.n_q // DENSE_KEY_TILE) * DENSE_KEY_TILE
     heads = batch * g.n_heads
-    parts = [heads * g.n_q * g.head_dim * 2, heads * S * g.head_dim * 2, heads * S * g.d_v * 2,
-             batch * g.n_q * g.n_heads * g.d_v * 2, 2 * workgroups * ATTN_MAX_ROWS * g.d_v * 4,
-             2 * workgroups * ATTN_MAX_ROWS * 2 * 4]
-    return sum(_al(x) for x in parts)
+    persistent = [4, g.hidden * g.n_heads * g.d_v * 2]
+    per_call = [heads * g.n_q * g.head_dim * 2, heads * S * g.head_dim * 2, heads * S * g.d_v * 2,
+                batch * g.n_q * g.n_heads * g.d_v * 2, 2 * workgroups * ATTN_MAX_ROWS * g.d_v * 2,
+                2 * workgroups * ATTN_MAX_ROWS * 2 * 4]
+    a, b = sum(_al(x) for x in persistent), sum(_al(x) for x in per_call)
+    return {"persistent": a, "per_call": b, "total": a + b}[part]
 
 
 def latent_weight_bytes(g, es: int = 2) -> int:
@@ -81,14 +90,19 @@ class Capacity:
 
 def capacity(g, layers: int, budget_bytes: int, dense: bool = False) -> Capacity:
     """Largest batch whose caches (all layers), one layer's per-call buffers and
-    all weights fit in budget_bytes.  Per-call buffers are linear in the batch
-    except the stream-K partial states, which are charged once."""
+    all weights (each layer's own and its prepared copies) fit in budget_bytes.
+    Per-call buffers are linear in the batch except the stream-K partial states,
+    which are charged once."""
     io = 2 * g.n_q * g.hidden * 2  # x and out of one call, per stream
     if dense:
-        cache, fixed = dense_cache_bytes(g) * layers, dense_weight_bytes(g) * layers
+        cache = dense_cache_bytes(g) * layers
+        fixed = (dense_weight_bytes(g) + dense_workspace_bytes(g, 1, part="persistent")) * (layers - 1)
+        fixed += dense_weight_bytes(g)
         ws1, ws2 = dense_workspace_bytes(g, 1), dense_workspace_bytes(g, 2)
     else:
-        cache, fixed = latent_cache_bytes(g) * layers, latent_weight_bytes(g) * layers
+        cache = latent_cache_bytes(g) * layers
+        fixed = (latent_weight_bytes(g) + latent_workspace_bytes(g, 1, part="persistent")) * (layers - 1)
+        fixed += latent_weight_bytes(g)
         ws1, ws2 = latent_workspace_bytes(g, 1), latent_workspace_bytes(g, 2)
     slope = ws2 - ws1
     fixed += ws1 - slope  # the batch-independent part of the workspace

@@ -82,7 +82,7 @@ namespace vmla {
 // a batch stream for latent attention (rows = token*heads + head), a (batch
 // stream, head) pair for dense attention (rows = tokens).
 template <typename T> struct FlashArgs {
-  const T* q;               // row r of stream s: q + s*q_ss + r*D
+  const void* q;            // row r of stream s: q + s*q_ss + r*D (query type: fp16 for 16-bit storage)
   long q_ss;
   const T* key0;            // ring segment: key k of stream s at key0 + s*key_ss0 + k*D
   const T* key1;            // chunk segment
@@ -91,8 +91,16 @@ template <typename T> struct FlashArgs {
   const void* val1;         //   of the chunk segment; or the per-call pre-pass tiles (val0)
   long val_ss0, val_ss1;    // elements per stream
   int val_rs0, val_rs1;     // elements per value row
-  T* out;                   // row r of stream s: out + (s/heads)*out_so + (s%heads)*out_sh + r*out_rs
-  long out_so, out_sh, out_rs;
+  void* out;                // row r of stream s: out + (s/heads)*out_so + (s%heads)*out_sh + r*out_rs
+  long out_so, out_sh, out_rs;  //   (output type = value-operand type: fp16 for 16-bit storage)
+  uint32_t* range_flag;     // latent key-tile pre-pass: raised when a cached element saturates
+  // Rotation at use (latent key-tile pre-pass): with rot_ring, the ring segment
+  // holds k^ un-rotated in channels [rot_dc, D); ring row r (slot r / T, token
+  // r % T) is turned at the local coordinate of its slot's frame (rot_n frames
+  // appended, rot_S sink slots, rot_W window slots) before the fp16 conversion.
+  int rot_ring, rot_dc, rot_S, rot_W;
+  int64_t rot_n;
+  Rope rope;
   int heads;
   float* part_o;            // [2G][kAttnMaxRows][DV] of PartT<T> (normalised partial outputs)
   float* part_ml;           // [2G][kAttnMaxRows][2]
@@ -246,7 +254,10 @@ __global__ __launch_bounds__(256) void latent_value_tiles(FlashArgs<T> p) {
 
 // Pre-pass (latent attention, bf16 storage): fp16 copies of the key tiles.
 // Tile (s, t) is row-major [KTILE][D] without padding; keys past the segment's
-// end repeat its last key (their probabilities are zero).
+// end repeat its last key (their probabilities are zero).  bf16 values in
+// fp16's normal range convert exactly; a finite value beyond +-65504 saturates
+// and raises the range flag.  With rotation at use, the ring rows' k^ channels
+// are turned in fp32 at their local coordinate first (one rounding, to fp16).
 template <typename T, int D, int KTILE>
 __global__ __launch_bounds__(256) void latent_key_tiles(FlashArgs<T> p) {
   static_assert(std::is_same<T, bf16>::value, "the key tiles widen bf16");
@@ -256,18 +267,30 @@ __global__ __launch_bounds__(256) void latent_key_tiles(FlashArgs<T> p) {
   tile_segment<T, KTILE>(p, t, g, kbase, len);
   const T* keys = g ? p.key1 + s * p.key_ss1 : p.key0 + s * p.key_ss0;
   f16* img = reinterpret_cast<f16*>(const_cast<void*>(p.val0)) + ((size_t)s * p.KT + t) * (KTILE * D);
+  bool over = false;
   for (int v = threadIdx.x; v < KTILE * CV; v += 256) {
     const int r = v / CV, c = v % CV;
     const int key = min(kbase + r, len - 1);
     const u32x4 k = ld16(keys + (long)key * D + c * 8);
-    f16x8 h;
+    float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t w = k[e >> 1];
-      h[e] = (f16)((e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16));
+      x[e] = (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
     }
+    if (p.rot_ring && g == 0 && c * 8 >= p.rot_dc) {
+      const int tpf = p.rope.tokens_per_frame;
+      const int64_t tau = local_frame(key / tpf, p.rot_n, p.rot_S, p.rot_W);
+      const int pair0 = (c * 8 - p.rot_dc) >> 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p.rope.rotate2(pair0 + j, tau, key % tpf, x[2 * j], x[2 * j + 1]);
+    }
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = to_f16_sat(x[e], over);
     *reinterpret_cast<f16x8*>(img + r * D + c * 8) = h;
   }
+  raise_range_flag(over, p.range_flag);
 }
 
 // VROWS = false (latent): bf16 storage stages the pre-pass key tiles (val0) and
@@ -427,22 +450,16 @@ void flash_attn_kernel(FlashArgs<T> p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) mask_from[nb] = causal ? row_limit(row0 + 32 * nb + l32) : 0x7fffffff;
 
+    // queries arrive in the score operand type (fp16 for 16-bit storage)
     using QFrag = typename std::conditional<VT_FROM_K, f16x8, typename MF::Frag>::type;
     QFrag qf[NB][NKS];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int qrow = row0 + 32 * nb + l32;
-      const T* qsrc = p.q + s * p.q_ss + (long)qrow * D + KPL * h32;
+      const VT* qsrc = static_cast<const VT*>(p.q) + s * p.q_ss + (long)qrow * D + KPL * h32;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const auto b = qrow < p.R ? MF::load(qsrc + ks * 2 * KPL) : MF::zero();
-        if constexpr (VT_FROM_K) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qf[nb][ks][e] = (f16)(float)b[e];
-        } else {
-          qf[nb][ks] = b;
-        }
-      }
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[nb][ks] = qrow < p.R ? *reinterpret_cast<const QFrag*>(qsrc + ks * 2 * KPL) : QFrag{};
     }
     f32x16 o[NB][NFB];
     float m_run[NB], l_run[NB];
@@ -669,14 +686,14 @@ void flash_attn_kernel(FlashArgs<T> p) {
     }
 
     const bool full = causal || (kt0 == 0 && kt1 == p.KT);
-    T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
+    VT* out_s = static_cast<VT*>(p.out) + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float l_tot = pair_sum(l_run[nb]);
       const int qrow = row0 + 32 * nb + l32;
       if (full) {
         if (qrow < p.R) {
-          T* dst = out_s + (long)qrow * p.out_rs;
+          VT* dst = out_s + (long)qrow * p.out_rs;
           const float inv = 1.f / l_tot;
 #pragma unroll
           for (int fb = 0; fb < NFB; ++fb)
@@ -808,6 +825,7 @@ template <int D, int DV, int KTILE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   using T = bf16;
+  using VT = f16;  // query, value-operand and output type
   using G = TileGeo<T, D, DV, KTILE>;
   constexpr int NW = 4, NB = 2, RW = 64;
   // LDS key tile (16-B chunk c of key row r): four regions of 16 rows (wave w
@@ -905,13 +923,10 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int qrow = row0 + 32 * nb + l32;
-      const T* qsrc = p.q + s * p.q_ss + (long)qrow * D + 8 * h32;
+      const f16* qsrc = static_cast<const f16*>(p.q) + s * p.q_ss + (long)qrow * D + 8 * h32;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 b = qrow < p.R ? *reinterpret_cast<const bf16x8*>(qsrc + 16 * ks) : bf16x8{};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[nb][ks][e] = (f16)(float)b[e];
-      }
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[nb][ks] = qrow < p.R ? *reinterpret_cast<const f16x8*>(qsrc + 16 * ks) : f16x8{};
     }
     f32x16 o[NB][NFB];
     float m_run[NB], l_run[NB];
@@ -1233,14 +1248,14 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     }
 
     const bool full = causal || (kt0 == 0 && kt1 == p.KT);
-    T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
+    VT* out_s = static_cast<VT*>(p.out) + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float l_tot = pair_sum(l_run[nb]);
       const int qrow = row0 + 32 * nb + l32;
       if (full) {
         if (qrow < p.R) {
-          T* dst = out_s + (long)qrow * p.out_rs;
+          VT* dst = out_s + (long)qrow * p.out_rs;
           const float inv = 1.f / l_tot;
 #pragma unroll
           for (int fb = 0; fb < NFB; ++fb)
@@ -1295,7 +1310,7 @@ __global__ __launch_bounds__(256) void flash_attn_combine(FlashArgs<T> p) {
   const long slot0 = 2 * w0 + (start(w0) < i0 ? 1 : 0);
   const int npieces = (int)(w1 - w0 + 1);
   const int s = (int)(unit / p.RB), rb = (int)(unit % p.RB);
-  T* out_s = p.out + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
+  PartT<T>* out_s = static_cast<PartT<T>*>(p.out) + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
   constexpr int CW = sizeof(PartT<T>) == 2 ? 8 : 4;  // columns per task: one 16-byte partial load per piece
   static_assert(DV % CW == 0, "whole column groups");
   constexpr int Q = DV / CW;  // column groups per row
@@ -1395,14 +1410,15 @@ size_t latent_prepass_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, 
 template <typename T>
 static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
   FlashArgs<T> a = {};
-  a.q = static_cast<const T*>(c.qt);
+  a.q = c.qt;
   a.q_ss = (long)c.R * (c.dc + c.dr);
+  a.range_flag = c.range_flag;
   a.key0 = static_cast<const T*>(c.cache);
   a.key1 = static_cast<const T*>(c.stage);
   a.key_ss0 = c.cache_bstride;
   a.key_ss1 = c.stage_bstride;
   a.val0 = c.vtiles;
-  a.out = static_cast<T*>(c.out);
+  a.out = c.out;
   a.out_so = (long)c.R * c.dc;
   a.out_sh = 0;
   a.out_rs = c.dc;
@@ -1415,6 +1431,16 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
   a.S = c.B;
   a.causal_tokens = c.causal_tokens;
   a.row_div = c.R / c.n_stage;  // rows are (token, head) pairs
+  a.rot_ring = c.rot_ring;
+  a.rot_dc = c.dc;
+  a.rot_S = c.rot_S;
+  a.rot_W = c.rot_W;
+  a.rot_n = c.rot_n;
+  a.rope.pairs_t = c.pairs_t;
+  a.rope.pairs_h = c.pairs_h;
+  a.rope.grid_w = c.grid_w;
+  a.rope.tokens_per_frame = c.tokens_per_frame;
+  for (int i = 0; i < kMaxRopePairs; ++i) a.rope.freq[i] = c.freq[i];
   if constexpr (std::is_same<T, float>::value) {
     if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     return hipErrorInvalidValue;
@@ -1440,11 +1466,11 @@ bool dense_attention_supported(DType dt, int dh, int dv) {
 
 hipError_t run_dense_attention(const DenseAttnCall& c, hipStream_t s) {
   if (!dense_attention_supported(DType::BF16, c.dh, c.dv)) return hipErrorInvalidValue;
-  FlashArgs<bf16> a = {};
-  a.q = static_cast<const bf16*>(c.q);
+  FlashArgs<f16> a = {};
+  a.q = c.q;
   a.q_ss = (long)c.Nq * c.dh;
-  a.key0 = static_cast<const bf16*>(c.kring);
-  a.key1 = static_cast<const bf16*>(c.kstage);
+  a.key0 = static_cast<const f16*>(c.kring);
+  a.key1 = static_cast<const f16*>(c.kstage);
   a.key_ss0 = (long)c.ring_stride * c.dh;
   a.key_ss1 = (long)c.stage_stride * c.dh;
   a.val0 = c.vring;
@@ -1453,7 +1479,7 @@ hipError_t run_dense_attention(const DenseAttnCall& c, hipStream_t s) {
   a.val_ss1 = (long)c.dv * c.stage_stride;
   a.val_rs0 = c.ring_stride;
   a.val_rs1 = c.stage_stride;
-  a.out = static_cast<bf16*>(c.out);
+  a.out = c.out;
   a.out_so = (long)c.Nq * c.H * c.dv;
   a.out_sh = c.dv;
   a.out_rs = (long)c.H * c.dv;
@@ -1464,7 +1490,7 @@ hipError_t run_dense_attention(const DenseAttnCall& c, hipStream_t s) {
   a.len1 = c.Nq;
   a.R = c.Nq;
   a.S = c.B * c.H;
-  return launch_flash<bf16, 128, 128, kDenseKeyTile, 8, 1, true>(a, c.G, c.ev_start, c.ev_stop, s);
+  return launch_flash<f16, 128, 128, kDenseKeyTile, 8, 1, true>(a, c.G, c.ev_start, c.ev_stop, s);
 }
 
 }  // namespace vmla

@@ -1,15 +1,19 @@
 // Launch sequences of the dense per-head baseline (VideoMLA paper, section 1 and
 // appendix C.1: the layer whose cache holds every head's key and value).
 //
+//   prepare (once per ctx): the fp16 copy of W_O.
 //   append: one GEMM x . [W_K; W_V]^T whose epilogue rotates each head's key by
-//     3D-RoPE (all d_h channels, absolute frame index), writes it to the key row
-//     of its ring slot, and writes the value transposed (fp16) to the value
-//     column of that slot; then the value columns past the valid keys up to the
-//     next key-tile boundary are zeroed, so the attention kernel can stage
-//     whole tiles.
-//   attend: q = RoPE(W_Q x) scaled by log2(e)/sqrt(d_h); the chunk's own keys
-//     and values into staging with the same epilogue; dense flash attention
-//     over ring + chunk (attention.hip); out = W_O o.
+//     3D-RoPE (all d_h channels, absolute frame index), writes it (fp16) to the
+//     key row of its ring slot, and writes the value transposed (fp16) to the
+//     value column of that slot; then the value columns past the valid keys up
+//     to the next key-tile boundary are zeroed, so the attention kernel can
+//     stage whole tiles.
+//   attend: q = RoPE(W_Q x) scaled by log2(e)/sqrt(d_h) (fp16); the chunk's own
+//     keys and values into staging with the same epilogue; dense flash
+//     attention over ring + chunk on fp16 operands (attention.hip); out = W_O o.
+// Keys, values, queries and the attention output are fp16: 16-bit like the
+// pages' bf16 cache, with 11 significant bits.  Conversions saturate beyond
+// fp16's range and raise the ctx's range flag.
 #include "gemm.h"
 #include "plan.h"
 
@@ -28,11 +32,12 @@ static Rope dense_rope(const DensePlan& p) {
 // q[(b*nh + h)][t][j] = qscale * RoPE(W_Q^h x_t)[j]; token m is chunk token
 // m % Nq of stream m / Nq, in frame frame0 + t / T.
 struct EpiDenseQ {
-  bf16* q;
+  f16* q;
   int Nq, nh, dh;
   float qscale;
   int64_t frame0;
   Rope rope;
+  uint32_t* flag;
   __device__ void operator()(int, int m, int n, const float* v) const {
     const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
     const int64_t frame = frame0 + t / rope.tokens_per_frame;
@@ -40,20 +45,21 @@ struct EpiDenseQ {
     float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
     rope.rotate2(j >> 1, frame, s, a0, a1);
     rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
-    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0 * qscale, a1 * qscale, a2 * qscale, a3 * qscale);
+    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0 * qscale, a1 * qscale, a2 * qscale, a3 * qscale, flag);
   }
 };
 
 // Features [0, nh*dh) are keys, [nh*dh, nh*(dh+dv)) values.  Key row / value
 // column of token t: its ring slot row (frame % W)*T + s, or t for staging.
 struct EpiDenseKV {
-  bf16* k;  // [B][nh][P][dh]
-  f16* v;   // [B][nh][dv][P]
+  f16* k;  // [B][nh][P][dh]
+  f16* v;  // [B][nh][dv][P]
   long P;
   int Nq, nh, dh, dv, W;
   int ring;
   int64_t frame0;
   Rope rope;
+  uint32_t* flag;
   __device__ void operator()(int, int m, int n, const float* x) const {
     const int b = m / Nq, t = m % Nq;
     const int64_t frame = frame0 + t / rope.tokens_per_frame;
@@ -64,12 +70,14 @@ struct EpiDenseKV {
       float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
       rope.rotate2(j >> 1, frame, s, a0, a1);
       rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
-      store4(k + (((long)b * nh + h) * P + row) * dh + j, a0, a1, a2, a3);
+      store4(k + (((long)b * nh + h) * P + row) * dh + j, a0, a1, a2, a3, flag);
     } else {
       const int n2 = n - nh * dh, h = n2 / dv, f = n2 % dv;
       f16* dst = v + (((long)b * nh + h) * dv + f) * P + (row & ~15L) + perm16((int)(row & 15));
+      bool over = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i * P] = (f16)x[i];
+      for (int i = 0; i < 4; ++i) dst[i * P] = to_f16_sat(x[i], over);
+      raise_range_flag(over, flag);
     }
   }
 };
@@ -91,14 +99,15 @@ void zero_value_columns_async(void* v, long rows, long P, int c0, int c1, hipStr
   zero_value_columns<<<grid, 256, 0, s>>>(static_cast<f16*>(v), rows, P, c0, c1);
 }
 
-static GemmOps<bf16> dense_ops(const void* w, const void* w2, int n_split, const void* x, long ldx, int N,
-                               int M, int K) {
-  GemmOps<bf16> o;
-  o.w = static_cast<const bf16*>(w);
-  o.w2 = static_cast<const bf16*>(w2);
+template <typename T = bf16>
+static GemmOps<T> dense_ops(const void* w, const void* w2, int n_split, const void* x, long ldx, int N, int M,
+                            int K) {
+  GemmOps<T> o;
+  o.w = static_cast<const T*>(w);
+  o.w2 = static_cast<const T*>(w2);
   o.ldw = K;
   o.wz = 0;
-  o.x = static_cast<const bf16*>(x);
+  o.x = static_cast<const T*>(x);
   o.ldx = ldx;
   o.xz = 0;
   o.N = N;
@@ -111,7 +120,7 @@ static GemmOps<bf16> dense_ops(const void* w, const void* w2, int n_split, const
 // K/V of x's tokens (frames frame0..) into the ring or the staging buffers.
 static void dense_kv(const DensePlan& p, const void* x, int64_t frame0, bool ring, hipStream_t s) {
   EpiDenseKV e;
-  e.k = static_cast<bf16*>(ring ? p.kring : p.kstage);
+  e.k = static_cast<f16*>(ring ? p.kring : p.kstage);
   e.v = static_cast<f16*>(ring ? p.vring : p.vstage);
   e.P = ring ? p.ring_stride : p.stage_stride;
   e.Nq = p.Nq;
@@ -122,11 +131,28 @@ static void dense_kv(const DensePlan& p, const void* x, int64_t frame0, bool rin
   e.ring = ring ? 1 : 0;
   e.frame0 = frame0;
   e.rope = dense_rope(p);
+  e.flag = p.flags;
   gemm<bf16, false>(dense_ops(p.w_k, p.w_v, p.nh * p.dh, x, p.d, p.nh * (p.dh + p.dv), p.B * p.Nq, p.d), 1, e, s);
 }
 
 static int round_tile(long keys) {
   return (int)((keys + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile);
+}
+
+__global__ __launch_bounds__(256) void dense_convert_weight(f16* dst, const bf16* src, long n, uint32_t* flag) {
+  bool over = false;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+    dst[i] = to_f16_sat((float)src[i], over);
+  raise_range_flag(over, flag);
+}
+
+hipError_t run_dense_prepare(const DensePlan& p, hipStream_t s) {
+  hipError_t err = run_clear_flags(p.flags, s);
+  if (err != hipSuccess) return err;
+  const long n = (long)p.d * p.nh * p.dv;
+  dense_convert_weight<<<(int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048), 256, 0, s>>>(
+      static_cast<f16*>(p.wo), static_cast<const bf16*>(p.w_o), n, p.flags);
+  return hipGetLastError();
 }
 
 hipError_t run_dense_append(const DensePlan& p, int64_t n, const void* x, hipStream_t s) {
@@ -143,13 +169,14 @@ hipError_t run_dense_attend(const DensePlan& p, int64_t n, const void* x, void* 
   const int M = p.B * p.Nq;
   {
     EpiDenseQ e;
-    e.q = static_cast<bf16*>(p.q);
+    e.q = static_cast<f16*>(p.q);
     e.Nq = p.Nq;
     e.nh = p.nh;
     e.dh = p.dh;
     e.qscale = p.qscale;
     e.frame0 = n;
     e.rope = dense_rope(p);
+    e.flag = p.flags;
     gemm<bf16, false>(dense_ops(p.w_q, p.w_q, p.nh * p.dh, x, p.d, p.nh * p.dh, M, p.d), 1, e, s);
   }
   dense_kv(p, x, n, false, s);
@@ -180,9 +207,9 @@ hipError_t run_dense_attend(const DensePlan& p, int64_t n, const void* x, void* 
     err = run_dense_attention(a, s);
     if (err != hipSuccess) return err;
   }
-  {  // out = W_O o
+  {  // out = W_O o (fp16 operands, bf16 result)
     EpiStore<bf16> e{static_cast<bf16*>(out), p.d, 0};
-    gemm<bf16, false>(dense_ops(p.w_o, p.w_o, p.d, p.o, (long)p.nh * p.dv, p.d, M, p.nh * p.dv), 1, e, s);
+    gemm<f16, false>(dense_ops<f16>(p.wo, p.wo, p.d, p.o, (long)p.nh * p.dv, p.d, M, p.nh * p.dv), 1, e, s);
   }
   return hipGetLastError();
 }

@@ -1,5 +1,6 @@
 // Device-side building blocks shared by the GEMM and attention kernels:
-// storage types, 32x32 MFMA fragments for gfx950 and small vector helpers.
+// storage types, 32x32 MFMA fragments for gfx950 (bf16, fp16, fp32) and small
+// vector helpers.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,6 +35,16 @@ template <> struct Mfma<bf16> {
   __device__ static inline Frag zero() { return Frag{}; }
 };
 
+template <> struct Mfma<f16> {
+  static constexpr int KPL = 8;
+  using Frag = f16x8;
+  __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline Frag load(const f16* p) { return *reinterpret_cast<const Frag*>(p); }
+  __device__ static inline Frag zero() { return Frag{}; }
+};
+
 template <> struct Mfma<float> {
   static constexpr int KPL = 1;
   using Frag = float;
@@ -53,6 +64,40 @@ __device__ inline void store4(bf16* p, float a, float b, float c, float d) {
 __device__ inline void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
+// fp16, round to nearest even.  Used where the values cannot leave fp16's
+// range (convex combinations of fp16 values).
+__device__ inline void store4(f16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f16x4*>(p) = f16x4{(f16)a, (f16)b, (f16)c, (f16)d};
+}
+
+// Largest finite fp16 magnitude.  The fp16 operand copies (queries, latent key
+// tiles, intermediate activations, converted weights) saturate a finite value
+// beyond it to +-kF16Max instead of rounding it to infinity, and record that
+// they did in bit 0 of a range-flag word the host can read back.  NaN and
+// infinite values pass through unchanged.
+constexpr float kF16Max = 65504.f;
+__device__ inline f16 to_f16_sat(float v, bool& over) {
+  const float a = __builtin_fabsf(v);
+  if (a > kF16Max && a < __builtin_huge_valf()) {
+    over = true;
+    v = __builtin_copysignf(kF16Max, v);
+  }
+  return (f16)v;
+}
+__device__ inline void raise_range_flag(bool over, uint32_t* flag) {
+  if (over && flag) atomicOr(flag, 1u);
+}
+
+// Store four values in an epilogue's output type; fp16 outputs saturate and
+// flag as above, bf16 and fp32 outputs cover fp32's range.
+__device__ inline void store4(f16* p, float a, float b, float c, float d, uint32_t* flag) {
+  bool over = false;
+  *reinterpret_cast<f16x4*>(p) =
+      f16x4{to_f16_sat(a, over), to_f16_sat(b, over), to_f16_sat(c, over), to_f16_sat(d, over)};
+  raise_range_flag(over, flag);
+}
+__device__ inline void store4(bf16* p, float a, float b, float c, float d, uint32_t*) { store4(p, a, b, c, d); }
+__device__ inline void store4(float* p, float a, float b, float c, float d, uint32_t*) { store4(p, a, b, c, d); }
 
 // 16-byte global load / zero of one vector of storage elements.
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -97,5 +142,18 @@ struct Rope {
     b = y;
   }
 };
+
+// Local temporal coordinate of the frame held in ring slot `slot` after n
+// appends, with S pinned sink slots ahead of a W-frame FIFO: the frame's index
+// in the visible context [sink frames, window frames oldest first], numbered
+// from 0 without gaps (sink slot i holds frame i; window slot S + j holds the
+// window frame f with (f - S) % W == j).
+__device__ inline int64_t local_frame(int slot, int64_t n, int S, int W) {
+  if (slot < S) return slot;
+  const int64_t n_sink = n < S ? n : S;
+  const int64_t w0 = n - W > S ? n - W : S;  // first window frame
+  const int64_t f = w0 + ((((int64_t)(slot - S) - (w0 - S)) % W) + W) % W;
+  return n_sink + (f - w0);
+}
 
 }  // namespace vmla

@@ -5,15 +5,19 @@
 // step:
 //
 //   expand: per stream and head, keys [W_UK^h c | k_r] of the valid ring rows
-//     (one GEMM with the per-head lift [W_UK^h 0 ; 0 I], so the rotated k_r is
-//     copied exactly) and values W_UV^h c, transposed (a GEMM with the operand
+//     (one GEMM with the per-head lift [W_UK^h 0 ; 0 I], so k_r is copied
+//     exactly, and turned at its local coordinate in the epilogue when the
+//     cache holds it un-rotated) and values W_UV^h c, transposed (a GEMM with the operand
 //     roles swapped, so each lane holds 4 consecutive keys of one value channel
 //     and stores them together), then the value columns past the valid keys are
 //     zeroed up to the key-tile boundary.
 //   attend: compress the chunk into staging (latent path), c^Q = W_DQ x, the
-//     per-head queries [q_nope | RoPE(q_rope)] (not absorbed), the chunk's own
-//     keys and values by the same up-projection, dense flash attention over the
-//     expanded window + chunk (attention.hip), out = W_O o.
+//     per-head queries [q_nope | RoPE(q_rope)] (not absorbed; the prepared
+//     qscale * W_UQ), the chunk's own keys and values by the same up-projection,
+//     dense flash attention over the expanded window + chunk (attention.hip),
+//     out = W_O o.
+// Expanded keys and values, queries, c^Q and the attention output are fp16, as
+// in the dense layer; conversions saturate and raise the ctx's range flag.
 #include "gemm.h"
 #include "plan.h"
 
@@ -45,13 +49,27 @@ __global__ __launch_bounds__(256) void build_key_lift(bf16* wext, const bf16* w_
   }
 }
 
-// Key rows: K[b][h][row m][n] (z = head).
+// Key rows: K[b][h][row m][n] (z = head).  With rot (ring rows of a
+// rope_at_use layer, whose cache holds k^ un-rotated) the rotary features
+// n >= d_nope are turned at the local coordinate of ring row m's frame.
 struct EpiExpandKey {
-  bf16* k;
+  f16* k;
   long P;
   int nh, dh, b;
+  uint32_t* flag;
+  int rot, d_nope, S, W;
+  int64_t n_frames;
+  Rope rope;
   __device__ void operator()(int z, int m, int n, const float* v) const {
-    store4(k + (((long)b * nh + z) * P + m) * dh + n, v[0], v[1], v[2], v[3]);
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    if (rot && n >= d_nope) {
+      const int T = rope.tokens_per_frame;
+      const int64_t tau = local_frame(m / T, n_frames, S, W);
+      const int pair = (n - d_nope) >> 1;
+      rope.rotate2(pair, tau, m % T, a0, a1);
+      rope.rotate2(pair + 1, tau, m % T, a2, a3);
+    }
+    store4(k + (((long)b * nh + z) * P + m) * dh + n, a0, a1, a2, a3, flag);
   }
 };
 
@@ -61,24 +79,20 @@ struct EpiExpandValueT {
   f16* vt;
   long P;
   int nh, dv, b;
+  uint32_t* flag;
   __device__ void operator()(int z, int m, int n, const float* v) const {
-    f16* dst = vt + (((long)b * nh + z) * dv + m) * P + (n & ~15) + perm16(n & 15);
-    f16x4 h4;
-    h4[0] = (f16)v[0];
-    h4[1] = (f16)v[1];
-    h4[2] = (f16)v[2];
-    h4[3] = (f16)v[3];
-    *reinterpret_cast<f16x4*>(dst) = h4;
+    store4(vt + (((long)b * nh + z) * dv + m) * P + (n & ~15) + perm16(n & 15), v[0], v[1], v[2], v[3], flag);
   }
 };
 
-// Per-head queries [q_nope | RoPE(q_rope)] * qscale into Q[b][h][t][dh].
+// Per-head queries [q_nope | RoPE(q_rope)] into Q[b][h][t][dh] (the prepared
+// weight carries qscale).
 struct EpiQueryHead {
-  bf16* q;
+  f16* q;
   int Nq, nh, dh, d_nope;
-  float qscale;
   int64_t frame0;
   Rope rope;
+  uint32_t* flag;
   __device__ void operator()(int, int m, int n, const float* v) const {
     const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
     float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
@@ -89,16 +103,17 @@ struct EpiQueryHead {
       rope.rotate2(pair, frame, s, a0, a1);
       rope.rotate2(pair + 1, frame, s, a2, a3);
     }
-    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0 * qscale, a1 * qscale, a2 * qscale, a3 * qscale);
+    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0, a1, a2, a3, flag);
   }
 };
 
-static GemmOps<bf16> gops(const void* w, long ldw, long wz, const void* x, long ldx, long xz, int N, int M, int K) {
-  GemmOps<bf16> o;
-  o.w = o.w2 = static_cast<const bf16*>(w);
+template <typename T = bf16>
+static GemmOps<T> gops(const void* w, long ldw, long wz, const void* x, long ldx, long xz, int N, int M, int K) {
+  GemmOps<T> o;
+  o.w = o.w2 = static_cast<const T*>(w);
   o.ldw = ldw;
   o.wz = wz;
-  o.x = static_cast<const bf16*>(x);
+  o.x = static_cast<const T*>(x);
   o.ldx = ldx;
   o.xz = xz;
   o.N = N;
@@ -116,14 +131,17 @@ bool expanded_supported(const Plan& p) {
 
 // Up-project `rows` latent rows of every stream (row stride D, stream stride
 // lat_bstride) into key rows / transposed value columns [0, rows) of stride P.
+// rot_n >= 0: the rows are the ring of a rope_at_use layer after rot_n appends
+// (k^ stored un-rotated; turned at use in the key epilogue).
 static void up_project(const Plan& p, const DensePlan&, const bf16* wext, const void* lat, long lat_bstride,
-                       int rows, bf16* kdst, f16* vdst, long P, hipStream_t s) {
+                       int rows, f16* kdst, f16* vdst, long P, int64_t rot_n, hipStream_t s) {
   if (rows <= 0) return;
   for (int b = 0; b < p.B; ++b) {
     const bf16* lb = static_cast<const bf16*>(lat) + (long)b * lat_bstride;
-    EpiExpandKey ek{kdst, P, p.nh, p.dh, b};
+    EpiExpandKey ek{kdst, P, p.nh, p.dh, b, p.flags, rot_n >= 0 ? 1 : 0, p.d_nope, p.S, p.W, rot_n,
+                    latent_rope(p)};
     gemm<bf16, false>(gops(wext, p.D, (long)p.dh * p.D, lb, p.D, 0, p.dh, rows, p.D), p.nh, ek, s);
-    EpiExpandValueT ev{vdst, P, p.nh, p.dv, b};
+    EpiExpandValueT ev{vdst, P, p.nh, p.dv, b, p.flags};
     gemm<bf16, false>(gops(lb, p.D, 0, p.w_uv, p.dc, (long)p.dv * p.dc, rows, p.dv, p.dc), p.nh, ev, s);
   }
   zero_value_columns_async(vdst, (long)p.B * p.nh * p.dv, P, rows, (int)round_up(rows, kDenseKeyTile), s);
@@ -135,13 +153,9 @@ hipError_t run_expand(const Plan& p, const DensePlan& ex, void* wext_buf, int64_
   build_key_lift<<<(int)((total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024), 256, 0, s>>>(
       wext, static_cast<const bf16*>(p.w_uk), p.nh, p.d_nope, p.dc, p.dr);
   const int n_ring = (int)(cached_frames(p, n) * p.Tpf);
-  // rope_at_use: up-project the window with k^ rotated at local coordinates
-  if (p.rope_at_use) {
-    const hipError_t err = run_assemble(p, n, s);
-    if (err != hipSuccess) return err;
-  }
-  up_project(p, ex, wext, p.rope_at_use ? p.assembled : p.cache, (long)(p.S + p.W) * p.Tpf * p.D, n_ring,
-             static_cast<bf16*>(ex.kring), static_cast<f16*>(ex.vring), ex.ring_stride, s);
+  // rope_at_use: the key epilogue turns k^ at each ring row's local coordinate
+  up_project(p, ex, wext, p.cache, (long)(p.S + p.W) * p.Tpf * p.D, n_ring, static_cast<f16*>(ex.kring),
+             static_cast<f16*>(ex.vring), ex.ring_stride, p.rope_at_use ? n : -1, s);
   return hipGetLastError();
 }
 
@@ -151,24 +165,24 @@ hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* w
   const int64_t tq = p.rope_at_use ? cached_frames(p, n) : n;  // temporal coordinate of the chunk's first frame
   hipError_t err = run_compress(p, x, tq, p.stage, false, s);
   if (err != hipSuccess) return err;
-  {  // c^Q = W_DQ x
-    EpiStore<bf16> e{static_cast<bf16*>(p.cq), p.dq, 0};
+  {  // c^Q = W_DQ x (fp16)
+    EpiStore<f16> e{static_cast<f16*>(p.cq), p.dq, 0, p.flags};
     gemm<bf16, false>(gops(p.w_dq, p.d, 0, x, p.d, 0, p.dq, M, p.d), 1, e, s);
   }
   {  // per-head queries, not absorbed
     EpiQueryHead e;
-    e.q = static_cast<bf16*>(ex.q);
+    e.q = static_cast<f16*>(ex.q);
     e.Nq = p.Nq;
     e.nh = p.nh;
     e.dh = p.dh;
     e.d_nope = p.d_nope;
-    e.qscale = p.qscale;
     e.frame0 = tq;
     e.rope = latent_rope(p);
-    gemm<bf16, false>(gops(p.w_uq, p.dq, 0, p.cq, p.dq, 0, p.nh * p.dh, M, p.dq), 1, e, s);
+    e.flag = p.flags;
+    gemm<f16, false>(gops<f16>(p.wuq, p.dq, 0, p.cq, p.dq, 0, p.nh * p.dh, M, p.dq), 1, e, s);
   }
-  up_project(p, ex, static_cast<const bf16*>(wext), p.stage, (long)p.Nq * p.D, p.Nq, static_cast<bf16*>(ex.kstage),
-             static_cast<f16*>(ex.vstage), ex.stage_stride, s);
+  up_project(p, ex, static_cast<const bf16*>(wext), p.stage, (long)p.Nq * p.D, p.Nq, static_cast<f16*>(ex.kstage),
+             static_cast<f16*>(ex.vstage), ex.stage_stride, -1, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     DenseAttnCall a;
@@ -193,9 +207,10 @@ hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* w
     a.G = ex.G;
     if ((err = run_dense_attention(a, s)) != hipSuccess) return err;
   }
-  {  // out = W_O o
+  {  // out = W_O o (fp16 operands, bf16 result)
     EpiStore<bf16> e{static_cast<bf16*>(out), p.d, 0};
-    gemm<bf16, false>(gops(p.w_o, (long)p.nh * p.dv, 0, ex.o, (long)p.nh * p.dv, 0, p.d, M, p.nh * p.dv), 1, e, s);
+    gemm<f16, false>(gops<f16>(ex.wo, (long)p.nh * p.dv, 0, ex.o, (long)p.nh * p.dv, 0, p.d, M, p.nh * p.dv), 1, e,
+                     s);
   }
   return hipGetLastError();
 }

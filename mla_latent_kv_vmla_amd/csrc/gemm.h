@@ -1,7 +1,8 @@
 // MFMA GEMM for the projections around latent attention:
 //   Y[m][n] = sum_k X[m][k] * W[n][k]      (W in Linear layout [N][K])
 //   Y[m][n] = sum_k X[m][k] * W[k][n]      (W_KN: W stored [K][N])
-// batched over z with element strides.  The kernel computes tiles of Y^T
+// batched over z with element strides.  Both operands have the type T (bf16,
+// fp16 or fp32), accumulated in fp32.  The kernel computes tiles of Y^T
 // (features n as MFMA rows, tokens m as MFMA columns), so each lane ends with
 // four consecutive output features of one token -- the shape a rotary pair or
 // a packed row store wants.  The epilogue functor receives (z, m, n, v[4]) for
@@ -156,12 +157,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
     }
 }
 
-// Y[m][n] -> y[z*yz + m*ldy + n]
-template <typename T> struct EpiStore {
-  T* y;
+// Y[m][n] -> y[z*yz + m*ldy + n] in the output type O (fp16 outputs saturate
+// and raise *flag, see store4)
+template <typename O> struct EpiStore {
+  O* y;
   long ldy, yz;
+  uint32_t* flag = nullptr;
   __device__ void operator()(int z, int m, int n, const float* v) const {
-    store4(y + (long)z * yz + (long)m * ldy + n, v[0], v[1], v[2], v[3]);
+    store4(y + (long)z * yz + (long)m * ldy + n, v[0], v[1], v[2], v[3], flag);
   }
 };
 

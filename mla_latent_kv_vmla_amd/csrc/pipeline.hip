@@ -1,17 +1,25 @@
 // Launch sequences of the two library calls and the GEMM epilogues they use.
 //
+//   prepare (once per ctx): the weights the activation-type GEMMs consume, in
+//     that type (fp16 for bf16 storage): the absorbed query weight
+//     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] per head (the MLA
+//     absorption, VideoMLA paper section 3.3, taken into the weight so one GEMM
+//     yields the absorbed query), qscale * W_UQ, W_UV and W_O.
 //   compress (VideoMLA paper, sections 3.1-3.2): one GEMM x . [W_DKV; W_KR]^T whose
 //     epilogue rotates the decoupled key channels by 3D-RoPE at the absolute
 //     frame (ring rows with rope_at_use stay un-rotated), rounds to the storage
 //     type and scatters each token's row to its ring slot (slot * T + s; frames
 //     f < S take sink slot f, later ones slot S + (f - S) % W) or to a linear
 //     buffer.
-//   attend: compress the chunk into staging; with rope_at_use, rotate the
-//     visible ring rows at their window-local coordinates into the workspace
-//     (assemble_window); c^Q = W_DQ x; q = W_UQ c^Q with the
-//     rotary channels turned and scaled straight into the absorbed query;
-//     absorbed query q~_h = W_UK^h^T q_nope_h (per-head GEMM on MFMA);
-//     latent attention (attention.hip); o_h = W_UV^h o~_h; out = W_O o.
+//   attend: compress the chunk into staging; with rope_at_use and fp32
+//     storage, rotate the visible ring rows at their window-local coordinates
+//     into the workspace (assemble_window; with bf16 storage the attention
+//     pre-pass rotates them); c^Q = W_DQ x; absorbed query = prepared weight . c^Q
+//     with the rotary channels turned in the epilogue; latent attention
+//     (attention.hip); o_h = W_UV^h o~_h; out = W_O o.  Everything between x
+//     and out is held in the activation type.
+#include <type_traits>
+
 #include "gemm.h"
 #include "plan.h"
 
@@ -54,43 +62,103 @@ template <typename T> struct EpiLatent {
   }
 };
 
-// q = W_UQ c^Q, per head [q_nope (d_nope) ; q_rope (dr)].  q_nope goes to its
-// own buffer; q_rope is rotated, scaled by qscale and written into the rotary
-// part of the absorbed query row.
-template <typename T> struct EpiQuery {
-  T* qnope;  // [M][nh][d_nope]
-  T* qt;     // [M][nh][D]
-  int Nq, nh, d_nope, dh, dc, D;
-  float qscale;
-  Rope rope;
-  __device__ void operator()(int, int m, int n, const float* v) const {
-    const int h = n / dh, j = n % dh;
-    if (j < d_nope) {
-      store4(qnope + ((long)m * nh + h) * d_nope + j, v[0], v[1], v[2], v[3]);
-      return;
-    }
-    const int t = m % Nq;
-    const int64_t frame = frame0 + t / rope.tokens_per_frame;
-    const int s = t % rope.tokens_per_frame;
-    const int pair = (j - d_nope) >> 1;
-    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-    rope.rotate2(pair, frame, s, a0, a1);
-    rope.rotate2(pair + 1, frame, s, a2, a3);
-    store4(qt + ((long)m * nh + h) * D + dc + (j - d_nope), a0 * qscale, a1 * qscale, a2 * qscale,
-           a3 * qscale);
-  }
+// Absorbed query straight from c^Q through the prepared weight: feature n of
+// token m is channel j = n % D of head n / D; channels [0, dc) are the content
+// part qscale * W_UK^h^T q_nope, channels [dc, D) the rotary part qscale * q_rope,
+// turned here at the token's (frame, row, column).
+template <typename A> struct EpiQueryAbs {
+  A* qt;  // [M][nh*D]
+  int Nq, N, dc, D;
   int64_t frame0;
+  Rope rope;
+  uint32_t* flag;
+  __device__ void operator()(int, int m, int n, const float* v) const {
+    const int j = n % D;
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    if (j >= dc) {
+      const int t = m % Nq;
+      const int64_t frame = frame0 + t / rope.tokens_per_frame;
+      const int s = t % rope.tokens_per_frame;
+      const int pair = (j - dc) >> 1;
+      rope.rotate2(pair, frame, s, a0, a1);
+      rope.rotate2(pair + 1, frame, s, a2, a3);
+    }
+    store4(qt + (long)m * N + n, a0, a1, a2, a3, flag);
+  }
 };
 
-// Absorbed content query: q~[m][h][n] = qscale * (q_nope_h W_UK^h)[n]
-template <typename T> struct EpiAbsorb {
-  T* qt;
-  int nh, D;
-  float qscale;
-  __device__ void operator()(int z, int m, int n, const float* v) const {
-    store4(qt + ((long)m * nh + z) * D + n, v[0] * qscale, v[1] * qscale, v[2] * qscale, v[3] * qscale);
+// ---------------------------------------------------------------- prepare
+// Absorbed query weight, head h = row / D, channel j = row % D, column k:
+//   j <  dc: qscale * sum_i W_UK^h[i][j] * W_UQ[h*dh + i][k]   (i < d_nope)
+//   j >= dc: qscale * W_UQ[h*dh + d_nope + (j - dc)][k]
+// One thread per element, fp32 sums of the stored weights, one rounding.
+template <typename T, typename A>
+__global__ __launch_bounds__(256) void derive_query_weight(A* wqa, const T* w_uq, const T* w_uk, int nh, int d_nope,
+                                                           int dr, int dc, int dq, float qscale, uint32_t* flag) {
+  const int D = dc + dr, dh = d_nope + dr;
+  const long total = (long)nh * D * dq;
+  bool over = false;
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long)gridDim.x * 256) {
+    const int k = (int)(e % dq);
+    const long row = e / dq;
+    const int j = (int)(row % D), h = (int)(row / D);
+    float acc;
+    if (j < dc) {
+      acc = 0.f;
+      for (int i = 0; i < d_nope; ++i)
+        acc += (float)w_uk[((long)h * d_nope + i) * dc + j] * (float)w_uq[((long)h * dh + i) * dq + k];
+    } else {
+      acc = (float)w_uq[((long)h * dh + d_nope + (j - dc)) * dq + k];
+    }
+    acc *= qscale;
+    if constexpr (sizeof(A) == 2) wqa[e] = to_f16_sat(acc, over);
+    else wqa[e] = acc;
   }
-};
+  raise_range_flag(over, flag);
+}
+
+// dst[i] = scale * src[i] in the activation type.
+template <typename T, typename A>
+__global__ __launch_bounds__(256) void convert_weight(A* dst, const T* src, long n, float scale, uint32_t* flag) {
+  bool over = false;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const float v = (float)src[i] * scale;
+    if constexpr (sizeof(A) == 2) dst[i] = to_f16_sat(v, over);
+    else dst[i] = v;
+  }
+  raise_range_flag(over, flag);
+}
+
+__global__ void clear_flags(uint32_t* flags) { *flags = 0u; }
+
+hipError_t run_clear_flags(uint32_t* flags, hipStream_t s) {
+  clear_flags<<<1, 1, 0, s>>>(flags);
+  return hipGetLastError();
+}
+
+static int grid_for(long n) { return (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048); }
+
+template <typename T, typename A>
+static void prepare_t(const Plan& p, hipStream_t s) {
+  clear_flags<<<1, 1, 0, s>>>(p.flags);
+  const long nqa = (long)p.nh * p.D * p.dq;
+  derive_query_weight<T, A><<<grid_for(nqa), 256, 0, s>>>(static_cast<A*>(p.wqa), static_cast<const T*>(p.w_uq),
+                                                          static_cast<const T*>(p.w_uk), p.nh, p.d_nope, p.dr, p.dc,
+                                                          p.dq, p.qscale, p.flags);
+  const long nuq = (long)p.nh * p.dh * p.dq, nuv = (long)p.nh * p.dv * p.dc, no = (long)p.d * p.nh * p.dv;
+  convert_weight<T, A><<<grid_for(nuq), 256, 0, s>>>(static_cast<A*>(p.wuq), static_cast<const T*>(p.w_uq), nuq,
+                                                     p.qscale, p.flags);
+  convert_weight<T, A><<<grid_for(nuv), 256, 0, s>>>(static_cast<A*>(p.wuv), static_cast<const T*>(p.w_uv), nuv,
+                                                     1.f, p.flags);
+  convert_weight<T, A><<<grid_for(no), 256, 0, s>>>(static_cast<A*>(p.wo), static_cast<const T*>(p.w_o), no, 1.f,
+                                                    p.flags);
+}
+
+hipError_t run_prepare(const Plan& p, hipStream_t s) {
+  if (p.dtype == DType::F32) prepare_t<float, float>(p, s);
+  else prepare_t<bf16, f16>(p, s);
+  return hipGetLastError();
+}
 
 template <typename T>
 static GemmOps<T> ops(const void* w, long ldw, long wz, const void* x, long ldx, long xz, int N, int M, int K) {
@@ -137,8 +205,6 @@ template <typename T>
 __global__ __launch_bounds__(256) void assemble_window(const T* cache, T* out, long rows, long bstride, int64_t n,
                                                        int S, int W, int dc, int D, Rope rope) {
   const int dr = D - dc, pairs = dr / 2;
-  const int64_t n_sink = n < S ? n : S;
-  const int64_t w0 = n - W > S ? n - W : S;  // first window frame
   const int b = blockIdx.y;
   const T* src = cache + (long)b * bstride;
   T* dst = out + (long)b * bstride;
@@ -152,13 +218,7 @@ __global__ __launch_bounds__(256) void assemble_window(const T* cache, T* out, l
     }
     const int pair = e - dc;
     const int slot = (int)(r / rope.tokens_per_frame), s = (int)(r % rope.tokens_per_frame);
-    int64_t tau;
-    if (slot < S) {
-      tau = slot;
-    } else {
-      const int64_t f = w0 + (((int64_t)(slot - S) - (w0 - S)) % W + W) % W;
-      tau = n_sink + (f - w0);
-    }
+    const int64_t tau = local_frame(slot, n, S, W);
     float a = (float)src[r * D + dc + 2 * pair], bb = (float)src[r * D + dc + 2 * pair + 1];
     rope.rotate2(pair, tau, s, a, bb);
     dst[r * D + dc + 2 * pair] = (T)a;
@@ -183,38 +243,36 @@ hipError_t run_assemble(const Plan& p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Activation type of a storage type: fp16 for bf16, fp32 for fp32.
+template <typename T> using Act = typename std::conditional<sizeof(T) == 2, f16, float>::type;
+
 template <typename T>
 static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s, hipEvent_t ev0,
                            hipEvent_t ev1) {
+  using A = Act<T>;
   const int M = p.B * p.Nq;
   // temporal coordinate of the chunk's first frame: absolute, or local (after the visible cached frames)
   const int64_t tq = p.rope_at_use ? cached_frames(p, n) : n;
   compress_t<T>(p, x, tq, p.stage, false, s);
-  if (p.rope_at_use) assemble_t<T>(p, n, s);
-  {  // c^Q = W_DQ x
-    EpiStore<T> e{static_cast<T*>(p.cq), p.dq, 0};
+  // rotation at use: fp32 storage rotates the visible rows into a copy; bf16
+  // storage lets the attention pre-pass turn them as it converts them to fp16
+  const bool rot_in_prepass = p.rope_at_use && sizeof(T) == 2;
+  if (p.rope_at_use && !rot_in_prepass) assemble_t<T>(p, n, s);
+  {  // c^Q = W_DQ x (storage-type operands, activation-type result)
+    EpiStore<A> e{static_cast<A*>(p.cq), p.dq, 0, p.flags};
     gemm<T, false>(ops<T>(p.w_dq, p.d, 0, x, p.d, 0, p.dq, M, p.d), 1, e, s);
   }
-  {  // q = W_UQ c^Q -> q_nope, rotated/scaled q_rope into the absorbed query
-    EpiQuery<T> e;
-    e.qnope = static_cast<T*>(p.qnope);
-    e.qt = static_cast<T*>(p.qt);
+  {  // absorbed query [qscale W_UK^T q_nope | RoPE(qscale q_rope)] per head, one GEMM from c^Q
+    EpiQueryAbs<A> e;
+    e.qt = static_cast<A*>(p.qt);
     e.Nq = p.Nq;
-    e.nh = p.nh;
-    e.d_nope = p.d_nope;
-    e.dh = p.dh;
+    e.N = p.nh * p.D;
     e.dc = p.dc;
     e.D = p.D;
-    e.qscale = p.qscale;
-    e.rope = make_rope(p);
     e.frame0 = tq;
-    gemm<T, false>(ops<T>(p.w_uq, p.dq, 0, p.cq, p.dq, 0, p.nh * p.dh, M, p.dq), 1, e, s);
-  }
-  if (p.d_nope > 0) {  // q~_h = W_UK^h^T q_nope_h for every head (z = head)
-    EpiAbsorb<T> e{static_cast<T*>(p.qt), p.nh, p.D, p.qscale};
-    gemm<T, true>(ops<T>(p.w_uk, p.dc, (long)p.d_nope * p.dc, p.qnope, (long)p.nh * p.d_nope, p.d_nope,
-                         p.dc, M, p.d_nope),
-                  p.nh, e, s);
+    e.rope = make_rope(p);
+    e.flag = p.flags;
+    gemm<A, false>(ops<A>(p.wqa, p.dq, 0, p.cq, p.dq, 0, p.nh * p.D, M, p.dq), 1, e, s);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -223,8 +281,18 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
     a.dtype = p.dtype;
     a.dc = p.dc;
     a.dr = p.dr;
+    a.range_flag = p.flags;
     a.qt = p.qt;
-    a.cache = p.rope_at_use ? p.assembled : p.cache;
+    a.cache = p.rope_at_use && !rot_in_prepass ? p.assembled : p.cache;
+    a.rot_ring = rot_in_prepass ? 1 : 0;
+    a.rot_S = p.S;
+    a.rot_W = p.W;
+    a.rot_n = n;
+    a.pairs_t = p.pairs_t;
+    a.pairs_h = p.pairs_h;
+    a.grid_w = p.grid_w;
+    a.tokens_per_frame = p.Tpf;
+    for (int i = 0; i < kMaxRopePairs; ++i) a.freq[i] = p.freq[i];
     a.stage = p.stage;
     a.out = p.olat;
     a.part_o = p.part_o;
@@ -244,14 +312,13 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
     if (err != hipSuccess) return err;
   }
   {  // o_h = W_UV^h o~_h (z = head)
-    EpiStore<T> e{static_cast<T*>(p.o), (long)p.nh * p.dv, p.dv};
-    gemm<T, false>(ops<T>(p.w_uv, p.dc, (long)p.dv * p.dc, p.olat, (long)p.nh * p.dc, p.dc, p.dv, M, p.dc),
-                   p.nh, e, s);
+    EpiStore<A> e{static_cast<A*>(p.o), (long)p.nh * p.dv, p.dv, p.flags};
+    gemm<A, false>(ops<A>(p.wuv, p.dc, (long)p.dv * p.dc, p.olat, (long)p.nh * p.dc, p.dc, p.dv, M, p.dc), p.nh,
+                   e, s);
   }
-  {  // out = W_O o
+  {  // out = W_O o (storage type)
     EpiStore<T> e{static_cast<T*>(out), p.d, 0};
-    gemm<T, false>(ops<T>(p.w_o, (long)p.nh * p.dv, 0, p.o, (long)p.nh * p.dv, 0, p.d, M, p.nh * p.dv), 1, e,
-                   s);
+    gemm<A, false>(ops<A>(p.wo, (long)p.nh * p.dv, 0, p.o, (long)p.nh * p.dv, 0, p.d, M, p.nh * p.dv), 1, e, s);
   }
   return hipGetLastError();
 }

@@ -20,6 +20,14 @@ constexpr int kDenseKeyTile = 128;
 
 // Everything one layer call needs: geometry, borrowed device pointers and the
 // workspace carve-up.  Filled by the host runtime; read by the pipelines.
+//
+// Operand types.  The ring cache, x and out have the storage type (bf16 or
+// fp32).  Everything the layer computes between them -- c^Q, absorbed queries,
+// attention outputs, per-head outputs -- and the weights of the GEMMs that
+// consume those intermediates have the activation type: fp16 for bf16 storage
+// (11 significant bits where bf16 keeps 8, at the same MFMA rate), fp32 for
+// fp32 storage.  Those weights are converted (and, for the absorbed query,
+// derived) once per ctx by run_prepare into the persistent part of the workspace.
 struct Plan {
   DType dtype;
   int B, d, nh, d_nope, dr, dv, dc, dq, D, dh;  // D = dc + dr, dh = d_nope + dr
@@ -28,21 +36,26 @@ struct Plan {
   int causal_tokens;  // > 0: a whole clip of Nq tokens, block-causal in blocks of this many tokens
   int pairs_t, pairs_h, pairs_w;
   float freq[kMaxRopePairs];
-  float qscale;  // log2(e) / sqrt(dh): softmax scale folded into the absorbed query
+  float qscale;  // log2(e) / sqrt(dh): softmax scale folded into the query weights
   int G;         // persistent attention workgroups
   const void *w_dkv, *w_kr, *w_dq, *w_uq, *w_uk, *w_uv, *w_o;
-  void* cache;   // [B][W*Tpf][D]
-  // workspace regions
-  void *stage;   // [B][Nq][D]            chunk latents (rotated)
+  void* cache;   // [B][(S+W)*Tpf][D]
+  // persistent workspace (written by run_prepare)
+  uint32_t* flags;  // bit 0: an fp16 operand copy saturated (see kF16Max)
+  void *wqa;     // [nh][D][dq]   absorbed query weight: per head qscale*[W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope]
+  void *wuq;     // [nh*dh][dq]   qscale * W_UQ (per-head queries of the expanded path)
+  void *wuv;     // [nh][dv][dc]  W_UV
+  void *wo;      // [d][nh*dv]    W_O
+  // per-call workspace
+  void *stage;   // [B][Nq][D]            chunk latents (rotated), storage type
   void *cq;      // [B][Nq][dq]           query latent
-  void *qnope;   // [B][Nq][nh][d_nope]   content part of the per-head query
   void *qt;      // [B][Nq][nh][D]        absorbed query [W_UK^T q_nope | q_rope] * qscale
   void *olat;    // [B][Nq][nh][dc]       attention output in latent space
   void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV
-  float *part_o; // [2G][kAttnMaxRows][dc] normalised partial outputs (fp16 for 16-bit storage, else fp32)
+  float *part_o; // [2G][kAttnMaxRows][dc] normalised partial outputs (activation type)
   float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
   void *vtiles;  // pre-pass tiles of the visible keys (per call): fp16 key tiles for bf16, value images for fp32
-  void *assembled;  // rope_at_use: the visible cache rows with k_r rotated at local coordinates
+  void *assembled;  // rope_at_use with fp32 storage: the visible cache rows with k_r rotated at local coordinates
 };
 
 // Visible cached frames after n appends: sinks [0, min(n, S)) + window [max(S, n-W), n).
@@ -52,21 +65,34 @@ inline int64_t cached_frames(const Plan& p, int64_t n) {
   return sink + (win > 0 ? win : 0);
 }
 
+// Byte offsets of the workspace regions.  The persistent part (flags and
+// prepared weights) sits at the start of a ctx's workspace; the per-call part
+// follows it there, or fills a clip workspace of its own.
 struct WorkspaceLayout {
-  size_t stage, cq, qnope, qt, olat, o, part_o, part_ml, vtiles, assembled, total;
+  size_t flags, wqa, wuq, wuv, wo, persistent;                           // from the workspace start
+  size_t stage, cq, qt, olat, o, part_o, part_ml, vtiles, assembled, per_call;  // from the per-call start
+  size_t total;  // persistent + per_call
 };
 
 WorkspaceLayout workspace_layout(const Plan& p);
+// Bytes of one element of the activation type (fp16 for bf16 storage).
+inline size_t act_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
 
 // Kernel pipelines.  Each returns hipSuccess or the first launch error.
+// prepare: clear the range flag and write the persistent weights (wqa, wuq, wuv, wo).
+hipError_t run_prepare(const Plan& p, hipStream_t s);
+// Zero one flag word (a kernel, so the clear can sit in a captured graph).
+hipError_t run_clear_flags(uint32_t* flags, hipStream_t s);
 // compress: rows [c | RoPE(k^)] of x for frames frame0.. into dst; ring != 0
 // writes the frame's ring slot row (slot*Tpf + s; sinks pinned) of each
 // stream's cache, else row t of dst.  k^ is rotated with frame index frame0 + i
 // unless the rows go to the ring of a rope_at_use layer (stored un-rotated).
 hipError_t run_compress(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring,
                         hipStream_t s);
-// rope_at_use: the visible cache rows after n appends, k^ rotated with each
-// frame's local coordinate, into p.assembled.
+// rope_at_use with fp32 storage: the visible cache rows after n appends, k^
+// rotated with each frame's local coordinate, into p.assembled.  (With bf16
+// storage the rotation happens where the rows are converted: the attention
+// key-tile pre-pass and the expansion epilogue.)
 hipError_t run_assemble(const Plan& p, int64_t n, hipStream_t s);
 // attend: full chunk attention against the ring holding n frames.
 hipError_t run_attend(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s,
@@ -77,6 +103,7 @@ hipError_t run_attend(const Plan& p, int64_t n, const void* x, void* out, hipStr
 struct AttnCall {
   DType dtype;
   int dc, dr;
+  uint32_t* range_flag;  // raised when the fp16 key-tile pre-pass saturates a cached element
   const void* qt;
   const void* cache;
   const void* stage;
@@ -89,6 +116,13 @@ struct AttnCall {
   int B, R, n_ring, n_stage;
   int G;
   int causal_tokens;  // > 0: block-causal over the staged keys only (n_ring = 0), blocks of this many tokens
+  // rot_ring (bf16 storage, rope_at_use): the ring rows hold k^ un-rotated and the
+  // key-tile pre-pass turns them at their local coordinate (rot_n frames appended,
+  // rot_S sinks, rot_W window frames), with this rotary table
+  int rot_ring, rot_S, rot_W;
+  int64_t rot_n;
+  int pairs_t, pairs_h, grid_w, tokens_per_frame;
+  float freq[kMaxRopePairs];
 };
 hipError_t run_latent_attention(const AttnCall& a, hipStream_t s);
 bool latent_attention_supported(DType dt, int dc, int dr);
@@ -100,7 +134,7 @@ size_t latent_prepass_bytes(DType dt, int dc, int dr, int B, int max_ring_keys, 
 // ---------------------------------------------------------------- dense baseline
 // Per-head keys and values (the dense layer of the paper's section 1 and
 // appendix C.1).  Per (stream b, head h):
-//   keys   [P][dh] bf16, rotated by 3D-RoPE on all dh channels;
+//   keys   [P][dh] fp16, rotated by 3D-RoPE on all dh channels;
 //   values [dv][P] fp16, transposed, key j at column perm16(j) (bits 2 and 3
 //          of j swapped), zero at every column past the valid keys up to P;
 // P = ring_stride (ring: W*T keys, frame f in slots (f % W)*T..) or
@@ -115,8 +149,11 @@ struct DensePlan {
   int ring_stride, stage_stride;
   const void *w_q, *w_k, *w_v, *w_o;
   void *kring, *vring;  // cache
-  // workspace regions
-  void *q;       // [B][nh][Nq][dh]  rotated, scaled queries
+  // persistent workspace (run_dense_prepare)
+  uint32_t* flags;  // bit 0: an fp16 operand copy saturated
+  void* wo;         // [d][nh*dv] fp16 W_O
+  // per-call workspace
+  void *q;       // [B][nh][Nq][dh]  rotated, scaled queries (fp16)
   void *kstage;  // [B][nh][stage_stride][dh]
   void *vstage;  // [B][nh][dv][stage_stride]
   void *o;       // [B][Nq][nh*dv]  attention output
@@ -124,10 +161,15 @@ struct DensePlan {
 };
 
 struct DenseLayout {
-  size_t kring, vring, cache_total;                         // cache
-  size_t q, kstage, vstage, o, part_o, part_ml, ws_total;   // workspace
+  size_t kring, vring, cache_total;                                  // cache
+  size_t flags, wo, q, kstage, vstage, o, part_o, part_ml, ws_total;  // workspace
 };
-DenseLayout dense_layout(const DensePlan& p);
+// with_persistent = false (the expanded path's buffer, which takes the flag
+// and W_O of its latent ctx): flags and wo are left out (offsets 0, size 0).
+DenseLayout dense_layout(const DensePlan& p, bool with_persistent = true);
+
+// prepare: clear the range flag and write the fp16 W_O.
+hipError_t run_dense_prepare(const DensePlan& p, hipStream_t s);
 
 // append: K/V of the chunk (frames n..n+C-1) into ring slots.
 hipError_t run_dense_append(const DensePlan& p, int64_t n, const void* x, hipStream_t s);
@@ -136,7 +178,7 @@ hipError_t run_dense_attend(const DensePlan& p, int64_t n, const void* x, void* 
                             hipEvent_t attn_start = nullptr, hipEvent_t attn_stop = nullptr);
 
 struct DenseAttnCall {
-  int dh, dv;
+  int dh, dv;  // keys, queries and values fp16
   const void* q;
   const void *kring, *vring, *kstage, *vstage;
   void* out;  // [B][Nq][H][dv]

@@ -22,6 +22,7 @@ struct vmla_ctx {
   void* workspace;
   float freq[vmla::kMaxRopePairs];
   int64_t n;  // frames appended (lockstep over the batch)
+  int prepared;  // vmla_prepare has been enqueued
   // expanded latent path: buffer and frame count of the last vmla_expand
   const void* expanded;
   int64_t expanded_n;
@@ -34,6 +35,7 @@ struct vmla_dense_ctx {
   void* workspace;
   float freq[vmla::kMaxRopePairs];
   int64_t n;
+  int prepared;
 };
 
 namespace {
@@ -157,6 +159,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 namespace vmla {
 WorkspaceLayout workspace_layout(const Plan& p) {
   const size_t es = p.dtype == DType::F32 ? 4 : 2;
+  const size_t as = act_bytes(p.dtype);
   const size_t M = (size_t)p.B * p.Nq;
   WorkspaceLayout L;
   size_t off = 0;
@@ -165,21 +168,28 @@ WorkspaceLayout workspace_layout(const Plan& p) {
     off += align256(bytes);
     return o;
   };
+  L.flags = take(sizeof(uint32_t));
+  L.wqa = take((size_t)p.nh * p.D * p.dq * as);
+  L.wuq = take((size_t)p.nh * p.dh * p.dq * as);
+  L.wuv = take((size_t)p.nh * p.dv * p.dc * as);
+  L.wo = take((size_t)p.d * p.nh * p.dv * as);
+  L.persistent = off;
+  off = 0;
   L.stage = take(M * p.D * es);
-  L.cq = take(M * p.dq * es);
-  L.qnope = take(M * p.nh * (size_t)p.d_nope * es);
-  L.qt = take(M * p.nh * (size_t)p.D * es);
-  L.olat = take(M * p.nh * (size_t)p.dc * es);
-  L.o = take(M * p.nh * (size_t)p.dv * es);
-  L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * sizeof(float));
+  L.cq = take(M * p.dq * as);
+  L.qt = take(M * p.nh * (size_t)p.D * as);
+  L.olat = take(M * p.nh * (size_t)p.dc * as);
+  L.o = take(M * p.nh * (size_t)p.dv * as);
+  L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * as);
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
   L.vtiles = take(latent_prepass_bytes(p.dtype, p.dc, p.dr, p.B, (p.S + p.W) * p.Tpf, p.Nq));
-  L.assembled = take(p.rope_at_use ? (size_t)p.B * (p.S + p.W) * p.Tpf * p.D * es : 0);
-  L.total = off;
+  L.assembled = take(p.rope_at_use && p.dtype == DType::F32 ? (size_t)p.B * (p.S + p.W) * p.Tpf * p.D * es : 0);
+  L.per_call = off;
+  L.total = L.persistent + L.per_call;
   return L;
 }
 
-DenseLayout dense_layout(const DensePlan& p) {
+DenseLayout dense_layout(const DensePlan& p, bool with_persistent) {
   DenseLayout L;
   const size_t heads = (size_t)p.B * p.nh;
   size_t off = 0;
@@ -192,11 +202,13 @@ DenseLayout dense_layout(const DensePlan& p) {
   L.vring = take(heads * p.ring_stride * p.dv * 2);
   L.cache_total = off;
   off = 0;
+  L.flags = with_persistent ? take(sizeof(uint32_t)) : 0;
+  L.wo = with_persistent ? take((size_t)p.d * p.nh * p.dv * 2) : 0;
   L.q = take(heads * p.Nq * p.dh * 2);
   L.kstage = take(heads * p.stage_stride * p.dh * 2);
   L.vstage = take(heads * p.stage_stride * p.dv * 2);
   L.o = take((size_t)p.B * p.Nq * p.nh * p.dv * 2);
-  L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dv * sizeof(float));
+  L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dv * 2);
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
   L.ws_total = off;
   return L;
@@ -223,7 +235,7 @@ ExpandedLayout expanded_layout(const Plan& p, DensePlan& ex) {
   ex.ring_stride = (int)(((long)(p.S + p.W) * p.Tpf + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile);
   ex.stage_stride = (p.Nq + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile;
   ExpandedLayout L;
-  L.dense = dense_layout(ex);
+  L.dense = dense_layout(ex, false);
   L.wext = L.dense.cache_total + L.dense.ws_total;
   L.total = L.wext + align256((size_t)p.nh * p.dh * p.D * 2);
   return L;
@@ -305,8 +317,23 @@ VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* ca
   return VMLA_OK;
 }
 
-static Plan make_plan(const vmla_ctx* c) {
-  Plan p = geometry(&c->cfg);
+// Point a plan's per-call regions at `base` (laid out by L).
+static void set_per_call(Plan& p, const vmla::WorkspaceLayout& L, void* base) {
+  char* ws = static_cast<char*>(base);
+  p.stage = ws + L.stage;
+  p.cq = ws + L.cq;
+  p.qt = ws + L.qt;
+  p.olat = ws + L.olat;
+  p.o = ws + L.o;
+  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  p.vtiles = ws + L.vtiles;
+  p.assembled = ws + L.assembled;
+}
+
+// Weights, cache and the persistent workspace of a ctx on top of plan p's
+// geometry (a chunk call's, or a clip's).
+static void set_ctx_pointers(Plan& p, const vmla_ctx* c) {
   for (int i = 0; i < vmla::kMaxRopePairs; ++i) p.freq[i] = c->freq[i];
   p.w_dkv = c->w.w_dkv;
   p.w_kr = c->w.w_kr;
@@ -316,19 +343,40 @@ static Plan make_plan(const vmla_ctx* c) {
   p.w_uv = c->w.w_uv;
   p.w_o = c->w.w_o;
   p.cache = c->cache;
-  const vmla::WorkspaceLayout L = vmla::workspace_layout(p);
+  const vmla::WorkspaceLayout L = vmla::workspace_layout(geometry(&c->cfg));
   char* ws = static_cast<char*>(c->workspace);
-  p.stage = ws + L.stage;
-  p.cq = ws + L.cq;
-  p.qnope = ws + L.qnope;
-  p.qt = ws + L.qt;
-  p.olat = ws + L.olat;
-  p.o = ws + L.o;
-  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
-  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
-  p.vtiles = ws + L.vtiles;
-  p.assembled = ws + L.assembled;
+  p.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  p.wqa = ws + L.wqa;
+  p.wuq = ws + L.wuq;
+  p.wuv = ws + L.wuv;
+  p.wo = ws + L.wo;
+}
+
+static Plan make_plan(const vmla_ctx* c) {
+  Plan p = geometry(&c->cfg);
+  set_ctx_pointers(p, c);
+  const vmla::WorkspaceLayout L = vmla::workspace_layout(p);
+  set_per_call(p, L, static_cast<char*>(c->workspace) + L.persistent);
   return p;
+}
+
+VMLA_API int vmla_prepare(vmla_ctx* ctx, hipStream_t stream) {
+  if (!ctx) return VMLA_ERR_NULL;
+  if (vmla::run_prepare(make_plan(ctx), stream) != hipSuccess) return VMLA_ERR_HIP;
+  ctx->prepared = 1;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_range_flags(vmla_ctx* ctx, uint32_t* flags, hipStream_t stream) {
+  if (!ctx || !flags) return VMLA_ERR_NULL;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
+  uint32_t* dev = make_plan(ctx).flags;
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess) return VMLA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return VMLA_ERR_HIP;
+  if (vmla::run_clear_flags(dev, stream) != hipSuccess) return VMLA_ERR_HIP;
+  *flags = v;
+  return VMLA_OK;
 }
 
 VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stream) {
@@ -344,6 +392,7 @@ VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stre
 VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream) {
   if (!ctx || !x || !out) return VMLA_ERR_NULL;
   if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   Plan p = make_plan(ctx);
   if (vmla::run_attend(p, ctx->n, x, out, stream) != hipSuccess) return VMLA_ERR_HIP;
   return VMLA_OK;
@@ -353,6 +402,7 @@ VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEv
                                   hipEvent_t attn_stop, hipStream_t stream) {
   if (!ctx || !x || !out || !attn_start || !attn_stop) return VMLA_ERR_NULL;
   if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   Plan p = make_plan(ctx);
   if (vmla::run_attend(p, ctx->n, x, out, stream, attn_start, attn_stop) != hipSuccess) return VMLA_ERR_HIP;
   return VMLA_OK;
@@ -407,36 +457,17 @@ static bool clip_fits(const vmla_config* cfg) {
 
 VMLA_API size_t vmla_clip_workspace_bytes(const vmla_config* cfg) {
   if (check_config(cfg) != VMLA_OK || !clip_fits(cfg)) return 0;
-  return vmla::workspace_layout(clip_geometry(cfg)).total;
+  return vmla::workspace_layout(clip_geometry(cfg)).per_call;
 }
 
 static int attend_clip(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out, hipEvent_t e0, hipEvent_t e1,
                        hipStream_t stream) {
   if (!clip_fits(&ctx->cfg)) return VMLA_ERR_CONFIG;
   if (!aligned16(x) || !aligned16(clip_workspace) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   Plan p = clip_geometry(&ctx->cfg);
-  for (int i = 0; i < vmla::kMaxRopePairs; ++i) p.freq[i] = ctx->freq[i];
-  const Plan base = make_plan(ctx);  // weights and cache pointers
-  p.w_dkv = base.w_dkv;
-  p.w_kr = base.w_kr;
-  p.w_dq = base.w_dq;
-  p.w_uq = base.w_uq;
-  p.w_uk = base.w_uk;
-  p.w_uv = base.w_uv;
-  p.w_o = base.w_o;
-  p.cache = base.cache;
-  const vmla::WorkspaceLayout L = vmla::workspace_layout(p);
-  char* ws = static_cast<char*>(clip_workspace);
-  p.stage = ws + L.stage;
-  p.cq = ws + L.cq;
-  p.qnope = ws + L.qnope;
-  p.qt = ws + L.qt;
-  p.olat = ws + L.olat;
-  p.o = ws + L.o;
-  p.part_o = reinterpret_cast<float*>(ws + L.part_o);
-  p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
-  p.vtiles = ws + L.vtiles;
-  p.assembled = ws + L.assembled;
+  set_ctx_pointers(p, ctx);
+  set_per_call(p, vmla::workspace_layout(p), clip_workspace);
   // the clip's frames are 0..W-1 and nothing is cached: attend at n = 0
   if (vmla::run_attend(p, 0, x, out, stream, e0, e1) != hipSuccess) return VMLA_ERR_HIP;
   return VMLA_OK;
@@ -479,6 +510,8 @@ static DensePlan make_expanded_plan(const Plan& p, void* buf, void** wext) {
   ex.o = ws + L.dense.o;
   ex.part_o = reinterpret_cast<float*>(ws + L.dense.part_o);
   ex.part_ml = reinterpret_cast<float*>(ws + L.dense.part_ml);
+  ex.flags = p.flags;  // the latent ctx's range flag and fp16 W_O
+  ex.wo = p.wo;
   *wext = b + L.wext;
   return ex;
 }
@@ -487,6 +520,7 @@ VMLA_API int vmla_expand(vmla_ctx* ctx, void* expanded, hipStream_t stream) {
   if (!ctx || !expanded) return VMLA_ERR_NULL;
   if (!aligned16(expanded)) return VMLA_ERR_ALIGN;
   if (!expanded_ok(&ctx->cfg)) return VMLA_ERR_UNSUPPORTED;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   Plan p = make_plan(ctx);
   void* wext;
   DensePlan ex = make_expanded_plan(p, expanded, &wext);
@@ -500,6 +534,7 @@ static int attend_expanded(vmla_ctx* ctx, const void* expanded, const void* x, v
                            hipEvent_t e1, hipStream_t stream) {
   if (!aligned16(expanded) || !aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
   if (!expanded_ok(&ctx->cfg)) return VMLA_ERR_UNSUPPORTED;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   if (ctx->expanded != expanded || ctx->expanded_n != ctx->n) return VMLA_ERR_STATE;
   Plan p = make_plan(ctx);
   void* wext;
@@ -580,6 +615,8 @@ static DensePlan make_dense_plan(const vmla_dense_ctx* c) {
   char* ws = static_cast<char*>(c->workspace);
   p.kring = cache + L.kring;
   p.vring = cache + L.vring;
+  p.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  p.wo = ws + L.wo;
   p.q = ws + L.q;
   p.kstage = ws + L.kstage;
   p.vstage = ws + L.vstage;
@@ -589,10 +626,30 @@ static DensePlan make_dense_plan(const vmla_dense_ctx* c) {
   return p;
 }
 
+VMLA_API int vmla_dense_prepare(vmla_dense_ctx* ctx, hipStream_t stream) {
+  if (!ctx) return VMLA_ERR_NULL;
+  if (vmla::run_dense_prepare(make_dense_plan(ctx), stream) != hipSuccess) return VMLA_ERR_HIP;
+  ctx->prepared = 1;
+  return VMLA_OK;
+}
+
+VMLA_API int vmla_dense_range_flags(vmla_dense_ctx* ctx, uint32_t* flags, hipStream_t stream) {
+  if (!ctx || !flags) return VMLA_ERR_NULL;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
+  uint32_t* dev = make_dense_plan(ctx).flags;
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess) return VMLA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return VMLA_ERR_HIP;
+  if (vmla::run_clear_flags(dev, stream) != hipSuccess) return VMLA_ERR_HIP;
+  *flags = v;
+  return VMLA_OK;
+}
+
 VMLA_API int vmla_dense_append(vmla_dense_ctx* ctx, const void* x, hipStream_t stream) {
   if (!ctx || !x) return VMLA_ERR_NULL;
   if (!aligned16(x)) return VMLA_ERR_ALIGN;
   if (ctx->n > INT64_MAX / 2) return VMLA_ERR_STATE;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   if (vmla::run_dense_append(make_dense_plan(ctx), ctx->n, x, stream) != hipSuccess) return VMLA_ERR_HIP;
   ctx->n += ctx->cfg.chunk_frames;
   return VMLA_OK;
@@ -601,6 +658,7 @@ VMLA_API int vmla_dense_append(vmla_dense_ctx* ctx, const void* x, hipStream_t s
 VMLA_API int vmla_dense_attend(vmla_dense_ctx* ctx, const void* x, void* out, hipStream_t stream) {
   if (!ctx || !x || !out) return VMLA_ERR_NULL;
   if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   if (vmla::run_dense_attend(make_dense_plan(ctx), ctx->n, x, out, stream) != hipSuccess) return VMLA_ERR_HIP;
   return VMLA_OK;
 }
@@ -609,6 +667,7 @@ VMLA_API int vmla_dense_attend_profiled(vmla_dense_ctx* ctx, const void* x, void
                                         hipEvent_t attn_stop, hipStream_t stream) {
   if (!ctx || !x || !out || !attn_start || !attn_stop) return VMLA_ERR_NULL;
   if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
   if (vmla::run_dense_attend(make_dense_plan(ctx), ctx->n, x, out, stream, attn_start, attn_stop) != hipSuccess)
     return VMLA_ERR_HIP;
   return VMLA_OK;

@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from ctypes import POINTER, byref, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, byref, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvmla.so")
@@ -75,6 +75,10 @@ def lib():
         L.vmla_create.argtypes = [POINTER(vmla_config), POINTER(vmla_weights), c_void_p, c_void_p,
                                   POINTER(c_float), POINTER(c_void_p)]
         L.vmla_create.restype = c_int
+        L.vmla_prepare.argtypes = [c_void_p, c_void_p]
+        L.vmla_prepare.restype = c_int
+        L.vmla_range_flags.argtypes = [c_void_p, POINTER(c_uint32), c_void_p]
+        L.vmla_range_flags.restype = c_int
         L.vmla_compress_append.argtypes = [c_void_p, c_void_p, c_void_p]
         L.vmla_compress_append.restype = c_int
         L.vmla_attend.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
@@ -112,6 +116,10 @@ def lib():
         L.vmla_dense_create.argtypes = [POINTER(vmla_config), POINTER(vmla_dense_weights), c_void_p, c_void_p,
                                         POINTER(c_float), POINTER(c_void_p)]
         L.vmla_dense_create.restype = c_int
+        L.vmla_dense_prepare.argtypes = [c_void_p, c_void_p]
+        L.vmla_dense_prepare.restype = c_int
+        L.vmla_dense_range_flags.argtypes = [c_void_p, POINTER(c_uint32), c_void_p]
+        L.vmla_dense_range_flags.restype = c_int
         L.vmla_dense_append.argtypes = [c_void_p, c_void_p, c_void_p]
         L.vmla_dense_append.restype = c_int
         L.vmla_dense_attend.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
@@ -167,6 +175,16 @@ def vmla_create(cfg: vmla_config, weights: vmla_weights, cache, workspace, rope_
     _check(lib().vmla_create(byref(cfg), byref(weights), _ptr(cache), _ptr(workspace), _freq_array(rope_freqs),
                              byref(ctx)), "vmla_create")
     return ctx
+
+
+def vmla_prepare(ctx, stream=None) -> None:
+    _check(lib().vmla_prepare(ctx, _stream(stream)), "vmla_prepare")
+
+
+def vmla_range_flags(ctx, stream=None) -> int:
+    v = c_uint32()
+    _check(lib().vmla_range_flags(ctx, byref(v), _stream(stream)), "vmla_range_flags")
+    return v.value
 
 
 def vmla_compress_append(ctx, x, stream=None) -> None:
@@ -254,6 +272,16 @@ def vmla_dense_create(cfg: vmla_config, weights: vmla_dense_weights, cache, work
     return ctx
 
 
+def vmla_dense_prepare(ctx, stream=None) -> None:
+    _check(lib().vmla_dense_prepare(ctx, _stream(stream)), "vmla_dense_prepare")
+
+
+def vmla_dense_range_flags(ctx, stream=None) -> int:
+    v = c_uint32()
+    _check(lib().vmla_dense_range_flags(ctx, byref(v), _stream(stream)), "vmla_dense_range_flags")
+    return v.value
+
+
 def vmla_dense_append(ctx, x, stream=None) -> None:
     _check(lib().vmla_dense_append(ctx, _ptr(x), _stream(stream)), "vmla_dense_append")
 
@@ -303,6 +331,17 @@ def torch_dtype(g):
     return torch.float32 if g.dtype == "f32" else torch.bfloat16
 
 
+def _check_tensor(t, shape, dtype, device, what):
+    """A device tensor handed to the library: contiguous, of this shape and
+    dtype, on the layer's device (a host or foreign-device pointer would reach
+    the kernels otherwise)."""
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda
+            or t.device != device):
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}; "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
 class LatentAttention:
     """One layer: device weights, ring cache and workspace (torch-allocated),
     driven through the C entry points above."""
@@ -329,13 +368,19 @@ class LatentAttention:
         if cache_fill is not None:
             self.cache.fill_(cache_fill)
         self.workspace = torch.empty(wb, dtype=torch.uint8, device=device)
+        self.device = self.workspace.device
         wts = vmla_weights(**{n: self.w[n].data_ptr() for n in self.WEIGHT_NAMES})
+        if rope_freqs is None:
+            rope_freqs = getattr(g, "rope_freqs", None)
         self.ctx = vmla_create(self.cfg, wts, self.cache, self.workspace, rope_freqs)
+        vmla_prepare(self.ctx)
 
-    def _check_x(self, x):
+    def _check_x(self, x, out=None, tokens=None):
         g = self.g
-        if tuple(x.shape) != (g.batch, g.n_q, g.hidden) or x.dtype != self.dtype or not x.is_contiguous():
-            raise ValueError(f"x must be contiguous {self.dtype} of shape {(g.batch, g.n_q, g.hidden)}")
+        shape = (g.batch, g.n_q if tokens is None else tokens, g.hidden)
+        _check_tensor(x, shape, self.dtype, self.device, "x")
+        if out is not None:
+            _check_tensor(out, shape, self.dtype, self.device, "out")
 
     def append(self, x, stream=None):
         self._check_x(x)
@@ -343,7 +388,7 @@ class LatentAttention:
 
     def attend(self, x, out=None, stream=None):
         import torch
-        self._check_x(x)
+        self._check_x(x, out)
         if out is None:
             out = torch.empty_like(x)
         vmla_attend(self.ctx, x, out, stream)
@@ -352,8 +397,10 @@ class LatentAttention:
     def compress(self, x, frame0: int, out=None, stream=None):
         import torch
         self._check_x(x)
+        shape = (self.g.batch, self.g.n_q, self.g.latent_width)
         if out is None:
-            out = torch.empty(self.g.batch, self.g.n_q, self.g.latent_width, dtype=self.dtype, device=x.device)
+            out = torch.empty(shape, dtype=self.dtype, device=x.device)
+        _check_tensor(out, shape, self.dtype, self.device, "out")
         vmla_compress(self.ctx, x, frame0, out, stream)
         return out
 
@@ -363,13 +410,15 @@ class LatentAttention:
     def reset(self):
         vmla_reset(self.ctx)
 
+    def range_flags(self, stream=None) -> int:
+        """Read and clear the range flag (bit 0: an fp16 operand copy saturated)."""
+        return vmla_range_flags(self.ctx, stream)
+
     def attend_clip(self, x, out=None, stream=None):
         """Block-causal attention over a whole clip x [batch, window_frames*T, hidden]."""
         import torch
         g = self.g
-        shape = (g.batch, g.window_frames * g.tokens_per_frame, g.hidden)
-        if tuple(x.shape) != shape or x.dtype != self.dtype or not x.is_contiguous():
-            raise ValueError(f"x must be contiguous {self.dtype} of shape {shape}")
+        self._check_x(x, out, tokens=g.window_frames * g.tokens_per_frame)
         if getattr(self, "clip_workspace", None) is None:
             self.clip_workspace = torch.empty(vmla_clip_workspace_bytes(self.cfg), dtype=torch.uint8,
                                               device=self.cache.device)
@@ -391,7 +440,7 @@ class LatentAttention:
 
     def attend_expanded(self, x, out=None, stream=None):
         import torch
-        self._check_x(x)
+        self._check_x(x, out)
         if out is None:
             out = torch.empty_like(x)
         vmla_attend_expanded(self.ctx, getattr(self, "expanded", None), x, out, stream)
@@ -434,21 +483,31 @@ class DenseAttention:
         if cache_fill is not None:
             self.cache.view(torch.float16).fill_(cache_fill)
         self.workspace = torch.empty(wb, dtype=torch.uint8, device=device)
+        self.device = self.workspace.device
         wts = vmla_dense_weights(**{n: self.w[n].data_ptr() for n in self.WEIGHT_NAMES})
+        if rope_freqs is None:
+            rope_freqs = getattr(g, "rope_freqs", None)
         self.ctx = vmla_dense_create(self.cfg, wts, self.cache, self.workspace, rope_freqs)
+        vmla_dense_prepare(self.ctx)
 
-    def _check_x(self, x):
+    def _check_x(self, x, out=None):
         g = self.g
-        if tuple(x.shape) != (g.batch, g.n_q, g.hidden) or x.dtype != self.dtype or not x.is_contiguous():
-            raise ValueError(f"x must be contiguous {self.dtype} of shape {(g.batch, g.n_q, g.hidden)}")
+        shape = (g.batch, g.n_q, g.hidden)
+        _check_tensor(x, shape, self.dtype, self.device, "x")
+        if out is not None:
+            _check_tensor(out, shape, self.dtype, self.device, "out")
 
     def append(self, x, stream=None):
         self._check_x(x)
         vmla_dense_append(self.ctx, x, stream)
 
+    def range_flags(self, stream=None) -> int:
+        """Read and clear the range flag (bit 0: an fp16 operand copy saturated)."""
+        return vmla_dense_range_flags(self.ctx, stream)
+
     def attend(self, x, out=None, stream=None):
         import torch
-        self._check_x(x)
+        self._check_x(x, out)
         if out is None:
             out = torch.empty_like(x)
         vmla_dense_attend(self.ctx, x, out, stream)

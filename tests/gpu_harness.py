@@ -5,26 +5,21 @@ Parity metric (every attention comparison): max_abs = max |g - r| and
 mean_rel = sum |g - r| / sum |r| over all compared output elements, against the
 float64 oracle fed with the same (storage-rounded) inputs.
 
-Bar: max_abs <= 2e-2 and mean_rel <= 5e-3 -- the stated bar for the layer
-geometries' input recipe (weights and hidden states N(0,1)/sqrt(fan_in)), whose
-softmax is nearly flat (score spread sigma_s ~ 1e-3).  The steeper variants the
-tests add (unit hidden states, sharpened query projection) raise sigma_s to ~1
-and ~4.  With bf16 storage every score is a dot product of two rounded operands
-(cached latent row, absorbed query), so it carries an absolute error of order
-u*|s| (u = 2^-8, the bf16 rounding unit), and softmax turns a score error into
-the same relative error of that key's weight.  The derived bound is therefore
-mean_rel <= 5e-3 + u*sigma_s and max_abs <= 2e-2*max(1, max|r|); for the
-layer recipe it is the stated bar.  fp32 storage keeps the stated bar in every
-variant (its u is 2^-24).
+Bar: max_abs <= 2e-2 and mean_rel <= 5e-3.  Latent-layer comparisons with bf16
+storage are held to max(bar, 1.1 x floor), where the floor is the error that
+rounding the cache rows and the output to bf16 causes on its own on the same
+case (tests/rounding.py, pinned on the CPU by test_tolerance.py); for the layer
+recipe the floor is ~2e-3 and the bound is the stated bar.  The dense layer
+(fp16 cache) and fp32 storage are held to the stated bar.
 """
 from __future__ import annotations
 
 import numpy as np
 
+import rounding as rd
 from mla_latent_kv_vmla_amd import vmla, workloads as wl
 
-MAX_ABS, MEAN_REL = 2e-2, 5e-3
-U_BF16 = 2.0 ** -8
+MAX_ABS, MEAN_REL = rd.MAX_ABS, rd.MEAN_REL
 
 
 def to_dev(a, g):
@@ -37,23 +32,17 @@ def to_np(t):
 
 
 def parity(gpu: np.ndarray, ref: np.ndarray):
-    err = np.abs(gpu - ref)
-    return float(err.max()), float(err.sum() / np.abs(ref).sum())
+    return rd.parity(gpu, ref)
 
 
-def bounds(ref, sigma_s: float = 0.0, dtype: str = wl.BF16):
-    """(max_abs, mean_rel) bound for a comparison, see the module docstring."""
-    if dtype == wl.F32:
-        return MAX_ABS, MEAN_REL
-    return MAX_ABS * max(1.0, float(np.abs(ref).max())), MEAN_REL + U_BF16 * sigma_s
-
-
-def assert_parity(gpu, ref, what="", sigma_s: float = 0.0, dtype: str = wl.BF16):
+def assert_parity(gpu, ref, what="", floor=None):
+    """Assert the bound of a comparison whose floor (None: stated bar) is given."""
     ma, mr = parity(gpu, ref)
-    ba, br = bounds(ref, sigma_s, dtype)
+    ba, br = rd.bounds(floor)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    fl = "" if floor is None else f", floor mean_rel={floor[1]:.3e} max_abs={floor[0]:.3e}"
     assert ma <= ba and mr <= br, \
-        f"{what}: max_abs={ma:.3e} (bound {ba:.3e}) mean_rel={mr:.3e} (bound {br:.3e}, sigma_s={sigma_s:.3f})"
+        f"{what}: max_abs={ma:.3e} (bound {ba:.3e}) mean_rel={mr:.3e} (bound {br:.3e}{fl})"
     return ma, mr
 
 
@@ -87,14 +76,11 @@ class Rollout:
         from oracle import mla
         return mla.attend(self.g, self.w, self.hist[b], self.n, x_np[b], query_tokens=query_tokens)
 
-    def score_spread(self, x_np, b=0, query_tokens=None) -> float:
-        """Mean over (head, query) of the standard deviation of the natural-unit
-        scores over the visible keys, from the oracle."""
-        from oracle import mla
-        s = mla.scores(self.g, self.w, self.hist[b], self.n, x_np[b], query_tokens=query_tokens)
-        return float(s.std(axis=-1).mean())
-
-    def check(self, got_b, x_np, b=0, query_tokens=None, what=""):
-        ref = self.oracle(x_np, b, query_tokens)
-        sig = self.score_spread(x_np, b, query_tokens)
-        return assert_parity(got_b, ref, what, sig, self.g.dtype)
+    def check(self, got_b, x_np, b=0, query_tokens=None, what="", ref=None):
+        """Compare stream b's output (rows = query_tokens) with the oracle."""
+        if ref is None:
+            ref = self.oracle(x_np, b, query_tokens)
+        fl = None
+        if self.g.dtype == wl.BF16:
+            fl = rd.floor(self.g, self.w, self.hist[b], self.n, x_np[b], query_tokens, ref=ref)
+        return assert_parity(got_b, ref, what, fl)

@@ -3,11 +3,12 @@ oracle's attend_clip: chunk q of the clip attends to chunks 0..q (the
 training-time form of the layer).  Cases: the tiny fp32 layer, the Wan widths
 on a 6x10 grid with a 5-frame clip in 3-frame chunks (a shorter last block,
 row blocks straddling block boundaries; d_c = 192, 96 and 448), and the full 21-frame Wan clip
-(32,760 tokens, 7 blocks) on sampled queries of three blocks.  Same bar as the
-other GPU tests (gpu_harness)."""
+(32,760 tokens, 7 blocks) on sampled queries of three blocks, in the layer
+recipe and the sharpened one.  Same bar as the other GPU tests (gpu_harness)."""
 import numpy as np
 import pytest
 
+import rounding as rd
 from gpu_harness import Rollout, assert_parity, to_dev, to_np
 from mla_latent_kv_vmla_amd import workloads as wl
 from oracle import mla
@@ -31,22 +32,17 @@ def test_clip_matches_oracle(g, mode):
     got = to_np(r.dev.attend_clip(to_dev(x, g)))
     assert r.dev.state() == (0, 0, 0)  # the cache and counter are untouched
     ref = mla.attend_clip(g, r.w, x[0])
-    s = []
-    T, C = g.tokens_per_frame, g.chunk_frames
-    for q0 in range(0, g.window_frames, C):  # score spread per block for the derived bound
-        c = min(C, g.window_frames - q0)
-        hist = {f: x[0].reshape(g.window_frames, T, g.hidden)[f] for f in range(q0)}
-        s.append(mla.scores(g.replace(chunk_frames=c), r.w, hist, q0,
-                            x[0][q0 * T:(q0 + c) * T]).std(axis=-1).mean())
-    ma, mr = assert_parity(got[0], ref, f"clip {g.name} {mode}", float(np.mean(s)), g.dtype)
+    fl = rd.floor_clip(g, r.w, x[0], ref=ref) if g.dtype == wl.BF16 else None
+    ma, mr = assert_parity(got[0], ref, f"clip {g.name} {mode}", fl)
     print(f"  max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
 
 
-def test_clip_wan_full_size_sampled():
+@pytest.mark.parametrize("mode", ["literal", "sharp"])
+def test_clip_wan_full_size_sampled(mode):
     g = wl.WAN_LAYER
-    print("case: clip wan-full", flush=True)
-    r = Rollout(g, mode="literal")
-    x = _clip_x(g, "literal")
+    print("case: clip wan-full", mode, flush=True)
+    r = Rollout(g, mode=mode)
+    x = _clip_x(g, mode)
     got = to_np(r.dev.attend_clip(to_dev(x, g)))[0]
     assert np.all(np.isfinite(got))
     T, C, F = g.tokens_per_frame, g.chunk_frames, g.window_frames
@@ -54,8 +50,9 @@ def test_clip_wan_full_size_sampled():
     rng = np.random.default_rng(5)
     for q in (0, 3, 6):
         q0 = q * C
-        sample = np.unique(np.concatenate([[0, C * T - 1], rng.choice(C * T, 14, replace=False)]))
-        ref = mla.attend(g, r.w, {f: frames[f] for f in range(q0)}, q0, x[0][q0 * T:(q0 + C) * T],
-                         query_tokens=sample)
-        ma, mr = assert_parity(got[q0 * T + sample], ref, f"clip wan block {q}")
+        sample = np.unique(np.concatenate([[0, C * T - 1], rng.choice(C * T, 30, replace=False)]))
+        hist = {f: frames[f] for f in range(q0)}
+        ref = mla.attend(g, r.w, hist, q0, x[0][q0 * T:(q0 + C) * T], query_tokens=sample)
+        fl = rd.floor(g, r.w, hist, q0, x[0][q0 * T:(q0 + C) * T], sample, ref=ref)
+        ma, mr = assert_parity(got[q0 * T + sample], ref, f"clip wan block {q} {mode}", fl)
         print(f"  block {q}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)

@@ -1,8 +1,9 @@
 """Parity of the dense per-head baseline (through the vmla_dense_* C ABI) with
 the CPU oracle's attend_dense.
 
-Same bar and tolerance derivation as the latent path (gpu_harness): keys and
-queries are rounded to bf16 once, values to fp16, probabilities to fp16.
+Held to the stated bar (max_abs <= 2e-2, mean_rel <= 5e-3) in every input
+recipe: keys, values and queries are fp16 (the dense cache stores fp16), so the
+unavoidable roundings are the fp16 cache and the bf16 output.
 Cases: the Wan widths (12 heads x 128) on a 6x10 grid over empty, partial,
 full and wrapped windows with NaN canaries in every unwritten cache byte, two
 input scalings, batched streams, stream-K cuts, and the full Wan-1.3B layer
@@ -33,6 +34,7 @@ class DenseRollout:
                                        attn_workgroups=attn_workgroups)
         self.dev.cache.fill_(255)      # NaN in both bf16 and fp16: reading an unwritten byte shows
         self.dev.workspace.fill_(255)
+        vmla.vmla_dense_prepare(self.dev.ctx)  # the persistent part (fp16 W_O, range flag) again
         torch.cuda.synchronize()
         self.hist = [dict() for _ in range(g.batch)]
         self.n = 0
@@ -50,9 +52,8 @@ class DenseRollout:
         self.n += g.chunk_frames
 
     def check(self, got_b, x_np, b=0, query_tokens=None, what=""):
-        ref, s = mla.attend_dense(self.g, self.w, self.hist[b], self.n, x_np[b], query_tokens=query_tokens,
-                                  return_scores=True)
-        return assert_parity(got_b, ref, what, float(s.std(axis=-1).mean()), self.g.dtype)
+        ref = mla.attend_dense(self.g, self.w, self.hist[b], self.n, x_np[b], query_tokens=query_tokens)
+        return assert_parity(got_b, ref, what)
 
 
 def _dense_rollout(g, mode, n_chunks, attn_workgroups=0):
@@ -84,18 +85,20 @@ def test_dense_batched_streams():
     _dense_rollout(SMALL.replace(batch=2, window_frames=4), "sharp", n_chunks=3)
 
 
-def test_dense_wan_layer_full_size_sampled():
+@pytest.mark.parametrize("mode", ["literal", "sharp"])
+def test_dense_wan_layer_full_size_sampled(mode):
     """21 cached frames (32,760 keys per head) + a 3-frame chunk (4,680 queries x
     12 heads), default launch configuration."""
     g = wl.WAN_DENSE
-    _print_case("dense wan-full")
-    r = DenseRollout(g, mode="literal")
+    _print_case("dense wan-full", mode)
+    r = DenseRollout(g, mode=mode)
     for k in range(g.prefill_chunks):
         r.append(r.x(chunk=k))
     x = r.x(chunk=g.prefill_chunks)
     got = to_np(r.dev.attend(to_dev(x, g)))
     assert np.all(np.isfinite(got))
     q = np.unique(np.concatenate([np.arange(8), np.arange(g.n_q - 8, g.n_q),
-                                  np.random.default_rng(0).choice(g.n_q, 32, replace=False)]))
-    ma, mr = r.check(got[0][q], x, 0, q, "dense wan-full literal")
-    print(f"dense wan-full: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+                                  np.random.default_rng(0).choice(g.n_q, 64, replace=False)]))
+    ma, mr = r.check(got[0][q], x, 0, q, f"dense wan-full {mode}")
+    print(f"dense wan-full {mode}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+    assert r.dev.range_flags() == 0

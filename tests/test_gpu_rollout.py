@@ -9,13 +9,17 @@ of (k, s) rolled by 37*l tokens (same distribution, cheap to rebuild on both
 sides).  Sampled (layer, chunk) attends -- empty, partial, just-full and
 wrapped windows -- are compared with the oracle on sampled query tokens.
 
+A second rollout runs one layer in the sharpened recipe through all 20 chunks
+and compares the last three chunks (absolute frames 51-59).
+
 Stress (B = 4 streams, 42-frame window = 65,520 cached keys, d_c in
-{96, 192, 448}): prefill the ring, then one attend, compared on sampled
-query tokens of two streams.
+{96, 192, 448}, layer recipe and sharpened): prefill the ring, then one
+attend, compared on sampled query tokens of the first and last stream.
 """
 import numpy as np
 import pytest
 
+import rounding as rd
 from gpu_harness import assert_parity, to_dev, to_np
 from mla_latent_kv_vmla_amd import vmla, workloads as wl
 from oracle import mla
@@ -77,15 +81,53 @@ def test_rollout_30_layers_20_chunks():
         lay.close()
 
 
+def test_rollout_sharp_late_chunks():
+    """One layer of the rollout in the sharpened recipe (peaked softmax, scores
+    that see every rotary and content error) through all 20 chunks x (4 attends +
+    1 append); the late chunks -- frames 51-53, 54-56 and 57-59 attending to
+    windows that start at absolute frame 30-36 -- are compared on 64 query tokens."""
+    import torch
+    g = wl.WAN_ROLLOUT
+    K, S = g.chunks, g.steps
+    w = wl.latent_weights(g, mode="sharp")
+    layer = vmla.LatentAttention(g, {n: to_dev(v, g) for n, v in w.as_dict().items()}, cache_fill=float("nan"))
+    q = np.unique(np.concatenate([np.arange(4), np.arange(g.n_q - 4, g.n_q),
+                                  np.random.default_rng(2).choice(g.n_q, 56, replace=False)]))
+    hist, pending = {}, []
+    out = torch.empty(g.batch, g.n_q, g.hidden, dtype=torch.bfloat16, device="cuda")
+    for k in range(K):
+        xs = [wl.hidden_states(g, chunk=k, step=s, mode="sharp") for s in range(S)]
+        for s in range(S):
+            layer.attend(to_dev(xs[s], g), out=out)
+            if k >= K - 3 and s == S - 1:
+                pending.append((k, xs[s][0], to_np(out)[0][q], dict(hist)))
+        layer.append(to_dev(xs[S - 1], g))
+        fr = xs[S - 1][0].reshape(g.chunk_frames, g.tokens_per_frame, g.hidden)
+        for i in range(g.chunk_frames):
+            hist[k * g.chunk_frames + i] = fr[i]
+    torch.cuda.synchronize()
+    _case("rollout sharp: 20 chunks done")
+    assert layer.state() == (K * g.chunk_frames, K * g.chunk_frames - g.window_frames, g.window_frames)
+    for k, xq, got, h in pending:
+        n = k * g.chunk_frames
+        ref = mla.attend(g, w, h, n, xq, query_tokens=q)
+        fl = rd.floor(g, w, h, n, xq, q, ref=ref)
+        ma, mr = assert_parity(got, ref, f"rollout sharp chunk {k}", fl)
+        print(f"  sharp chunk {k} (frames {n}-{n + 2}): max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+    assert layer.range_flags() == 0
+    layer.close()
+
+
+@pytest.mark.parametrize("mode", ["literal", "sharp"])
 @pytest.mark.parametrize("dc", [96, 192, 448])
-def test_stress_b4_w42_full_size(dc):
+def test_stress_b4_w42_full_size(dc, mode):
     g = wl.STRESS[dc]
-    _case("stress", g.name)
-    w = wl.latent_weights(g, mode="literal")
+    _case("stress", g.name, mode)
+    w = wl.latent_weights(g, mode=mode)
     layer = vmla.LatentAttention(g, {n: to_dev(v, g) for n, v in w.as_dict().items()}, cache_fill=float("nan"))
     hist = [dict() for _ in range(g.batch)]
     for k in range(g.prefill_chunks):
-        xk = wl.hidden_states(g, chunk=k)
+        xk = wl.hidden_states(g, chunk=k, mode=mode)
         layer.append(to_dev(xk, g))
         for b in range(g.batch):
             fr = xk[b].reshape(g.chunk_frames, g.tokens_per_frame, g.hidden)
@@ -93,13 +135,15 @@ def test_stress_b4_w42_full_size(dc):
                 hist[b][k * g.chunk_frames + i] = fr[i]
     n = layer.state()[0]
     assert n == g.window_frames
-    x = wl.hidden_states(g, chunk=g.prefill_chunks)
+    x = wl.hidden_states(g, chunk=g.prefill_chunks, mode=mode)
     got = to_np(layer.attend(to_dev(x, g)))
     assert np.all(np.isfinite(got))
     q = np.unique(np.concatenate([np.arange(4), np.arange(g.n_q - 4, g.n_q),
-                                  np.random.default_rng(dc).choice(g.n_q, 16, replace=False)]))
+                                  np.random.default_rng(dc).choice(g.n_q, 24, replace=False)]))
     for b in (0, g.batch - 1):
         ref = mla.attend(g, w, hist[b], n, x[b], query_tokens=q)
-        ma, mr = assert_parity(got[b][q], ref, f"{g.name} b={b}")
-        print(f"  {g.name} b={b}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+        fl = rd.floor(g, w, hist[b], n, x[b], q, ref=ref)
+        ma, mr = assert_parity(got[b][q], ref, f"{g.name} {mode} b={b}", fl)
+        print(f"  {g.name} {mode} b={b}: max_abs={ma:.3e} mean_rel={mr:.3e}", flush=True)
+    assert layer.range_flags() == 0
     layer.close()
