@@ -49,7 +49,8 @@ enum {
   VMLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
   VMLA_ERR_STATE = 5,       /* call not valid in the ctx's current state */
   VMLA_ERR_ARG = 6,         /* another argument out of range */
-  VMLA_ERR_HIP = 7          /* the HIP runtime reported an error for a launch */
+  VMLA_ERR_HIP = 7,         /* the HIP runtime reported an error for a launch */
+  VMLA_ERR_SCRATCH = 8      /* per-call buffers larger than VMLA_SCRATCH_BYTES (vmla_attend_noalloc) */
 };
 
 enum { VMLA_DTYPE_BF16 = 0, VMLA_DTYPE_F32 = 1 };
@@ -211,6 +212,25 @@ VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t st
  * VMLA_ERR_NULL. */
 VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEvent_t attn_start,
                                   hipEvent_t attn_stop, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): vmla_attend
+ * with the per-call buffers (chunk latents, c^Q, absorbed queries, latent and
+ * per-head outputs, partial softmax states, key tiles) taken from a scratch
+ * array inside the library instead of the ctx's workspace.  The array holds
+ * VMLA_SCRATCH_BYTES (128 MiB) on every GPU the library runs on, from when its
+ * code is loaded there until the process ends -- enough for one Wan-1.3B layer
+ * call (4,680 query tokens against 37,440 keys needs ~118 MiB).  The ctx must
+ * be prepared; only the persistent part of its workspace (prepared weights,
+ * range flag) is read.  Same inputs, outputs and results as vmla_attend.
+ * Allocates nothing and needs no free call.  Errors: VMLA_ERR_SCRATCH if the
+ * ctx's per-call buffers exceed VMLA_SCRATCH_BYTES (larger batch or chunk),
+ * else as vmla_attend.  Every call on one GPU uses the same array and leaves it
+ * holding that call's buffers; nothing is assumed about its contents at entry.
+ * Calls that overlap on one GPU (several streams or host threads at once) race
+ * on it: issue them in one stream order. */
+#define VMLA_SCRATCH_BYTES ((size_t)128 << 20)
+VMLA_API int vmla_attend_noalloc(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream);
 
 /* Test hook: compute the cache rows [c | RoPE(k^)] of x ([batch, C*T, hidden])
  * as frames frame0..frame0+C-1 into latents_out ([batch, C*T, d_c+d_rope]) --

@@ -41,8 +41,8 @@ def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
     tiles = (-(-(g.sink_frames + g.window_frames) * g.tokens_per_frame // key_tile)
              + -(-g.n_q // key_tile))
     persistent = [4, nh * D * g.d_q * es, nh * dh * g.d_q * es, nh * g.d_v * g.d_c * es, g.hidden * nh * g.d_v * es]
-    per_call = [M * D * es, M * g.d_q * es, M * nh * D * es, M * nh * g.d_c * es,
-                M * nh * g.d_v * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
+    per_call = [M * D * es, M * g.d_q * es, M * nh * max(D, g.d_v) * es,  # absorbed queries, then per-head outputs
+                M * nh * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
                 # pre-pass tiles: fp16 key tiles (16-bit storage), transposed value images (fp32)
                 batch * tiles * key_tile * D * 2 if es == 2 else batch * tiles * dcp * (key_tile + 16 // es) * es,
                 # rotated copy of the visible rows: rotation at use with fp32 storage only

@@ -51,7 +51,7 @@ struct Plan {
   void *cq;      // [B][Nq][dq]           query latent
   void *qt;      // [B][Nq][nh][D]        absorbed query [W_UK^T q_nope | q_rope] * qscale
   void *olat;    // [B][Nq][nh][dc]       attention output in latent space
-  void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV
+  void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV (same bytes as qt)
   float *part_o; // [2G][kAttnMaxRows][dc] normalised partial outputs (activation type)
   float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
   void *vtiles;  // pre-pass tiles of the visible keys (per call): fp16 key tiles for bf16, value images for fp32

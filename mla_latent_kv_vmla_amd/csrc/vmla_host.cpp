@@ -4,7 +4,9 @@
 // runs before anything is enqueued; only the run_* pipelines touch HIP.
 #include "vmla.h"
 
+#include <hip/hip_runtime.h>
 #include <math.h>
+#include <mutex>
 #include <new>
 #include <string.h>
 
@@ -177,9 +179,11 @@ WorkspaceLayout workspace_layout(const Plan& p) {
   off = 0;
   L.stage = take(M * p.D * es);
   L.cq = take(M * p.dq * as);
-  L.qt = take(M * p.nh * (size_t)p.D * as);
+  // the per-head outputs reuse the absorbed queries' bytes: the queries are dead
+  // once the attention kernel has run, before W_UV writes them
+  L.qt = take(M * p.nh * (size_t)(p.D > p.dv ? p.D : p.dv) * as);
+  L.o = L.qt;
   L.olat = take(M * p.nh * (size_t)p.dc * as);
-  L.o = take(M * p.nh * (size_t)p.dv * as);
   L.part_o = take((size_t)2 * p.G * kAttnMaxRows * p.dc * as);
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
   L.vtiles = take(latent_prepass_bytes(p.dtype, p.dc, p.dr, p.B, (p.S + p.W) * p.Tpf, p.Nq));
@@ -405,6 +409,48 @@ VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEv
   if (!ctx->prepared) return VMLA_ERR_STATE;
   Plan p = make_plan(ctx);
   if (vmla::run_attend(p, ctx->n, x, out, stream, attn_start, attn_stop) != hipSuccess) return VMLA_ERR_HIP;
+  return VMLA_OK;
+}
+
+/* ------------------------------------------------------- allocation-free attend */
+
+// Per-call buffers of vmla_attend_noalloc: one array per GPU, in the library's
+// device code, allocated when the code object is loaded on that GPU and held
+// until the process ends.  Its name is only a host-side stand-in for the
+// symbol: host code uses the address hipGetSymbolAddress reports per device.
+static __device__ __align__(256) unsigned char scratch[VMLA_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, set on first use
+
+// Device address of the current device's scratch array (nullptr on failure).
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+VMLA_API int vmla_attend_noalloc(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream) {
+  if (!ctx || !x || !out) return VMLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return VMLA_ERR_ALIGN;
+  if (!ctx->prepared) return VMLA_ERR_STATE;
+  Plan p = geometry(&ctx->cfg);
+  set_ctx_pointers(p, ctx);
+  const vmla::WorkspaceLayout L = vmla::workspace_layout(p);
+  if (L.per_call > VMLA_SCRATCH_BYTES) return VMLA_ERR_SCRATCH;
+  void* base = device_scratch();
+  if (!base) return VMLA_ERR_HIP;
+  set_per_call(p, L, base);
+  if (vmla::run_attend(p, ctx->n, x, out, stream) != hipSuccess) return VMLA_ERR_HIP;
   return VMLA_OK;
 }
 
@@ -701,6 +747,7 @@ VMLA_API const char* vmla_status_string(int status) {
     case VMLA_ERR_STATE: return "call not valid in the current state";
     case VMLA_ERR_ARG: return "argument out of range";
     case VMLA_ERR_HIP: return "HIP runtime error on launch";
+    case VMLA_ERR_SCRATCH: return "per-call buffers exceed the library's scratch array (VMLA_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

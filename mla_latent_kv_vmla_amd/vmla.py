@@ -83,6 +83,8 @@ def lib():
         L.vmla_compress_append.restype = c_int
         L.vmla_attend.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
         L.vmla_attend.restype = c_int
+        L.vmla_attend_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p]
+        L.vmla_attend_noalloc.restype = c_int
         L.vmla_attend_profiled.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.vmla_attend_profiled.restype = c_int
         L.vmla_compress.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]
@@ -193,6 +195,10 @@ def vmla_compress_append(ctx, x, stream=None) -> None:
 
 def vmla_attend(ctx, x, out, stream=None) -> None:
     _check(lib().vmla_attend(ctx, _ptr(x), _ptr(out), _stream(stream)), "vmla_attend")
+
+
+def vmla_attend_noalloc(ctx, x, out, stream=None) -> None:
+    _check(lib().vmla_attend_noalloc(ctx, _ptr(x), _ptr(out), _stream(stream)), "vmla_attend_noalloc")
 
 
 def vmla_attend_profiled(ctx, x, out, attn_start: int, attn_stop: int, stream=None) -> None:

@@ -134,6 +134,13 @@ def test_calls_reject_bad_arguments_before_launch():
             (lambda: vmla.vmla_compress_append(ctx, FAKE + 8, 0), "VMLA_ERR_ALIGN"),
             (lambda: vmla.vmla_compress(ctx, FAKE, -1, FAKE, 0), "VMLA_ERR_ARG"),
             (lambda: vmla.vmla_compress(ctx, FAKE, 0, 0, 0), "VMLA_ERR_NULL"),
+            # attend-type calls before vmla_prepare
+            (lambda: vmla.vmla_attend(ctx, FAKE, FAKE, 0), "VMLA_ERR_STATE"),
+            (lambda: vmla.vmla_attend_noalloc(ctx, FAKE, FAKE, 0), "VMLA_ERR_STATE"),
+            (lambda: vmla.vmla_attend_noalloc(ctx, 0, FAKE, 0), "VMLA_ERR_NULL"),
+            (lambda: vmla.vmla_attend_noalloc(ctx, FAKE, FAKE + 4, 0), "VMLA_ERR_ALIGN"),
+            (lambda: vmla.vmla_attend_clip(ctx, FAKE, FAKE, FAKE, 0), "VMLA_ERR_STATE"),
+            (lambda: vmla.vmla_range_flags(ctx, 0), "VMLA_ERR_STATE"),
         ]
         for f, code in bad:
             with pytest.raises(vmla.VmlaError) as e:
