@@ -165,7 +165,9 @@ VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* ca
                          void* workspace, const float* rope_freqs, vmla_ctx** out);
 
 /* Enqueue the one-time set-up of a ctx: clear its range flag and write, into
- * the persistent part of the workspace, the weights in the activation type:
+ * the persistent part of the workspace, [W_DKV; W_KR; W_DQ] (storage type: the
+ * chunk's cache rows and c^Q come from one GEMM over x) and the weights in the
+ * activation type:
  *   absorbed query weight, per head h, the [d_c + d_rope, d_q] block
  *     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope]  (qscale = log2(e)/sqrt(d_h)),
  *   so one GEMM from c^Q gives the absorbed query q~_h = W_UK^h^T q^nope_h

@@ -32,7 +32,8 @@ def latent_cache_bytes(g, batch: int = 1, es: int = 2) -> int:
 def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
                            workgroups: int = DEFAULT_WORKGROUPS, part: str = "total") -> int:
     """Mirror of the library's latent workspace layout for `batch` streams:
-    part = "persistent" (range flag and the prepared weights, per layer),
+    part = "persistent" (range flag and the prepared weights, per layer:
+    [W_DKV; W_KR; W_DQ], the absorbed query weight, W_UQ, W_UV, W_O),
     "per_call" (the buffers of one attend) or "total".  The activation type has
     the storage type's width (fp16 for bf16, fp32 for fp32)."""
     M = batch * g.n_q
@@ -40,7 +41,8 @@ def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
     dcp = (g.d_c + 31) // 32 * 32
     tiles = (-(-(g.sink_frames + g.window_frames) * g.tokens_per_frame // key_tile)
              + -(-g.n_q // key_tile))
-    persistent = [4, nh * D * g.d_q * es, nh * dh * g.d_q * es, nh * g.d_v * g.d_c * es, g.hidden * nh * g.d_v * es]
+    persistent = [4, (D + g.d_q) * g.hidden * es, nh * D * g.d_q * es, nh * dh * g.d_q * es, nh * g.d_v * g.d_c * es,
+                  g.hidden * nh * g.d_v * es]
     per_call = [M * D * es, M * g.d_q * es, M * nh * max(D, g.d_v) * es,  # absorbed queries, then per-head outputs
                 M * nh * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
                 # pre-pass tiles: fp16 key tiles (16-bit storage), transposed value images (fp32)

@@ -11,7 +11,7 @@
 //     roles swapped, so each lane holds 4 consecutive keys of one value channel
 //     and stores them together), then the value columns past the valid keys are
 //     zeroed up to the key-tile boundary.
-//   attend: compress the chunk into staging (latent path), c^Q = W_DQ x, the
+//   attend: the chunk's cache rows into staging and c^Q = W_DQ x (latent path), the
 //     per-head queries [q_nope | RoPE(q_rope)] (not absorbed; the prepared
 //     qscale * W_UQ), the chunk's own keys and values by the same up-projection,
 //     dense flash attention over the expanded window + chunk (attention.hip),
@@ -163,12 +163,8 @@ hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* w
                                void* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int M = p.B * p.Nq;
   const int64_t tq = p.rope_at_use ? cached_frames(p, n) : n;  // temporal coordinate of the chunk's first frame
-  hipError_t err = run_compress(p, x, tq, p.stage, false, s);
+  hipError_t err = run_chunk_rows_and_cq(p, x, tq, s);  // the chunk's cache rows and c^Q, one GEMM
   if (err != hipSuccess) return err;
-  {  // c^Q = W_DQ x (fp16)
-    EpiStore<f16> e{static_cast<f16*>(p.cq), p.dq, 0, p.flags};
-    gemm<bf16, false>(gops(p.w_dq, p.d, 0, x, p.d, 0, p.dq, M, p.d), 1, e, s);
-  }
   {  // per-head queries, not absorbed
     EpiQueryHead e;
     e.q = static_cast<f16*>(ex.q);

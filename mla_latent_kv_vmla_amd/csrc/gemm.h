@@ -170,7 +170,7 @@ template <typename O> struct EpiStore {
 
 // Tile shape: the largest of (features x tokens) = 128x128, 128x64, 64x128,
 // 64x64 that wastes at most 15% of the padded tile area and still launches
-// >= 384 workgroups (1.5 per compute unit); otherwise the shape with the most
+// >= 256 workgroups (one per compute unit); otherwise the shape with the most
 // workgroups.
 template <typename T, bool W_KN, class Epi>
 inline void gemm(const GemmOps<T>& op, int Z, const Epi& epi, hipStream_t s) {
@@ -182,7 +182,7 @@ inline void gemm(const GemmOps<T>& op, int Z, const Epi& epi, hipStream_t s) {
     const long tn = (op.N + bn - 1) / bn, tm = (op.M + bm - 1) / bm;
     const long wg = tn * tm * Z;
     const double waste = (double)(tn * bn) * (tm * bm) / ((double)op.N * op.M);
-    if (pick < 0 && waste <= 1.15 && wg >= 384) pick = i;
+    if (pick < 0 && waste <= 1.15 && wg >= 256) pick = i;
     if (wg > best_wg) best_wg = wg, best = i;
   }
   if (pick < 0) pick = best;

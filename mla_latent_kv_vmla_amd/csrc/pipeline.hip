@@ -1,7 +1,8 @@
 // Launch sequences of the two library calls and the GEMM epilogues they use.
 //
-//   prepare (once per ctx): the weights the activation-type GEMMs consume, in
-//     that type (fp16 for bf16 storage): the absorbed query weight
+//   prepare (once per ctx): the concatenation [W_DKV; W_KR; W_DQ] (storage
+//     type), and the weights the activation-type GEMMs consume, in that type
+//     (fp16 for bf16 storage): the absorbed query weight
 //     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] per head (the MLA
 //     absorption, VideoMLA paper section 3.3, taken into the weight so one GEMM
 //     yields the absorbed query), qscale * W_UQ, W_UV and W_O.
@@ -11,10 +12,11 @@
 //     type and scatters each token's row to its ring slot (slot * T + s; frames
 //     f < S take sink slot f, later ones slot S + (f - S) % W) or to a linear
 //     buffer.
-//   attend: compress the chunk into staging; with rope_at_use and fp32
+//   attend: the chunk's cache rows into staging and c^Q = W_DQ x (one GEMM over
+//     x with the prepared [W_DKV; W_KR; W_DQ]); with rope_at_use and fp32
 //     storage, rotate the visible ring rows at their window-local coordinates
 //     into the workspace (assemble_window; with bf16 storage the attention
-//     pre-pass rotates them); c^Q = W_DQ x; absorbed query = prepared weight . c^Q
+//     pre-pass rotates them); absorbed query = prepared weight . c^Q
 //     with the rotary channels turned in the epilogue; latent attention
 //     (attention.hip); o_h = W_UV^h o~_h; out = W_O o.  Everything between x
 //     and out is held in the activation type.
@@ -87,6 +89,22 @@ template <typename A> struct EpiQueryAbs {
   }
 };
 
+// One GEMM over the chunk's hidden states with the prepared weight [W_DKV; W_KR;
+// W_DQ]: features [0, D) are the chunk's cache rows (EpiLatent to the staging
+// buffer), features [D, D + d_q) are c^Q (activation type).  The row features
+// accumulate in the same k order as in a compress alone, so the staged rows
+// are the ones an append of the same x would write.
+template <typename T, typename A> struct EpiLatentCq {
+  EpiLatent<T> lat;
+  A* cq;
+  int dq;
+  uint32_t* flag;
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    if (n < lat.D) lat(z, m, n, v);
+    else store4(cq + (long)m * dq + (n - lat.D), v[0], v[1], v[2], v[3], flag);
+  }
+};
+
 // ---------------------------------------------------------------- prepare
 // Absorbed query weight, head h = row / D, channel j = row % D, column k:
 //   j <  dc: qscale * sum_i W_UK^h[i][j] * W_UQ[h*dh + i][k]   (i < d_nope)
@@ -129,6 +147,14 @@ __global__ __launch_bounds__(256) void convert_weight(A* dst, const T* src, long
   raise_range_flag(over, flag);
 }
 
+// Plain copy of n elements (16-byte vectors; n a multiple of 16 B / sizeof(T)).
+template <typename T>
+__global__ __launch_bounds__(256) void copy_rows(T* dst, const T* src, long n) {
+  const long nv = n * (long)sizeof(T) / 16;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < nv; i += (long)gridDim.x * 256)
+    reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
+}
+
 __global__ void clear_flags(uint32_t* flags) { *flags = 0u; }
 
 hipError_t run_clear_flags(uint32_t* flags, hipStream_t s) {
@@ -141,6 +167,13 @@ static int grid_for(long n) { return (int)((n + 255) / 256 < 2048 ? (n + 255) / 
 template <typename T, typename A>
 static void prepare_t(const Plan& p, hipStream_t s) {
   clear_flags<<<1, 1, 0, s>>>(p.flags);
+  {  // [W_DKV; W_KR; W_DQ], storage type, rows of `hidden`
+    T* wx = static_cast<T*>(p.wx);
+    const long a = (long)p.dc * p.d, b = (long)p.dr * p.d, c = (long)p.dq * p.d;
+    copy_rows<T><<<grid_for(a * (long)sizeof(T) / 16), 256, 0, s>>>(wx, static_cast<const T*>(p.w_dkv), a);
+    copy_rows<T><<<grid_for(b * (long)sizeof(T) / 16), 256, 0, s>>>(wx + a, static_cast<const T*>(p.w_kr), b);
+    copy_rows<T><<<grid_for(c * (long)sizeof(T) / 16), 256, 0, s>>>(wx + a + b, static_cast<const T*>(p.w_dq), c);
+  }
   const long nqa = (long)p.nh * p.D * p.dq;
   derive_query_weight<T, A><<<grid_for(nqa), 256, 0, s>>>(static_cast<A*>(p.wqa), static_cast<const T*>(p.w_uq),
                                                           static_cast<const T*>(p.w_uk), p.nh, p.d_nope, p.dr, p.dc,
@@ -177,11 +210,7 @@ static GemmOps<T> ops(const void* w, long ldw, long wz, const void* x, long ldx,
 }
 
 template <typename T>
-static void compress_t(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring, hipStream_t s) {
-  const int M = p.B * p.Nq;
-  GemmOps<T> op = ops<T>(p.w_dkv, p.d, 0, x, p.d, 0, p.D, M, p.d);
-  op.w2 = static_cast<const T*>(p.w_kr);
-  op.n_split = p.dc;
+static EpiLatent<T> latent_epilogue(const Plan& p, int64_t frame0, void* dst, bool ring) {
   EpiLatent<T> e;
   e.dst = static_cast<T*>(dst);
   e.bstride = ring ? (long)(p.S + p.W) * p.Tpf * p.D : (long)p.Nq * p.D;
@@ -194,7 +223,32 @@ static void compress_t(const Plan& p, const void* x, int64_t frame0, void* dst, 
   e.ring = ring ? 1 : 0;
   e.rotate = ring && p.rope_at_use ? 0 : 1;
   e.rope = make_rope(p);
-  gemm<T, false>(op, 1, e, s);
+  return e;
+}
+
+template <typename T>
+static void compress_t(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring, hipStream_t s) {
+  const int M = p.B * p.Nq;
+  GemmOps<T> op = ops<T>(p.w_dkv, p.d, 0, x, p.d, 0, p.D, M, p.d);
+  op.w2 = static_cast<const T*>(p.w_kr);
+  op.n_split = p.dc;
+  gemm<T, false>(op, 1, latent_epilogue<T>(p, frame0, dst, ring), s);
+}
+
+// The chunk's cache rows (rotated at frame frame0.., into p.stage) and c^Q
+// (into p.cq), one GEMM with the prepared [W_DKV; W_KR; W_DQ].
+template <typename T>
+static void chunk_rows_and_cq_t(const Plan& p, const void* x, int64_t frame0, hipStream_t s) {
+  using A = typename std::conditional<sizeof(T) == 2, f16, float>::type;
+  const int M = p.B * p.Nq;
+  EpiLatentCq<T, A> e{latent_epilogue<T>(p, frame0, p.stage, false), static_cast<A*>(p.cq), p.dq, p.flags};
+  gemm<T, false>(ops<T>(p.wx, p.d, 0, x, p.d, 0, p.D + p.dq, M, p.d), 1, e, s);
+}
+
+hipError_t run_chunk_rows_and_cq(const Plan& p, const void* x, int64_t frame0, hipStream_t s) {
+  if (p.dtype == DType::F32) chunk_rows_and_cq_t<float>(p, x, frame0, s);
+  else chunk_rows_and_cq_t<bf16>(p, x, frame0, s);
+  return hipGetLastError();
 }
 
 // rope_at_use: visible cache row r of stream b (slot r / T, token r % T) with
@@ -253,15 +307,11 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
   const int M = p.B * p.Nq;
   // temporal coordinate of the chunk's first frame: absolute, or local (after the visible cached frames)
   const int64_t tq = p.rope_at_use ? cached_frames(p, n) : n;
-  compress_t<T>(p, x, tq, p.stage, false, s);
+  chunk_rows_and_cq_t<T>(p, x, tq, s);  // the chunk's cache rows and c^Q = W_DQ x, one GEMM
   // rotation at use: fp32 storage rotates the visible rows into a copy; bf16
   // storage lets the attention pre-pass turn them as it converts them to fp16
   const bool rot_in_prepass = p.rope_at_use && sizeof(T) == 2;
   if (p.rope_at_use && !rot_in_prepass) assemble_t<T>(p, n, s);
-  {  // c^Q = W_DQ x (storage-type operands, activation-type result)
-    EpiStore<A> e{static_cast<A*>(p.cq), p.dq, 0, p.flags};
-    gemm<T, false>(ops<T>(p.w_dq, p.d, 0, x, p.d, 0, p.dq, M, p.d), 1, e, s);
-  }
   {  // absorbed query [qscale W_UK^T q_nope | RoPE(qscale q_rope)] per head, one GEMM from c^Q
     EpiQueryAbs<A> e;
     e.qt = static_cast<A*>(p.qt);

@@ -42,6 +42,7 @@ struct Plan {
   void* cache;   // [B][(S+W)*Tpf][D]
   // persistent workspace (written by run_prepare)
   uint32_t* flags;  // bit 0: an fp16 operand copy saturated (see kF16Max)
+  void *wx;      // [D + dq][d]   [W_DKV; W_KR; W_DQ] in the storage type
   void *wqa;     // [nh][D][dq]   absorbed query weight: per head qscale*[W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope]
   void *wuq;     // [nh*dh][dq]   qscale * W_UQ (per-head queries of the expanded path)
   void *wuv;     // [nh][dv][dc]  W_UV
@@ -69,7 +70,7 @@ inline int64_t cached_frames(const Plan& p, int64_t n) {
 // prepared weights) sits at the start of a ctx's workspace; the per-call part
 // follows it there, or fills a clip workspace of its own.
 struct WorkspaceLayout {
-  size_t flags, wqa, wuq, wuv, wo, persistent;                           // from the workspace start
+  size_t flags, wx, wqa, wuq, wuv, wo, persistent;                       // from the workspace start
   size_t stage, cq, qt, olat, o, part_o, part_ml, vtiles, assembled, per_call;  // from the per-call start
   size_t total;  // persistent + per_call
 };
@@ -89,6 +90,9 @@ hipError_t run_clear_flags(uint32_t* flags, hipStream_t s);
 // unless the rows go to the ring of a rope_at_use layer (stored un-rotated).
 hipError_t run_compress(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring,
                         hipStream_t s);
+// The chunk's cache rows (frames frame0.., into p.stage) and c^Q (into p.cq)
+// from one GEMM with the prepared [W_DKV; W_KR; W_DQ].
+hipError_t run_chunk_rows_and_cq(const Plan& p, const void* x, int64_t frame0, hipStream_t s);
 // rope_at_use with fp32 storage: the visible cache rows after n appends, k^
 // rotated with each frame's local coordinate, into p.assembled.  (With bf16
 // storage the rotation happens where the rows are converted: the attention

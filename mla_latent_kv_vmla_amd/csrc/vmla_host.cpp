@@ -171,6 +171,7 @@ WorkspaceLayout workspace_layout(const Plan& p) {
     return o;
   };
   L.flags = take(sizeof(uint32_t));
+  L.wx = take((size_t)(p.D + p.dq) * p.d * es);
   L.wqa = take((size_t)p.nh * p.D * p.dq * as);
   L.wuq = take((size_t)p.nh * p.dh * p.dq * as);
   L.wuv = take((size_t)p.nh * p.dv * p.dc * as);
@@ -350,6 +351,7 @@ static void set_ctx_pointers(Plan& p, const vmla_ctx* c) {
   const vmla::WorkspaceLayout L = vmla::workspace_layout(geometry(&c->cfg));
   char* ws = static_cast<char*>(c->workspace);
   p.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  p.wx = ws + L.wx;
   p.wqa = ws + L.wqa;
   p.wuq = ws + L.wuq;
   p.wuv = ws + L.wuv;
