@@ -1386,7 +1386,7 @@ static bool latent_shape(DType dt, int dc, int dr, LatentShape& sh) {
     return false;
   }
   if (dc == 24 && dr == 8) return sh = {64, 4, 1}, true;
-  if (dr == 32 && dc == 96) return sh = {64, 8, 1}, true;
+  if (dr == 32 && dc == 96) return sh = {128, 8, 1}, true;
   if (dr == 32 && dc == 192) return sh = {64, 4, 2}, true;
   if (dr == 32 && dc == 448) return sh = {64, 4, 1}, true;
   return false;
@@ -1447,7 +1447,7 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
   } else {
     if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     if (c.dr == 32) {
-      if (c.dc == 96) return launch_flash<T, 128, 96, 64, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+      if (c.dc == 96) return launch_flash<T, 128, 96, 128, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
       if (c.dc == 192) return launch_flash<T, 224, 192, 64, 4, 2, false, true>(a, c.G, c.ev_start, c.ev_stop, s);
       if (c.dc == 448) return launch_flash<T, 480, 448, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     }
