@@ -136,16 +136,17 @@ VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg);
 
 /* Bytes of device memory a ctx needs beside the cache: a persistent part
  * written by vmla_prepare (the range flag and the weights in the activation
- * type, below) and the per-call buffers of vmla_attend (chunk latents, c^Q,
+ * type, below) and the per-call buffers of vmla_attend (chunk latents,
  * absorbed queries, latent outputs, per-head outputs, partial softmax states,
- * key tiles).  Returns 0 for an invalid config.
+ * key tiles; vmla_prepare also uses them as scratch).  Returns 0 for an
+ * invalid config.
  *
  * Operand types.  x, out, the cache and the caller's weights have the config's
- * dtype.  What the layer computes between x and out (c^Q, absorbed queries,
+ * dtype.  What the layer computes between x and out (absorbed queries,
  * attention outputs, per-head outputs) is held in the activation type: fp16
  * for bf16 storage (same 16 bits, 11 significant bits instead of 8, same MFMA
- * rate on gfx950), fp32 for fp32 storage; so are the absorbed query weight and
- * the copies of W_UQ, W_UV and W_O that vmla_prepare writes, and the fp16 key
+ * rate on gfx950), fp32 for fp32 storage; so are the weights vmla_prepare
+ * writes, the copy of x the chunk GEMM of an attend stages, and the fp16 key
  * tiles the attention kernel reads the cached rows from.  bf16 values within
  * fp16's normal range (2^-14 .. 65504 in magnitude) convert exactly; smaller
  * ones become fp16 subnormals (absolute error below 2^-25).  A finite value
@@ -165,14 +166,17 @@ VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* ca
                          void* workspace, const float* rope_freqs, vmla_ctx** out);
 
 /* Enqueue the one-time set-up of a ctx: clear its range flag and write, into
- * the persistent part of the workspace, [W_DKV; W_KR; W_DQ] (storage type: the
- * chunk's cache rows and c^Q come from one GEMM over x) and the weights in the
- * activation type:
- *   absorbed query weight, per head h, the [d_c + d_rope, d_q] block
- *     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope]  (qscale = log2(e)/sqrt(d_h)),
- *   so one GEMM from c^Q gives the absorbed query q~_h = W_UK^h^T q^nope_h
- *   and the un-rotated q^R_h of the MLA absorption (paper section 3.3);
- *   qscale * W_UQ, W_UV and W_O.
+ * the persistent part of the workspace, these weights in the activation type:
+ *   [W_DKV; W_KR];
+ *   absorbed query weight, per head h, the [d_c + d_rope, hidden] block
+ *     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] W_DQ  (qscale = log2(e)/sqrt(d_h)),
+ *   so one GEMM over x gives the chunk's cache rows together with the
+ *   absorbed query q~_h = W_UK^h^T q^nope_h and the un-rotated q^R_h of the
+ *   MLA absorption (paper section 3.3; c^Q = W_DQ x only ever feeds W_UQ, so
+ *   W_DQ is taken into the product, with one rounding of it);
+ *   qscale * W_UQ W_DQ (the per-head queries of the expanded path), W_UV, W_O.
+ * The products are summed in fp32 and rounded once; the per-call part of the
+ * workspace holds the fp32 intermediate.
  * Must follow vmla_create before any vmla_attend*, vmla_expand or
  * vmla_range_flags on the ctx (else those return VMLA_ERR_STATE); appends and
  * vmla_compress do not need it.  Since it copies the weights, the caller's
@@ -181,8 +185,9 @@ VMLA_API int vmla_prepare(vmla_ctx* ctx, hipStream_t stream);
 
 /* Read and clear the ctx's range flag: waits for `stream`, stores the flag in
  * *flags (bit 0 set: since vmla_prepare or the last read, some fp16 operand
- * copy -- a cached or chunk latent element, c^Q, an absorbed query, a per-head
- * output, an expanded key or value, a prepared weight -- had a finite value
+ * copy -- a cached or chunk latent element, a hidden-state element of x, an
+ * absorbed query, a per-head output, an expanded key or value, a prepared
+ * weight -- had a finite value
  * beyond +-65504 and was saturated), then enqueues the clear on `stream`. */
 VMLA_API int vmla_range_flags(vmla_ctx* ctx, uint32_t* flags, hipStream_t stream);
 
@@ -201,10 +206,10 @@ VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stre
  * tokens of the chunk itself (chunk-causal, appendix D.4), followed by W_UV and
  * W_O (paper section 3.3, absorbed form).  Leaves the cache and n unchanged:
  * the frozen-cache denoising steps of a rollout call this repeatedly, then
- * append the final step's x.  Needs vmla_prepare.  With bf16 storage the scores
- * and the value sum run on fp16 operands: fp16 copies of the visible cached
- * rows (saturating beyond +-65504, see the operand types above) and the fp16
- * absorbed queries. */
+ * append the final step's x.  Needs vmla_prepare.  With bf16 storage every
+ * product runs on fp16 operands: x as the chunk GEMM stages it, fp16 copies of
+ * the visible cached rows (each saturating beyond +-65504, see the operand
+ * types above), the fp16 absorbed queries and the prepared fp16 weights. */
 VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream);
 
 /* Same as vmla_attend, and additionally records attn_start on the stream right
@@ -217,12 +222,12 @@ VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEv
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): vmla_attend
- * with the per-call buffers (chunk latents, c^Q, absorbed queries, latent and
+ * with the per-call buffers (chunk latents, absorbed queries, latent and
  * per-head outputs, partial softmax states, key tiles) taken from a scratch
  * array inside the library instead of the ctx's workspace.  The array holds
  * VMLA_SCRATCH_BYTES (128 MiB) on every GPU the library runs on, from when its
  * code is loaded there until the process ends -- enough for one Wan-1.3B layer
- * call (4,680 query tokens against 37,440 keys needs ~118 MiB).  The ctx must
+ * call (4,680 query tokens against 37,440 keys needs ~112 MiB).  The ctx must
  * be prepared; only the persistent part of its workspace (prepared weights,
  * range flag) is read.  Same inputs, outputs and results as vmla_attend.
  * Allocates nothing and needs no free call.  Errors: VMLA_ERR_SCRATCH if the

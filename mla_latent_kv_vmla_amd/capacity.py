@@ -33,24 +33,27 @@ def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
                            workgroups: int = DEFAULT_WORKGROUPS, part: str = "total") -> int:
     """Mirror of the library's latent workspace layout for `batch` streams:
     part = "persistent" (range flag and the prepared weights, per layer:
-    [W_DKV; W_KR; W_DQ], the absorbed query weight, W_UQ, W_UV, W_O),
-    "per_call" (the buffers of one attend) or "total".  The activation type has
-    the storage type's width (fp16 for bf16, fp32 for fp32)."""
+    [W_DKV; W_KR], the absorbed query weight and W_UQ (each with W_DQ taken in),
+    W_UV, W_O), "per_call" (the buffers of one attend, at least the fp32 scratch
+    the preparation of the query weight uses) or "total".  The activation type
+    has the storage type's width (fp16 for bf16, fp32 for fp32)."""
     M = batch * g.n_q
     D, nh, dh = g.d_c + g.d_rope, g.n_heads, g.d_nope + g.d_rope
     dcp = (g.d_c + 31) // 32 * 32
     tiles = (-(-(g.sink_frames + g.window_frames) * g.tokens_per_frame // key_tile)
              + -(-g.n_q // key_tile))
-    persistent = [4, (D + g.d_q) * g.hidden * es, nh * D * g.d_q * es, nh * dh * g.d_q * es, nh * g.d_v * g.d_c * es,
+    persistent = [4, D * g.hidden * es, nh * D * g.hidden * es, nh * dh * g.hidden * es, nh * g.d_v * g.d_c * es,
                   g.hidden * nh * g.d_v * es]
-    per_call = [M * D * es, M * g.d_q * es, M * nh * max(D, g.d_v) * es,  # absorbed queries, then per-head outputs
+    per_call = [M * D * es, M * g.hidden * es if es == 2 else 0,  # chunk rows; fp16 copy of x (16-bit storage)
+                M * nh * max(D, g.d_v) * es,  # absorbed queries, then per-head outputs
                 M * nh * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
                 # pre-pass tiles: fp16 key tiles (16-bit storage), transposed value images (fp32)
                 batch * tiles * key_tile * D * 2 if es == 2 else batch * tiles * dcp * (key_tile + 16 // es) * es,
                 # rotated copy of the visible rows: rotation at use with fp32 storage only
                 batch * (g.sink_frames + g.window_frames) * g.tokens_per_frame * D * es
                 if (g.rope_at_use or g.sink_frames) and es == 4 else 0]
-    a, b = sum(_al(x) for x in persistent), sum(_al(x) for x in per_call)
+    a = sum(_al(x) for x in persistent)
+    b = max(sum(_al(x) for x in per_call), _al(nh * D * g.d_q * 4))
     return {"persistent": a, "per_call": b, "total": a + b}[part]
 
 

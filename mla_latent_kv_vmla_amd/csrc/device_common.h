@@ -99,6 +99,32 @@ __device__ inline void store4(f16* p, float a, float b, float c, float d, uint32
 __device__ inline void store4(bf16* p, float a, float b, float c, float d, uint32_t*) { store4(p, a, b, c, d); }
 __device__ inline void store4(float* p, float a, float b, float c, float d, uint32_t*) { store4(p, a, b, c, d); }
 
+// Eight bf16 values (one 16-byte vector) to fp16 by the rule above: round to
+// nearest even (exact in fp16's normal range), finite values beyond kF16Max
+// saturate and set `over`, NaN and infinities pass through.  The common case,
+// every magnitude within range, costs one test per vector.
+__device__ inline u32x4 bf16x8_to_f16x8(u32x4 v, bool& over) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(f[j]));
+  u32x4 r;
+  if (m > kF16Max) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = __builtin_bit_cast(uint32_t, f16x2{to_f16_sat(f[2 * i], over), to_f16_sat(f[2 * i + 1], over)});
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, f16x2{(f16)f[2 * i], (f16)f[2 * i + 1]});
+  }
+  return r;
+}
+
 // 16-byte global load / zero of one vector of storage elements.
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 

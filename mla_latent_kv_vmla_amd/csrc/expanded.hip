@@ -11,13 +11,13 @@
 //     roles swapped, so each lane holds 4 consecutive keys of one value channel
 //     and stores them together), then the value columns past the valid keys are
 //     zeroed up to the key-tile boundary.
-//   attend: the chunk's cache rows into staging and c^Q = W_DQ x (latent path), the
-//     per-head queries [q_nope | RoPE(q_rope)] (not absorbed; the prepared
-//     qscale * W_UQ), the chunk's own keys and values by the same up-projection,
-//     dense flash attention over the expanded window + chunk (attention.hip),
-//     out = W_O o.
-// Expanded keys and values, queries, c^Q and the attention output are fp16, as
-// in the dense layer; conversions saturate and raise the ctx's range flag.
+//   attend: the chunk's cache rows into staging and the per-head queries
+//     [q_nope | RoPE(q_rope)] (not absorbed; the prepared qscale * W_UQ W_DQ),
+//     one GEMM over x; the chunk's own keys and values by the same
+//     up-projection, dense flash attention over the expanded window + chunk
+//     (attention.hip), out = W_O o.
+// Expanded keys and values, queries and the attention output are fp16, as in
+// the dense layer; conversions saturate and raise the ctx's range flag.
 #include "gemm.h"
 #include "plan.h"
 
@@ -85,28 +85,6 @@ struct EpiExpandValueT {
   }
 };
 
-// Per-head queries [q_nope | RoPE(q_rope)] into Q[b][h][t][dh] (the prepared
-// weight carries qscale).
-struct EpiQueryHead {
-  f16* q;
-  int Nq, nh, dh, d_nope;
-  int64_t frame0;
-  Rope rope;
-  uint32_t* flag;
-  __device__ void operator()(int, int m, int n, const float* v) const {
-    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
-    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-    if (j >= d_nope) {
-      const int64_t frame = frame0 + t / rope.tokens_per_frame;
-      const int s = t % rope.tokens_per_frame;
-      const int pair = (j - d_nope) >> 1;
-      rope.rotate2(pair, frame, s, a0, a1);
-      rope.rotate2(pair + 1, frame, s, a2, a3);
-    }
-    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0, a1, a2, a3, flag);
-  }
-};
-
 template <typename T = bf16>
 static GemmOps<T> gops(const void* w, long ldw, long wz, const void* x, long ldx, long xz, int N, int M, int K) {
   GemmOps<T> o;
@@ -163,20 +141,9 @@ hipError_t run_attend_expanded(const Plan& p, const DensePlan& ex, const void* w
                                void* out, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int M = p.B * p.Nq;
   const int64_t tq = p.rope_at_use ? cached_frames(p, n) : n;  // temporal coordinate of the chunk's first frame
-  hipError_t err = run_chunk_rows_and_cq(p, x, tq, s);  // the chunk's cache rows and c^Q, one GEMM
+  // the chunk's cache rows and its per-head queries, one GEMM over x
+  hipError_t err = run_chunk_rows_and_queries(p, x, tq, QueryForm::PerHead, ex.q, s);
   if (err != hipSuccess) return err;
-  {  // per-head queries, not absorbed
-    EpiQueryHead e;
-    e.q = static_cast<f16*>(ex.q);
-    e.Nq = p.Nq;
-    e.nh = p.nh;
-    e.dh = p.dh;
-    e.d_nope = p.d_nope;
-    e.frame0 = tq;
-    e.rope = latent_rope(p);
-    e.flag = p.flags;
-    gemm<f16, false>(gops<f16>(p.wuq, p.dq, 0, p.cq, p.dq, 0, p.nh * p.dh, M, p.dq), 1, e, s);
-  }
   up_project(p, ex, static_cast<const bf16*>(wext), p.stage, (long)p.Nq * p.D, p.Nq, static_cast<f16*>(ex.kstage),
              static_cast<f16*>(ex.vstage), ex.stage_stride, -1, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;

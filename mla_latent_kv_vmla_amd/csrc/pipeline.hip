@@ -1,25 +1,24 @@
 // Launch sequences of the two library calls and the GEMM epilogues they use.
 //
-//   prepare (once per ctx): the concatenation [W_DKV; W_KR; W_DQ] (storage
-//     type), and the weights the activation-type GEMMs consume, in that type
-//     (fp16 for bf16 storage): the absorbed query weight
-//     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] per head (the MLA
-//     absorption, VideoMLA paper section 3.3, taken into the weight so one GEMM
-//     yields the absorbed query), qscale * W_UQ, W_UV and W_O.
+//   prepare (once per ctx): the weights of the activation-type GEMMs, in that
+//     type (fp16 for bf16 storage): [W_DKV; W_KR]; the absorbed query weight
+//     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] W_DQ per head (the MLA
+//     absorption, VideoMLA paper section 3.3, taken into the weight, and the
+//     query down-projection with it, so one GEMM over x yields the absorbed
+//     query); qscale * W_UQ W_DQ; W_UV and W_O.
 //   compress (VideoMLA paper, sections 3.1-3.2): one GEMM x . [W_DKV; W_KR]^T whose
 //     epilogue rotates the decoupled key channels by 3D-RoPE at the absolute
 //     frame (ring rows with rope_at_use stay un-rotated), rounds to the storage
 //     type and scatters each token's row to its ring slot (slot * T + s; frames
 //     f < S take sink slot f, later ones slot S + (f - S) % W) or to a linear
 //     buffer.
-//   attend: the chunk's cache rows into staging and c^Q = W_DQ x (one GEMM over
-//     x with the prepared [W_DKV; W_KR; W_DQ]); with rope_at_use and fp32
-//     storage, rotate the visible ring rows at their window-local coordinates
-//     into the workspace (assemble_window; with bf16 storage the attention
-//     pre-pass rotates them); absorbed query = prepared weight . c^Q
-//     with the rotary channels turned in the epilogue; latent attention
-//     (attention.hip); o_h = W_UV^h o~_h; out = W_O o.  Everything between x
-//     and out is held in the activation type.
+//   attend: the chunk's cache rows into staging and the absorbed query, one GEMM
+//     over x with the prepared [W_DKV; W_KR] and query weight, the query's rotary
+//     channels turned in the epilogue; with rope_at_use and fp32 storage, rotate
+//     the visible ring rows at their window-local coordinates into the workspace
+//     (assemble_window; with bf16 storage the attention pre-pass rotates them);
+//     latent attention (attention.hip); o_h = W_UV^h o~_h; out = W_O o.
+//     Everything between x and out is held in the activation type.
 #include <type_traits>
 
 #include "gemm.h"
@@ -89,19 +88,38 @@ template <typename A> struct EpiQueryAbs {
   }
 };
 
-// One GEMM over the chunk's hidden states with the prepared weight [W_DKV; W_KR;
-// W_DQ]: features [0, D) are the chunk's cache rows (EpiLatent to the staging
-// buffer), features [D, D + d_q) are c^Q (activation type).  The row features
-// accumulate in the same k order as in a compress alone, so the staged rows
-// are the ones an append of the same x would write.
-template <typename T, typename A> struct EpiLatentCq {
-  EpiLatent<T> lat;
-  A* cq;
-  int dq;
+// Per-head query of the non-absorbed form, [q_nope | RoPE(q_rope)] * qscale:
+// feature n of token m is channel j = n % dh of head n / dh, written to the dense
+// query layout [B][nh][Nq][dh].
+struct EpiQueryHead {
+  f16* q;
+  int Nq, nh, dh, d_nope;
+  int64_t frame0;
+  Rope rope;
   uint32_t* flag;
+  __device__ void operator()(int, int m, int n, const float* v) const {
+    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
+    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    if (j >= d_nope) {
+      const int64_t frame = frame0 + t / rope.tokens_per_frame;
+      const int s = t % rope.tokens_per_frame;
+      const int pair = (j - d_nope) >> 1;
+      rope.rotate2(pair, frame, s, a0, a1);
+      rope.rotate2(pair + 1, frame, s, a2, a3);
+    }
+    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0, a1, a2, a3, flag);
+  }
+};
+
+// One GEMM over the chunk's hidden states: features [0, D) are the chunk's cache
+// rows (EpiLatent to the staging buffer), features [D, ...) the queries (Q, with
+// the feature index rebased to 0).
+template <typename T, class Q> struct EpiRowsAndQuery {
+  EpiLatent<T> lat;
+  Q q;
   __device__ void operator()(int z, int m, int n, const float* v) const {
     if (n < lat.D) lat(z, m, n, v);
-    else store4(cq + (long)m * dq + (n - lat.D), v[0], v[1], v[2], v[3], flag);
+    else q(z, m, n - lat.D, v);
   }
 };
 
@@ -147,6 +165,53 @@ __global__ __launch_bounds__(256) void convert_weight(A* dst, const T* src, long
   raise_range_flag(over, flag);
 }
 
+// out[r][k] = scale * sum_l a[r][l] * b[l][k]: a [R][L], b [L][K] row-major,
+// fp32 products and sums, one rounding to the output type (saturating for
+// fp16).  Plain LDS-tiled fp32 FMA (64x64 outputs per workgroup, 4x4 per
+// thread, 16 l per step); it runs once per ctx.
+template <typename TA, typename TB, typename O>
+__global__ __launch_bounds__(256) void fold_weight(O* out, const TA* a, const TB* b, int R, int L, int K, float scale,
+                                                   uint32_t* flag) {
+  __shared__ float As[16][64 + 1];  // [l][r]
+  __shared__ float Bs[16][64];      // [l][k]
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int r0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int l0 = 0; l0 < L; l0 += 16) {
+    for (int i = threadIdx.x; i < 16 * 64; i += 256) {
+      const int ra = i / 16, la = i % 16, lb = i / 64, kb = i % 64;
+      As[la][ra] = r0 + ra < R && l0 + la < L ? (float)a[(long)(r0 + ra) * L + l0 + la] : 0.f;
+      Bs[lb][kb] = l0 + lb < L && k0 + kb < K ? (float)b[(long)(l0 + lb) * K + k0 + kb] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int l = 0; l < 16; ++l) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[l][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[l][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + ty + 16 * i, k = k0 + tx + 16 * j;
+      if (r >= R || k >= K) continue;
+      const float v = acc[i][j] * scale;
+      if constexpr (sizeof(O) == 2) out[(long)r * K + k] = to_f16_sat(v, over);
+      else out[(long)r * K + k] = v;
+    }
+  raise_range_flag(over, flag);
+}
+
 // Plain copy of n elements (16-byte vectors; n a multiple of 16 B / sizeof(T)).
 template <typename T>
 __global__ __launch_bounds__(256) void copy_rows(T* dst, const T* src, long n) {
@@ -164,23 +229,31 @@ hipError_t run_clear_flags(uint32_t* flags, hipStream_t s) {
 
 static int grid_for(long n) { return (int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048); }
 
+template <typename TA, typename TB, typename O>
+static void fold(O* out, const TA* a, const TB* b, int R, int L, int K, float scale, uint32_t* flag, hipStream_t s) {
+  fold_weight<TA, TB, O><<<dim3((K + 63) / 64, (R + 63) / 64), 256, 0, s>>>(out, a, b, R, L, K, scale, flag);
+}
+
 template <typename T, typename A>
 static void prepare_t(const Plan& p, hipStream_t s) {
   clear_flags<<<1, 1, 0, s>>>(p.flags);
-  {  // [W_DKV; W_KR; W_DQ], storage type, rows of `hidden`
-    T* wx = static_cast<T*>(p.wx);
-    const long a = (long)p.dc * p.d, b = (long)p.dr * p.d, c = (long)p.dq * p.d;
-    copy_rows<T><<<grid_for(a * (long)sizeof(T) / 16), 256, 0, s>>>(wx, static_cast<const T*>(p.w_dkv), a);
-    copy_rows<T><<<grid_for(b * (long)sizeof(T) / 16), 256, 0, s>>>(wx + a, static_cast<const T*>(p.w_kr), b);
-    copy_rows<T><<<grid_for(c * (long)sizeof(T) / 16), 256, 0, s>>>(wx + a + b, static_cast<const T*>(p.w_dq), c);
+  {  // [W_DKV; W_KR], rows of `hidden`
+    A* wl = static_cast<A*>(p.wlat);
+    const long a = (long)p.dc * p.d, b = (long)p.dr * p.d;
+    convert_weight<T, A><<<grid_for(a), 256, 0, s>>>(wl, static_cast<const T*>(p.w_dkv), a, 1.f, p.flags);
+    convert_weight<T, A><<<grid_for(b), 256, 0, s>>>(wl + a, static_cast<const T*>(p.w_kr), b, 1.f, p.flags);
   }
+  // absorbed query weight over c^Q in fp32 (scratch), then W_DQ taken in
+  float* wq32 = static_cast<float*>(p.prep);
   const long nqa = (long)p.nh * p.D * p.dq;
-  derive_query_weight<T, A><<<grid_for(nqa), 256, 0, s>>>(static_cast<A*>(p.wqa), static_cast<const T*>(p.w_uq),
-                                                          static_cast<const T*>(p.w_uk), p.nh, p.d_nope, p.dr, p.dc,
-                                                          p.dq, p.qscale, p.flags);
-  const long nuq = (long)p.nh * p.dh * p.dq, nuv = (long)p.nh * p.dv * p.dc, no = (long)p.d * p.nh * p.dv;
-  convert_weight<T, A><<<grid_for(nuq), 256, 0, s>>>(static_cast<A*>(p.wuq), static_cast<const T*>(p.w_uq), nuq,
-                                                     p.qscale, p.flags);
+  derive_query_weight<T, float><<<grid_for(nqa), 256, 0, s>>>(wq32, static_cast<const T*>(p.w_uq),
+                                                              static_cast<const T*>(p.w_uk), p.nh, p.d_nope, p.dr,
+                                                              p.dc, p.dq, p.qscale, p.flags);
+  const T* w_dq = static_cast<const T*>(p.w_dq);
+  fold<float, T, A>(static_cast<A*>(p.wqa), wq32, w_dq, p.nh * p.D, p.dq, p.d, 1.f, p.flags, s);
+  fold<T, T, A>(static_cast<A*>(p.wuq), static_cast<const T*>(p.w_uq), w_dq, p.nh * p.dh, p.dq, p.d, p.qscale,
+                p.flags, s);
+  const long nuv = (long)p.nh * p.dv * p.dc, no = (long)p.d * p.nh * p.dv;
   convert_weight<T, A><<<grid_for(nuv), 256, 0, s>>>(static_cast<A*>(p.wuv), static_cast<const T*>(p.w_uv), nuv,
                                                      1.f, p.flags);
   convert_weight<T, A><<<grid_for(no), 256, 0, s>>>(static_cast<A*>(p.wo), static_cast<const T*>(p.w_o), no, 1.f,
@@ -235,19 +308,80 @@ static void compress_t(const Plan& p, const void* x, int64_t frame0, void* dst, 
   gemm<T, false>(op, 1, latent_epilogue<T>(p, frame0, dst, ring), s);
 }
 
-// The chunk's cache rows (rotated at frame frame0.., into p.stage) and c^Q
-// (into p.cq), one GEMM with the prepared [W_DKV; W_KR; W_DQ].
-template <typename T>
-static void chunk_rows_and_cq_t(const Plan& p, const void* x, int64_t frame0, hipStream_t s) {
-  using A = typename std::conditional<sizeof(T) == 2, f16, float>::type;
-  const int M = p.B * p.Nq;
-  EpiLatentCq<T, A> e{latent_epilogue<T>(p, frame0, p.stage, false), static_cast<A*>(p.cq), p.dq, p.flags};
-  gemm<T, false>(ops<T>(p.wx, p.d, 0, x, p.d, 0, p.D + p.dq, M, p.d), 1, e, s);
+// Activation type of a storage type: fp16 for bf16, fp32 for fp32.
+template <typename T> using Act = typename std::conditional<sizeof(T) == 2, f16, float>::type;
+
+// x (bf16) to the activation type, 8 elements per thread and step
+// (bf16x8_to_f16x8: exact in fp16's normal range, saturating and flagging
+// beyond it); n8 = elements / 8.
+__global__ __launch_bounds__(256) void convert_x(u32x4* dst, const u32x4* src, long n8, uint32_t* flag) {
+  bool over = false;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256)
+    dst[i] = bf16x8_to_f16x8(src[i], over);
+  raise_range_flag(over, flag);
 }
 
-hipError_t run_chunk_rows_and_cq(const Plan& p, const void* x, int64_t frame0, hipStream_t s) {
-  if (p.dtype == DType::F32) chunk_rows_and_cq_t<float>(p, x, frame0, s);
-  else chunk_rows_and_cq_t<bf16>(p, x, frame0, s);
+// The chunk's cache rows (rotated at frames frame0.., into p.stage) and its
+// queries, one GEMM over x in the activation type with the prepared [W_DKV;
+// W_KR] and query weight.  The row features are the fp32 sums of the same
+// products as in a compress of x (bf16 -> fp16 is exact in fp16's normal
+// range), so the staged rows are, up to the order of the sums, the ones an
+// append of the same x writes.
+template <typename T, class Q>
+static void rows_and_queries_t(const Plan& p, const void* x, int64_t frame0, const void* wq, int nq, const Q& q,
+                               hipStream_t s) {
+  using A = Act<T>;
+  const int M = p.B * p.Nq;
+  const void* xa = x;
+  if constexpr (!std::is_same<T, A>::value) {
+    const long n8 = (long)M * p.d / 8;  // hidden is a multiple of 8 (config check)
+    convert_x<<<grid_for(n8), 256, 0, s>>>(static_cast<u32x4*>(p.xa), static_cast<const u32x4*>(x), n8, p.flags);
+    xa = p.xa;
+  }
+  GemmOps<A> op = ops<A>(p.wlat, p.d, 0, xa, p.d, 0, p.D + nq, M, p.d);
+  op.w2 = static_cast<const A*>(wq);
+  op.n_split = p.D;
+  EpiRowsAndQuery<T, Q> e{latent_epilogue<T>(p, frame0, p.stage, false), q};
+  gemm<A, false>(op, 1, e, s);
+}
+
+template <typename T>
+static void chunk_rows_and_queries_t(const Plan& p, const void* x, int64_t frame0, QueryForm form, void* qdst,
+                                     hipStream_t s) {
+  using A = Act<T>;
+  if (form == QueryForm::Absorbed) {
+    EpiQueryAbs<A> e;
+    e.qt = static_cast<A*>(qdst);
+    e.Nq = p.Nq;
+    e.N = p.nh * p.D;
+    e.dc = p.dc;
+    e.D = p.D;
+    e.frame0 = frame0;
+    e.rope = make_rope(p);
+    e.flag = p.flags;
+    rows_and_queries_t<T>(p, x, frame0, p.wqa, p.nh * p.D, e, s);
+  } else if constexpr (sizeof(T) == 2) {
+    EpiQueryHead e;
+    e.q = static_cast<f16*>(qdst);
+    e.Nq = p.Nq;
+    e.nh = p.nh;
+    e.dh = p.dh;
+    e.d_nope = p.d_nope;
+    e.frame0 = frame0;
+    e.rope = make_rope(p);
+    e.flag = p.flags;
+    rows_and_queries_t<T>(p, x, frame0, p.wuq, p.nh * p.dh, e, s);
+  }
+}
+
+hipError_t run_chunk_rows_and_queries(const Plan& p, const void* x, int64_t frame0, QueryForm form, void* q,
+                                      hipStream_t s) {
+  if (p.dtype == DType::F32) {
+    if (form != QueryForm::Absorbed) return hipErrorInvalidValue;  // the expanded path is bf16 only
+    chunk_rows_and_queries_t<float>(p, x, frame0, form, q, s);
+  } else {
+    chunk_rows_and_queries_t<bf16>(p, x, frame0, form, q, s);
+  }
   return hipGetLastError();
 }
 
@@ -297,9 +431,6 @@ hipError_t run_assemble(const Plan& p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Activation type of a storage type: fp16 for bf16, fp32 for fp32.
-template <typename T> using Act = typename std::conditional<sizeof(T) == 2, f16, float>::type;
-
 template <typename T>
 static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, hipStream_t s, hipEvent_t ev0,
                            hipEvent_t ev1) {
@@ -307,23 +438,12 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
   const int M = p.B * p.Nq;
   // temporal coordinate of the chunk's first frame: absolute, or local (after the visible cached frames)
   const int64_t tq = p.rope_at_use ? cached_frames(p, n) : n;
-  chunk_rows_and_cq_t<T>(p, x, tq, s);  // the chunk's cache rows and c^Q = W_DQ x, one GEMM
+  // the chunk's cache rows and the absorbed query [qscale W_UK^T q_nope | RoPE(qscale q_rope)], one GEMM over x
+  chunk_rows_and_queries_t<T>(p, x, tq, QueryForm::Absorbed, p.qt, s);
   // rotation at use: fp32 storage rotates the visible rows into a copy; bf16
   // storage lets the attention pre-pass turn them as it converts them to fp16
   const bool rot_in_prepass = p.rope_at_use && sizeof(T) == 2;
   if (p.rope_at_use && !rot_in_prepass) assemble_t<T>(p, n, s);
-  {  // absorbed query [qscale W_UK^T q_nope | RoPE(qscale q_rope)] per head, one GEMM from c^Q
-    EpiQueryAbs<A> e;
-    e.qt = static_cast<A*>(p.qt);
-    e.Nq = p.Nq;
-    e.N = p.nh * p.D;
-    e.dc = p.dc;
-    e.D = p.D;
-    e.frame0 = tq;
-    e.rope = make_rope(p);
-    e.flag = p.flags;
-    gemm<A, false>(ops<A>(p.wqa, p.dq, 0, p.cq, p.dq, 0, p.nh * p.D, M, p.dq), 1, e, s);
-  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   {

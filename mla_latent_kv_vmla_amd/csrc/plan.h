@@ -22,12 +22,15 @@ constexpr int kDenseKeyTile = 128;
 // workspace carve-up.  Filled by the host runtime; read by the pipelines.
 //
 // Operand types.  The ring cache, x and out have the storage type (bf16 or
-// fp32).  Everything the layer computes between them -- c^Q, absorbed queries,
+// fp32).  Everything the layer computes between them -- absorbed queries,
 // attention outputs, per-head outputs -- and the weights of the GEMMs that
-// consume those intermediates have the activation type: fp16 for bf16 storage
-// (11 significant bits where bf16 keeps 8, at the same MFMA rate), fp32 for
-// fp32 storage.  Those weights are converted (and, for the absorbed query,
-// derived) once per ctx by run_prepare into the persistent part of the workspace.
+// produce them have the activation type: fp16 for bf16 storage (11 significant
+// bits where bf16 keeps 8, at the same MFMA rate), fp32 for fp32 storage.  Those
+// weights are converted (and, for the queries, derived) once per ctx by
+// run_prepare into the persistent part of the workspace.  The query weights
+// take W_DQ in: c^Q = W_DQ x only ever feeds W_UQ, so the product of the two
+// (and of W_UK, for the absorbed form) is applied to x directly, one GEMM and
+// one rounding where the pages' order has two.
 struct Plan {
   DType dtype;
   int B, d, nh, d_nope, dr, dv, dc, dq, D, dh;  // D = dc + dr, dh = d_nope + dr
@@ -42,14 +45,14 @@ struct Plan {
   void* cache;   // [B][(S+W)*Tpf][D]
   // persistent workspace (written by run_prepare)
   uint32_t* flags;  // bit 0: an fp16 operand copy saturated (see kF16Max)
-  void *wx;      // [D + dq][d]   [W_DKV; W_KR; W_DQ] in the storage type
-  void *wqa;     // [nh][D][dq]   absorbed query weight: per head qscale*[W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope]
-  void *wuq;     // [nh*dh][dq]   qscale * W_UQ (per-head queries of the expanded path)
+  void *wlat;    // [D][d]        [W_DKV; W_KR]
+  void *wqa;     // [nh][D][d]    absorbed query weight: per head qscale*[W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] W_DQ
+  void *wuq;     // [nh*dh][d]    qscale * W_UQ W_DQ (per-head queries of the expanded path)
   void *wuv;     // [nh][dv][dc]  W_UV
   void *wo;      // [d][nh*dv]    W_O
   // per-call workspace
   void *stage;   // [B][Nq][D]            chunk latents (rotated), storage type
-  void *cq;      // [B][Nq][dq]           query latent
+  void *xa;      // [B][Nq][d]            x in the activation type (bf16 storage; fp32 reads x itself)
   void *qt;      // [B][Nq][nh][D]        absorbed query [W_UK^T q_nope | q_rope] * qscale
   void *olat;    // [B][Nq][nh][dc]       attention output in latent space
   void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV (same bytes as qt)
@@ -57,6 +60,7 @@ struct Plan {
   float *part_ml;// [2G][kAttnMaxRows][2]  running max (log2 domain) and sum
   void *vtiles;  // pre-pass tiles of the visible keys (per call): fp16 key tiles for bf16, value images for fp32
   void *assembled;  // rope_at_use with fp32 storage: the visible cache rows with k_r rotated at local coordinates
+  void *prep;    // run_prepare's fp32 scratch (the per-call region's start; no call is in flight then)
 };
 
 // Visible cached frames after n appends: sinks [0, min(n, S)) + window [max(S, n-W), n).
@@ -70,8 +74,9 @@ inline int64_t cached_frames(const Plan& p, int64_t n) {
 // prepared weights) sits at the start of a ctx's workspace; the per-call part
 // follows it there, or fills a clip workspace of its own.
 struct WorkspaceLayout {
-  size_t flags, wx, wqa, wuq, wuv, wo, persistent;                       // from the workspace start
-  size_t stage, cq, qt, olat, o, part_o, part_ml, vtiles, assembled, per_call;  // from the per-call start
+  size_t flags, wlat, wqa, wuq, wuv, wo, persistent;                  // from the workspace start
+  size_t stage, xa, qt, olat, o, part_o, part_ml, vtiles, assembled, per_call;  // from the per-call start
+  size_t prep;  // run_prepare's scratch: the first prep_bytes of the per-call part (per_call >= it)
   size_t total;  // persistent + per_call
 };
 
@@ -80,8 +85,12 @@ WorkspaceLayout workspace_layout(const Plan& p);
 inline size_t act_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
 
 // Kernel pipelines.  Each returns hipSuccess or the first launch error.
-// prepare: clear the range flag and write the persistent weights (wqa, wuq, wuv, wo).
+// prepare: clear the range flag and write the persistent weights (wlat, wqa,
+// wuq, wuv, wo), using p.prep (prep_bytes(p)) as scratch.
 hipError_t run_prepare(const Plan& p, hipStream_t s);
+// Scratch bytes run_prepare needs: the absorbed query weight before W_DQ is
+// taken in, [nh*D][dq] fp32.
+inline size_t prep_bytes(const Plan& p) { return (size_t)p.nh * p.D * p.dq * sizeof(float); }
 // Zero one flag word (a kernel, so the clear can sit in a captured graph).
 hipError_t run_clear_flags(uint32_t* flags, hipStream_t s);
 // compress: rows [c | RoPE(k^)] of x for frames frame0.. into dst; ring != 0
@@ -90,9 +99,14 @@ hipError_t run_clear_flags(uint32_t* flags, hipStream_t s);
 // unless the rows go to the ring of a rope_at_use layer (stored un-rotated).
 hipError_t run_compress(const Plan& p, const void* x, int64_t frame0, void* dst, bool ring,
                         hipStream_t s);
-// The chunk's cache rows (frames frame0.., into p.stage) and c^Q (into p.cq)
-// from one GEMM with the prepared [W_DKV; W_KR; W_DQ].
-hipError_t run_chunk_rows_and_cq(const Plan& p, const void* x, int64_t frame0, hipStream_t s);
+// The chunk's cache rows (frames frame0.., into p.stage) and its queries from
+// one GEMM over x with the prepared [W_DKV; W_KR] and query weight, the queries
+// rotated at the chunk's frames frame0..:
+//   Absorbed: p.wqa -> p.qt [B*Nq][nh*D] (latent attention);
+//   PerHead:  p.wuq -> q [B][nh][Nq][dh], fp16 (the expanded path's dense attention).
+enum class QueryForm { Absorbed, PerHead };
+hipError_t run_chunk_rows_and_queries(const Plan& p, const void* x, int64_t frame0, QueryForm form, void* q,
+                                      hipStream_t s);
 // rope_at_use with fp32 storage: the visible cache rows after n appends, k^
 // rotated with each frame's local coordinate, into p.assembled.  (With bf16
 // storage the rotation happens where the rows are converted: the attention

@@ -171,15 +171,15 @@ WorkspaceLayout workspace_layout(const Plan& p) {
     return o;
   };
   L.flags = take(sizeof(uint32_t));
-  L.wx = take((size_t)(p.D + p.dq) * p.d * es);
-  L.wqa = take((size_t)p.nh * p.D * p.dq * as);
-  L.wuq = take((size_t)p.nh * p.dh * p.dq * as);
+  L.wlat = take((size_t)p.D * p.d * as);
+  L.wqa = take((size_t)p.nh * p.D * p.d * as);
+  L.wuq = take((size_t)p.nh * p.dh * p.d * as);
   L.wuv = take((size_t)p.nh * p.dv * p.dc * as);
   L.wo = take((size_t)p.d * p.nh * p.dv * as);
   L.persistent = off;
   off = 0;
   L.stage = take(M * p.D * es);
-  L.cq = take(M * p.dq * as);
+  L.xa = take(p.dtype == DType::F32 ? 0 : M * p.d * as);
   // the per-head outputs reuse the absorbed queries' bytes: the queries are dead
   // once the attention kernel has run, before W_UV writes them
   L.qt = take(M * p.nh * (size_t)(p.D > p.dv ? p.D : p.dv) * as);
@@ -189,7 +189,8 @@ WorkspaceLayout workspace_layout(const Plan& p) {
   L.part_ml = take((size_t)2 * p.G * kAttnMaxRows * 2 * sizeof(float));
   L.vtiles = take(latent_prepass_bytes(p.dtype, p.dc, p.dr, p.B, (p.S + p.W) * p.Tpf, p.Nq));
   L.assembled = take(p.rope_at_use && p.dtype == DType::F32 ? (size_t)p.B * (p.S + p.W) * p.Tpf * p.D * es : 0);
-  L.per_call = off;
+  L.prep = 0;
+  L.per_call = off > align256(prep_bytes(p)) ? off : align256(prep_bytes(p));
   L.total = L.persistent + L.per_call;
   return L;
 }
@@ -326,7 +327,7 @@ VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* ca
 static void set_per_call(Plan& p, const vmla::WorkspaceLayout& L, void* base) {
   char* ws = static_cast<char*>(base);
   p.stage = ws + L.stage;
-  p.cq = ws + L.cq;
+  p.xa = ws + L.xa;
   p.qt = ws + L.qt;
   p.olat = ws + L.olat;
   p.o = ws + L.o;
@@ -334,6 +335,7 @@ static void set_per_call(Plan& p, const vmla::WorkspaceLayout& L, void* base) {
   p.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
   p.vtiles = ws + L.vtiles;
   p.assembled = ws + L.assembled;
+  p.prep = ws + L.prep;
 }
 
 // Weights, cache and the persistent workspace of a ctx on top of plan p's
@@ -351,7 +353,7 @@ static void set_ctx_pointers(Plan& p, const vmla_ctx* c) {
   const vmla::WorkspaceLayout L = vmla::workspace_layout(geometry(&c->cfg));
   char* ws = static_cast<char*>(c->workspace);
   p.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
-  p.wx = ws + L.wx;
+  p.wlat = ws + L.wlat;
   p.wqa = ws + L.wqa;
   p.wuq = ws + L.wuq;
   p.wuv = ws + L.wuv;

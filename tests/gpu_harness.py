@@ -6,9 +6,10 @@ mean_rel = sum |g - r| / sum |r| over all compared output elements, against the
 float64 oracle fed with the same (storage-rounded) inputs.
 
 Bar: max_abs <= 2e-2 and mean_rel <= 5e-3.  Latent-layer comparisons with bf16
-storage are held to max(bar, 1.1 x floor), where the floor is the error that
-rounding the cache rows and the output to bf16 causes on its own on the same
-case (tests/rounding.py, pinned on the CPU by test_tolerance.py); for the layer
+storage are held to mean_rel <= max(5e-3, 1.15 x floor) and max_abs <=
+max(2e-2, 1.6 x floor), where the floor is the error that rounding the cache
+rows and the output to bf16 causes on its own on the same case
+(tests/rounding.py, pinned on the CPU by test_tolerance.py); for the layer
 recipe the floor is ~2e-3 and the bound is the stated bar.  The dense layer
 (fp16 cache) and fp32 storage are held to the stated bar.
 """

@@ -62,14 +62,15 @@ def round_to(a, kind):
 # Rounding sequences, by stage of the absorbed computation:
 #   cache  the stored [c | k_r] rows (with rope_at_use k^ is stored before rotation)
 #   kr_use with rope_at_use, the cached k^ once rotated at its local coordinate
-#   wts    the prepared weights (absorbed query weight, W_UV, W_O)
-#   cq     c^Q;  qt  the absorbed query [q~ | q^R] (scale and log2 e folded in)
+#   wts    the prepared weights (the query weights with W_DQ taken in, W_UV, W_O)
+#   cq     c^Q, where a sequence computes it (then the query weights act on it);
+#          without it the query weights include W_DQ and act on x
+#   qt     the absorbed query [q~ | q^R] (scale and log2 e folded in)
 #   p      the probabilities fed to the value product
 #   olat   the attention output in latent space;  o  the per-head outputs
 #   u      the layer output
 MANDATED = dict(cache="bf16", u="bf16")
-AS_BUILT = dict(cache="bf16", kr_use="fp16", wts="fp16", cq="fp16", qt="fp16", p="fp16", olat="fp16", o="fp16",
-                u="bf16")
+AS_BUILT = dict(cache="bf16", kr_use="fp16", wts="fp16", qt="fp16", p="fp16", olat="fp16", o="fp16", u="bf16")
 # The rounding sequence of the earlier build (bf16 queries and intermediates,
 # q_nope rounded between two GEMMs), kept to show the bound tells them apart.
 BF16_INTERMEDIATES = dict(cache="bf16", cq="bf16", qnope="bf16", qt="bf16", p="fp16", olat="bf16", o="bf16",
@@ -114,7 +115,8 @@ def emulate(g, wts, history, n, chunk_x, query_tokens=None, steps=None, edit=Non
     qcoords = mla.token_coordinates(frames[len(cached):], g.grid_h, g.grid_w)[qi]
     nh, dn, dr, dh = g.n_heads, g.d_nope, g.d_rope, g.d_nope + g.d_rope
     scale = np.log2(np.e) / np.sqrt(dh)  # scores in log2 units, as the kernel computes them
-    cq = R("cq", xq @ f(wts.w_dq).T)
+    w_dq = f(wts.w_dq)
+    cq = R("cq", xq @ w_dq.T) if "cq" in steps else None
     w_uq = f(wts.w_uq).reshape(nh, dh, -1)
     w_uk, w_uv, w_o = f(wts.w_uk), f(wts.w_uv), f(wts.w_o)
     K = np.concatenate([c, kr], axis=1)
@@ -123,10 +125,15 @@ def emulate(g, wts, history, n, chunk_x, query_tokens=None, steps=None, edit=Non
         if "qnope" in steps:  # q_nope rounded, then absorbed
             qn = R("qnope", cq @ w_uq[h, :dn].T)
             qt = R("qt", scale * (qn @ w_uk[h]))
-        else:  # through the absorbed weight
-            wqa = R("wts", scale * (w_uk[h].T @ w_uq[h, :dn]))
-            qt = R("qt", cq @ wqa.T)
-        qr = R("qt", mla.rope_rotate(cq @ R("wts", scale * w_uq[h, dn:]).T, qcoords, g.rope_pairs, freqs))
+        elif cq is not None:  # the absorbed weight applied to a rounded c^Q
+            qt = R("qt", cq @ R("wts", scale * (w_uk[h].T @ w_uq[h, :dn])).T)
+        else:  # the absorbed weight with W_DQ taken in, applied to x
+            qt = R("qt", xq @ R("wts", (scale * (w_uk[h].T @ w_uq[h, :dn])) @ w_dq).T)
+        if cq is not None:
+            qr = cq @ R("wts", scale * w_uq[h, dn:]).T
+        else:
+            qr = xq @ R("wts", (scale * w_uq[h, dn:]) @ w_dq).T
+        qr = R("qt", mla.rope_rotate(qr, qcoords, g.rope_pairs, freqs))
         s = np.concatenate([qt, qr], axis=1) @ K.T
         p = np.exp2(s - s.max(axis=1, keepdims=True))
         o_lat = R("olat", (R("p", p) @ c) / p.sum(axis=1, keepdims=True))

@@ -215,3 +215,34 @@ def test_fp16_range_saturation_is_flagged():
     print(f"  saturated: max_abs={ma:.3e} (max |ref| {np.abs(ref).max():.3e}) mean_rel={mr:.3e}", flush=True)
     assert np.abs(got[0] - base[0]).max() > 1.0  # the element dominates the queries that favour it
     r.dev.close()
+
+
+def test_fp16_range_saturation_of_hidden_states_is_flagged():
+    """A hidden-state element beyond fp16's range (2^20; bf16 holds it): the
+    chunk GEMM stages x as fp16, so the element saturates to 65504 there, the
+    range flag goes up, and the output is the attention of the saturated chunk
+    (in an attend, x only feeds the chunk's own rows and queries).  The layer
+    recipe keeps the other elements small, so the saturated token dominates
+    only the scores it takes part in; the comparison takes the usual
+    floor-based bound of that case."""
+    g = SMALL
+    _print_case("range-x", g.name)
+    r = Rollout(g, mode="literal", cache_fill=float("nan"))
+    r.append(r.x(chunk=0))
+    r.append(r.x(chunk=1))
+    x = r.x(chunk=9)
+    base = r.attend(x)
+    assert r.dev.range_flags() == 0
+    tok, ch = 41, 7
+    x[0, tok, ch] = 2.0 ** 20
+    got = r.attend(x)
+    assert r.dev.range_flags() == 1
+    assert r.dev.range_flags() == 0
+    xs = x.copy()
+    xs[0, tok, ch] = 65504.0
+    ref = mla.attend(g, r.w, r.hist[0], r.n, xs[0])
+    fl = rd.floor(g, r.w, r.hist[0], r.n, xs[0], ref=ref)
+    ma, mr = assert_parity(got[0], ref, "saturated x", fl)
+    print(f"  saturated x: max_abs={ma:.3e} (max |ref| {np.abs(ref).max():.3e}) mean_rel={mr:.3e}", flush=True)
+    assert np.abs(got[0] - base[0]).max() > 1.0
+    r.dev.close()
