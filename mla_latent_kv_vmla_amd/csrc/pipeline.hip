@@ -47,20 +47,40 @@ template <typename T> struct EpiLatent {
   int Nq, W, S, dc, D;
   int ring, rotate;
   Rope rope;
-  __device__ void operator()(int, int m, int n, const float* v) const {
+  // features n..n+3 of token m after the rotation of the decoupled key channels
+  __device__ void values(int m, int n, const float* v, float* a) const {
+    a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
+    if (n >= dc && rotate) {
+      const int t = m % Nq;
+      const int64_t frame = frame0 + t / rope.tokens_per_frame;
+      const int s = t % rope.tokens_per_frame;
+      const int pair = (n - dc) >> 1;
+      rope.rotate2(pair, frame, s, a[0], a[1]);
+      rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+    }
+  }
+  __device__ T* row(int, int m, int n) const {
     const int b = m / Nq, t = m % Nq;
     const int64_t frame = frame0 + t / rope.tokens_per_frame;
     const int s = t % rope.tokens_per_frame;
     const int64_t slot = frame < S ? frame : S + (frame - S) % W;
-    const long row = ring ? (long)slot * rope.tokens_per_frame + s : (long)t;
-    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-    if (n >= dc && rotate) {
-      const int pair = (n - dc) >> 1;
-      rope.rotate2(pair, frame, s, a0, a1);
-      rope.rotate2(pair + 1, frame, s, a2, a3);
-    }
-    store4(dst + b * bstride + row * D + n, a0, a1, a2, a3);
+    const long r = ring ? (long)slot * rope.tokens_per_frame + s : (long)t;
+    return dst + b * bstride + r * D + n;
   }
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    float a[4];
+    values(m, n, v, a);
+    store4(row(z, m, n), a[0], a[1], a[2], a[3]);
+  }
+  static constexpr bool kRows = sizeof(T) == 2;
+  __device__ u32x2 pack(int, int m, int n, const float* v, bool& over) const {
+    float a[4];
+    values(m, n, v, a);
+    if constexpr (sizeof(T) == 2) return pack4<T>(a[0], a[1], a[2], a[3], over);
+    else return u32x2{0u, 0u};
+  }
+  __device__ void raise(bool) const {}
+  bool rows_aligned() const { return (uintptr_t)dst % 16 == 0 && D % 8 == 0 && bstride % 8 == 0; }
 };
 
 // Absorbed query straight from c^Q through the prepared weight: feature n of
@@ -73,19 +93,33 @@ template <typename A> struct EpiQueryAbs {
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
-  __device__ void operator()(int, int m, int n, const float* v) const {
+  __device__ void values(int m, int n, const float* v, float* a) const {
     const int j = n % D;
-    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (j >= dc) {
       const int t = m % Nq;
       const int64_t frame = frame0 + t / rope.tokens_per_frame;
       const int s = t % rope.tokens_per_frame;
       const int pair = (j - dc) >> 1;
-      rope.rotate2(pair, frame, s, a0, a1);
-      rope.rotate2(pair + 1, frame, s, a2, a3);
+      rope.rotate2(pair, frame, s, a[0], a[1]);
+      rope.rotate2(pair + 1, frame, s, a[2], a[3]);
     }
-    store4(qt + (long)m * N + n, a0, a1, a2, a3, flag);
   }
+  __device__ A* row(int, int m, int n) const { return qt + (long)m * N + n; }
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    float a[4];
+    values(m, n, v, a);
+    store4(row(z, m, n), a[0], a[1], a[2], a[3], flag);
+  }
+  static constexpr bool kRows = sizeof(A) == 2;
+  __device__ u32x2 pack(int, int m, int n, const float* v, bool& over) const {
+    float a[4];
+    values(m, n, v, a);
+    if constexpr (sizeof(A) == 2) return pack4<A>(a[0], a[1], a[2], a[3], over);
+    else return u32x2{0u, 0u};
+  }
+  __device__ void raise(bool over) const { raise_range_flag(over, flag); }
+  bool rows_aligned() const { return (uintptr_t)qt % 16 == 0 && N % 8 == 0; }
 };
 
 // Per-head query of the non-absorbed form, [q_nope | RoPE(q_rope)] * qscale:
@@ -97,18 +131,34 @@ struct EpiQueryHead {
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
-  __device__ void operator()(int, int m, int n, const float* v) const {
-    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
-    float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+  __device__ void values(int m, int n, const float* v, float* a) const {
+    const int t = m % Nq, j = n % dh;
+    a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (j >= d_nope) {
       const int64_t frame = frame0 + t / rope.tokens_per_frame;
       const int s = t % rope.tokens_per_frame;
       const int pair = (j - d_nope) >> 1;
-      rope.rotate2(pair, frame, s, a0, a1);
-      rope.rotate2(pair + 1, frame, s, a2, a3);
+      rope.rotate2(pair, frame, s, a[0], a[1]);
+      rope.rotate2(pair + 1, frame, s, a[2], a[3]);
     }
-    store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0, a1, a2, a3, flag);
   }
+  __device__ f16* row(int, int m, int n) const {
+    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
+    return q + (((long)b * nh + h) * Nq + t) * dh + j;
+  }
+  __device__ void operator()(int z, int m, int n, const float* v) const {
+    float a[4];
+    values(m, n, v, a);
+    store4(row(z, m, n), a[0], a[1], a[2], a[3], flag);
+  }
+  static constexpr bool kRows = true;
+  __device__ u32x2 pack(int, int m, int n, const float* v, bool& over) const {
+    float a[4];
+    values(m, n, v, a);
+    return pack4<f16>(a[0], a[1], a[2], a[3], over);
+  }
+  __device__ void raise(bool over) const { raise_range_flag(over, flag); }
+  bool rows_aligned() const { return (uintptr_t)q % 16 == 0 && dh % 8 == 0; }
 };
 
 // One GEMM over the chunk's hidden states: features [0, D) are the chunk's cache
@@ -121,6 +171,16 @@ template <typename T, class Q> struct EpiRowsAndQuery {
     if (n < lat.D) lat(z, m, n, v);
     else q(z, m, n - lat.D, v);
   }
+  static constexpr bool kRows = EpiLatent<T>::kRows && Q::kRows;
+  __device__ u32x2 pack(int z, int m, int n, const float* v, bool& over) const {
+    return n < lat.D ? lat.pack(z, m, n, v, over) : q.pack(z, m, n - lat.D, v, over);
+  }
+  __device__ void* row(int z, int m, int n) const {
+    return n < lat.D ? (void*)lat.row(z, m, n) : (void*)q.row(z, m, n - lat.D);
+  }
+  __device__ void raise(bool over) const { q.raise(over); }
+  // a 16-B chunk of features never straddles the two parts
+  bool rows_aligned() const { return lat.D % 8 == 0 && lat.rows_aligned() && q.rows_aligned(); }
 };
 
 // ---------------------------------------------------------------- prepare
