@@ -212,9 +212,10 @@ VMLA_API int vmla_compress_append(vmla_ctx* ctx, const void* x, hipStream_t stre
  * types above), the fp16 absorbed queries and the prepared fp16 weights. */
 VMLA_API int vmla_attend(vmla_ctx* ctx, const void* x, void* out, hipStream_t stream);
 
-/* Same as vmla_attend, and additionally records attn_start on the stream right
- * before the latent-attention kernel (the call's dominant kernel) and attn_stop
- * right after it, so a caller can time that kernel with hipEventElapsedTime.
+/* Same as vmla_attend, and additionally records attn_start and attn_stop at
+ * the start and the end of the latent-attention kernel (the call's dominant
+ * kernel; the events are attached to its dispatch, so timing adds no gap to
+ * the stream), so a caller can time that kernel with hipEventElapsedTime.
  * Both events must be created by the caller (hipEventCreate); NULL ->
  * VMLA_ERR_NULL. */
 VMLA_API int vmla_attend_profiled(vmla_ctx* ctx, const void* x, void* out, hipEvent_t attn_start,
@@ -280,7 +281,7 @@ VMLA_API void vmla_destroy(vmla_ctx* ctx);
 VMLA_API size_t vmla_clip_workspace_bytes(const vmla_config* cfg);
 VMLA_API int vmla_attend_clip(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out,
                               hipStream_t stream);
-/* vmla_attend_clip plus caller-made events recorded right before and after the
+/* vmla_attend_clip plus caller-made events taking the start and end time of the
  * attention kernel (NULL -> VMLA_ERR_NULL). */
 VMLA_API int vmla_attend_clip_profiled(vmla_ctx* ctx, const void* x, void* clip_workspace, void* out,
                                        hipEvent_t attn_start, hipEvent_t attn_stop, hipStream_t stream);
@@ -306,8 +307,8 @@ VMLA_API int vmla_attend_clip_profiled(vmla_ctx* ctx, const void* x, void* clip_
  *   chunk's own up-projected keys/values, then W_O.  `expanded` must be the
  *   buffer of the last vmla_expand, made after the last append (else
  *   VMLA_ERR_STATE; vmla_reset forgets it).
- * vmla_attend_expanded_profiled: same, recording caller-made events around the
- *   attention kernel (NULL -> VMLA_ERR_NULL).
+ * vmla_attend_expanded_profiled: same, with caller-made events taking the
+ *   attention kernel's start and end time (NULL -> VMLA_ERR_NULL).
  */
 VMLA_API size_t vmla_expanded_bytes(const vmla_config* cfg);
 VMLA_API int vmla_expand(vmla_ctx* ctx, void* expanded, hipStream_t stream);
@@ -381,8 +382,8 @@ VMLA_API int vmla_dense_append(vmla_dense_ctx* ctx, const void* x, hipStream_t s
  * [max(0, n-W), n) and the chunk itself; the cache and n are unchanged. */
 VMLA_API int vmla_dense_attend(vmla_dense_ctx* ctx, const void* x, void* out, hipStream_t stream);
 
-/* vmla_dense_attend plus caller-made events recorded right before and right
- * after the attention kernel (NULL -> VMLA_ERR_NULL). */
+/* vmla_dense_attend plus caller-made events taking the start and end time of
+ * the attention kernel (NULL -> VMLA_ERR_NULL). */
 VMLA_API int vmla_dense_attend_profiled(vmla_dense_ctx* ctx, const void* x, void* out,
                                         hipEvent_t attn_start, hipEvent_t attn_stop, hipStream_t stream);
 

@@ -71,6 +71,8 @@
 // units (log2(e) is folded into the query), and the running maximum is only
 // moved when a block exceeds it by more than 8 (a factor 2^8), which keeps
 // rescaling of the accumulator rare.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "device_common.h"
@@ -253,12 +255,15 @@ __global__ __launch_bounds__(256) void latent_value_tiles(FlashArgs<T> p) {
 }
 
 // Pre-pass (latent attention, bf16 storage): fp16 copies of the key tiles.
-// Tile (s, t) is row-major [KTILE][D] without padding; keys past the segment's
+// Tile (s, t) is row-major [KTILE][D] without padding, or (IMAGE) the byte
+// image of the pipelined kernel's LDS tile (16-row regions of 1-KB blocks,
+// see flash_attn_pipe_kernel), so that each of that kernel's wave-wide DMA
+// loads copies 1 KB of contiguous bytes; keys past the segment's
 // end repeat its last key (their probabilities are zero).  bf16 values in
 // fp16's normal range convert exactly; a finite value beyond +-65504 saturates
 // and raises the range flag.  With rotation at use, the ring rows' k^ channels
 // are turned in fp32 at their local coordinate first (one rounding, to fp16).
-template <typename T, int D, int KTILE>
+template <typename T, int D, int KTILE, bool IMAGE>
 __global__ __launch_bounds__(256) void latent_key_tiles(FlashArgs<T> p) {
   static_assert(std::is_same<T, bf16>::value, "the key tiles widen bf16");
   constexpr int CV = D / 8;
@@ -288,7 +293,12 @@ __global__ __launch_bounds__(256) void latent_key_tiles(FlashArgs<T> p) {
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = to_f16_sat(x[e], over);
-    *reinterpret_cast<f16x8*>(img + r * D + c * 8) = h;
+    int off = r * D + c * 8;
+    if constexpr (IMAGE) {  // region r / 16, block c / 4, slot 16 (c % 4) + ((r % 16) ^ 4 (c % 4))
+      const int cc = c & 3;
+      off = (r >> 4) * 16 * D + (c >> 2) * 512 + 8 * (16 * cc + ((r & 15) ^ (4 * cc)));
+    }
+    *reinterpret_cast<f16x8*>(img + off) = h;
   }
   raise_range_flag(over, p.range_flag);
 }
@@ -861,10 +871,11 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   };
   // LDS-DMA load k (0..NI_W-1) of this wave's share of a tile: block k of
   // region `wave`; lane L fills slot L: chunk 4k + L/16 of row
-  // 16 wave + ((L % 16) ^ 4 (L / 16))
-  const uint32_t dma_voff = (uint32_t)(((16 * wave + ((lane & 15) ^ (4 * (lane >> 4)))) * D + 8 * (lane >> 4)) * 2);
+  // 16 wave + ((L % 16) ^ 4 (L / 16)).  The pre-pass stores the tile as this
+  // LDS image, so the load copies the block's 1 KB of contiguous bytes.
+  const uint32_t dma_voff = (uint32_t)((wave * REG_EL + 8 * lane) * 2);
   auto issue_part = [&](__amdgpu_buffer_rsrc_t krs, T* buf, int k) __attribute__((always_inline)) {
-    lds_dma16(krs, dma_voff + (uint32_t)(64 * k), buf + wave * REG_EL + k * 512);
+    lds_dma16(krs, dma_voff + (uint32_t)(1024 * k), buf + wave * REG_EL + k * 512);
   };
   auto issue_tile = [&](int s, int t, T* buf) __attribute__((always_inline)) {
     const auto krs = tile_rsrc(s, t);
@@ -1357,18 +1368,23 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   const long I = (U - a.dp_units) * a.KT;
   if (a.row_div <= 0) a.row_div = 1;
   if constexpr (!VROWS) {
-    if constexpr (sizeof(T) == 2) latent_key_tiles<T, D, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
+    if constexpr (sizeof(T) == 2) latent_key_tiles<T, D, KTILE, PIPE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
     else latent_value_tiles<T, D, DV, KTILE><<<dim3(a.KT, a.S), 256, 0, s>>>(a);
   }
-  hipError_t err;
-  if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+  // The timing events (both or neither) are attached to the attention kernel's
+  // own dispatch: they take its start and end time stamps, with no marker
+  // packets of their own on the stream (a separate event record before and
+  // after the kernel leaves a gap of several microseconds on each side).
+  void* kernel;
   if constexpr (PIPE) {
     static_assert(NW == 4 && NB == 2 && !VROWS && sizeof(T) == 2, "pipelined kernel shape");
-    flash_attn_pipe_kernel<D, DV, KTILE><<<a.G, 256, 0, s>>>(a);
+    kernel = reinterpret_cast<void*>(&flash_attn_pipe_kernel<D, DV, KTILE>);
   } else {
-    flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS><<<a.G, NW * 64, 0, s>>>(a);
+    kernel = reinterpret_cast<void*>(&flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS>);
   }
-  if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
+  void* args[] = {&a};
+  hipError_t err = hipExtLaunchKernel(kernel, dim3(a.G), dim3(NW * 64), args, 0, s, ev0, ev1, 0);
+  if (err != hipSuccess) return err;
   if (!causal && I != (long)a.G * a.KT)
     flash_attn_combine<T, DV, ROWS><<<(U - a.dp_units) * (ROWS / 16), 256, 0, s>>>(a);
   return hipGetLastError();

@@ -145,6 +145,25 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* 
                                            0, 0);
 }
 
+// LDS-DMA load issued from inline asm: each active lane copies the 16 bytes at
+// byte offset `voff` of the buffer to LDS byte address lds_byte_addr + 16 *
+// lane (lds_byte_addr wave-uniform, in an SGPR).  The compiler does not know
+// this instruction writes LDS, so it adds no wait for it before LDS reads: the
+// caller waits (wait_vmcnt) before the barrier that publishes the data, and
+// before the workgroup ends.
+__device__ inline void dma16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_byte_addr) {
+  // one wait state between the M0 write and the LDS-DMA that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte_addr), "v"(voff), "s"(r)
+               : "memory");
+}
+template <int N> __device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Column of key j in a transposed value row: bits 2 and 3 of j swapped, so the
 // 8 keys one lane feeds to a value MFMA are contiguous (and every aligned group
 // of 4 keys stays contiguous).

@@ -218,19 +218,6 @@ template <typename T> struct GemmDmaOps {
   int tn, tm, Z;  // tiles along N, along M, batch
 };
 
-__device__ inline void dma16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_byte_addr) {
-  // one wait state between the M0 write and the LDS-DMA that reads it
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_byte_addr), "v"(voff), "s"(r)
-               : "memory");
-}
-template <int N> __device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <typename T, int BN, int BM, int NWN, int NWM, int NST, class Epi>
 __global__ __launch_bounds__(NWN * NWM * 64) void gemm_dma_kernel(GemmDmaOps<T> op, Epi epi) {
   static_assert(sizeof(T) == 2, "16-bit operands");
