@@ -135,8 +135,9 @@ typedef struct vmla_ctx vmla_ctx; /* opaque; holds host-side metadata only */
 VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg);
 
 /* Bytes of device memory a ctx needs beside the cache: a persistent part
- * written by vmla_prepare (the range flag and the weights in the activation
- * type, below) and the per-call buffers of vmla_attend (chunk latents,
+ * written by vmla_prepare (the range flag, the cosine and sine of the 3D-RoPE
+ * row and column angles -- d_rope/2 x max(grid_h, grid_w) pairs of fp32 --
+ * and the weights in the activation type, below) and the per-call buffers of vmla_attend (chunk latents,
  * absorbed queries, latent outputs, per-head outputs, partial softmax states,
  * key tiles; vmla_prepare also uses them as scratch).  Returns 0 for an
  * invalid config.
@@ -165,8 +166,9 @@ VMLA_API size_t vmla_workspace_bytes(const vmla_config* cfg);
 VMLA_API int vmla_create(const vmla_config* cfg, const vmla_weights* w, void* cache,
                          void* workspace, const float* rope_freqs, vmla_ctx** out);
 
-/* Enqueue the one-time set-up of a ctx: clear its range flag and write, into
- * the persistent part of the workspace, these weights in the activation type:
+/* Enqueue the one-time set-up of a ctx: clear its range flag, tabulate the
+ * rotary row and column angles, and write, into the persistent part of the
+ * workspace, these weights in the activation type:
  *   [W_DKV; W_KR];
  *   absorbed query weight, per head h, the [d_c + d_rope, hidden] block
  *     qscale * [W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] W_DQ  (qscale = log2(e)/sqrt(d_h)),

@@ -29,12 +29,18 @@ def latent_cache_bytes(g, batch: int = 1, es: int = 2) -> int:
     return batch * (g.sink_frames + g.window_frames) * g.tokens_per_frame * (g.d_c + g.d_rope) * es
 
 
+def rope_table_bytes(g, pairs: int) -> int:
+    """The rotary table of the row and column axes: per pair, cos and sin (fp32)
+    for max(grid_h, grid_w) positions."""
+    return pairs * max(g.grid_h, g.grid_w) * 2 * 4
+
+
 def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
                            workgroups: int = DEFAULT_WORKGROUPS, part: str = "total") -> int:
     """Mirror of the library's latent workspace layout for `batch` streams:
-    part = "persistent" (range flag and the prepared weights, per layer:
-    [W_DKV; W_KR], the absorbed query weight and W_UQ (each with W_DQ taken in),
-    W_UV, W_O), "per_call" (the buffers of one attend, at least the fp32 scratch
+    part = "persistent" (range flag, rotary table and the prepared weights, per
+    layer: [W_DKV; W_KR], the absorbed query weight and W_UQ (each with W_DQ
+    taken in), W_UV, W_O), "per_call" (the buffers of one attend, at least the fp32 scratch
     the preparation of the query weight uses) or "total".  The activation type
     has the storage type's width (fp16 for bf16, fp32 for fp32)."""
     M = batch * g.n_q
@@ -42,7 +48,7 @@ def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
     dcp = (g.d_c + 31) // 32 * 32
     tiles = (-(-(g.sink_frames + g.window_frames) * g.tokens_per_frame // key_tile)
              + -(-g.n_q // key_tile))
-    persistent = [4, D * g.hidden * es, nh * D * g.hidden * es, nh * dh * g.hidden * es, nh * g.d_v * g.d_c * es,
+    persistent = [4, rope_table_bytes(g, g.d_rope // 2), D * g.hidden * es, nh * D * g.hidden * es, nh * dh * g.hidden * es, nh * g.d_v * g.d_c * es,
                   g.hidden * nh * g.d_v * es]
     per_call = [M * D * es, M * g.hidden * es if es == 2 else 0,  # chunk rows; fp16 copy of x (16-bit storage)
                 M * nh * max(D, g.d_v) * es,  # absorbed queries, then per-head outputs
@@ -64,10 +70,10 @@ def dense_cache_bytes(g, batch: int = 1) -> int:
 
 
 def dense_workspace_bytes(g, batch: int = 1, workgroups: int = DEFAULT_WORKGROUPS, part: str = "total") -> int:
-    """Mirror of the dense workspace: persistent (range flag, fp16 W_O) and per call."""
+    """Mirror of the dense workspace: persistent (range flag, rotary table, fp16 W_O) and per call."""
     S = -(-g.n_q // DENSE_KEY_TILE) * DENSE_KEY_TILE
     heads = batch * g.n_heads
-    persistent = [4, g.hidden * g.n_heads * g.d_v * 2]
+    persistent = [4, rope_table_bytes(g, g.head_dim // 2), g.hidden * g.n_heads * g.d_v * 2]
     per_call = [heads * g.n_q * g.head_dim * 2, heads * S * g.head_dim * 2, heads * S * g.d_v * 2,
                 batch * g.n_q * g.n_heads * g.d_v * 2, 2 * workgroups * ATTN_MAX_ROWS * g.d_v * 2,
                 2 * workgroups * ATTN_MAX_ROWS * 2 * 4]

@@ -1452,11 +1452,8 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
   a.rot_S = c.rot_S;
   a.rot_W = c.rot_W;
   a.rot_n = c.rot_n;
-  a.rope.pairs_t = c.pairs_t;
-  a.rope.pairs_h = c.pairs_h;
-  a.rope.grid_w = c.grid_w;
-  a.rope.tokens_per_frame = c.tokens_per_frame;
-  for (int i = 0; i < kMaxRopePairs; ++i) a.rope.freq[i] = c.freq[i];
+  a.rope.set(c.pairs_t, c.pairs_h, c.grid_w, c.tokens_per_frame, c.freq, kMaxRopePairs, c.rope_tab,
+             rope_tab_stride(c.tokens_per_frame, c.grid_w));
   if constexpr (std::is_same<T, float>::value) {
     if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     return hipErrorInvalidValue;

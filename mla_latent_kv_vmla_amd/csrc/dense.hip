@@ -21,11 +21,7 @@ namespace vmla {
 
 static Rope dense_rope(const DensePlan& p) {
   Rope r;
-  r.pairs_t = p.pairs_t;
-  r.pairs_h = p.pairs_h;
-  r.grid_w = p.grid_w;
-  r.tokens_per_frame = p.Tpf;
-  for (int i = 0; i < kMaxRopePairs; ++i) r.freq[i] = p.freq[i];
+  r.set(p.pairs_t, p.pairs_h, p.grid_w, p.Tpf, p.freq, kMaxRopePairs, p.rope_tab, rope_tab_stride(p.Tpf, p.grid_w));
   return r;
 }
 
@@ -34,14 +30,15 @@ static Rope dense_rope(const DensePlan& p) {
 struct EpiDenseQ {
   f16* q;
   int Nq, nh, dh;
+  FastDiv nq, hd;  // Nq, dh
   float qscale;
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
   __device__ void operator()(int, int m, int n, const float* v) const {
-    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
-    const int64_t frame = frame0 + t / rope.tokens_per_frame;
-    const int s = t % rope.tokens_per_frame;
+    const int b = (int)nq.div(m), t = m - b * Nq, h = (int)hd.div(n), j = n - h * dh;
+    const int64_t frame = frame0 + (int)rope.tpf.div(t);
+    const int s = (int)rope.tpf.mod(t);
     float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
     rope.rotate2(j >> 1, frame, s, a0, a1);
     rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
@@ -57,22 +54,25 @@ struct EpiDenseKV {
   long P;
   int Nq, nh, dh, dv, W;
   int ring;
+  int wrel;  // frame0 mod W: chunk frame i sits in slot (wrel + i) mod W, wrel + i < 2W
+  FastDiv nq, hd, vd;  // Nq, dh, dv
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
   __device__ void operator()(int, int m, int n, const float* x) const {
-    const int b = m / Nq, t = m % Nq;
-    const int64_t frame = frame0 + t / rope.tokens_per_frame;
-    const int s = t % rope.tokens_per_frame;
-    const long row = ring ? (long)(frame % W) * rope.tokens_per_frame + s : (long)t;
+    const int b = (int)nq.div(m), t = m - b * Nq;
+    const int i = (int)rope.tpf.div(t), s = t - i * rope.tokens_per_frame;
+    const int64_t frame = frame0 + i;
+    const int slot = wrel + i >= W ? wrel + i - W : wrel + i;
+    const long row = ring ? (long)slot * rope.tokens_per_frame + s : (long)t;
     if (n < nh * dh) {
-      const int h = n / dh, j = n % dh;
+      const int h = (int)hd.div(n), j = n - h * dh;
       float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
       rope.rotate2(j >> 1, frame, s, a0, a1);
       rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
       store4(k + (((long)b * nh + h) * P + row) * dh + j, a0, a1, a2, a3, flag);
     } else {
-      const int n2 = n - nh * dh, h = n2 / dv, f = n2 % dv;
+      const int n2 = n - nh * dh, h = (int)vd.div(n2), f = n2 - h * dv;
       f16* dst = v + (((long)b * nh + h) * dv + f) * P + (row & ~15L) + perm16((int)(row & 15));
       bool over = false;
 #pragma unroll
@@ -129,6 +129,10 @@ static void dense_kv(const DensePlan& p, const void* x, int64_t frame0, bool rin
   e.dv = p.dv;
   e.W = p.W;
   e.ring = ring ? 1 : 0;
+  e.wrel = (int)(frame0 % p.W);
+  e.nq = FastDiv((uint32_t)p.Nq);
+  e.hd = FastDiv((uint32_t)p.dh);
+  e.vd = FastDiv((uint32_t)p.dv);
   e.frame0 = frame0;
   e.rope = dense_rope(p);
   e.flag = p.flags;
@@ -148,6 +152,8 @@ __global__ __launch_bounds__(256) void dense_convert_weight(f16* dst, const bf16
 
 hipError_t run_dense_prepare(const DensePlan& p, hipStream_t s) {
   hipError_t err = run_clear_flags(p.flags, s);
+  if (err != hipSuccess) return err;
+  err = run_rope_table(p.rope_tab, p.dh / 2, p.pairs_t, p.pairs_h, p.Tpf, p.grid_w, p.freq, s);
   if (err != hipSuccess) return err;
   const long n = (long)p.d * p.nh * p.dv;
   dense_convert_weight<<<(int)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048), 256, 0, s>>>(
@@ -173,6 +179,8 @@ hipError_t run_dense_attend(const DensePlan& p, int64_t n, const void* x, void* 
     e.Nq = p.Nq;
     e.nh = p.nh;
     e.dh = p.dh;
+    e.nq = FastDiv((uint32_t)p.Nq);
+    e.hd = FastDiv((uint32_t)p.dh);
     e.qscale = p.qscale;
     e.frame0 = n;
     e.rope = dense_rope(p);

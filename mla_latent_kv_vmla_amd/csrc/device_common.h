@@ -169,18 +169,60 @@ template <int N> __device__ inline void wait_vmcnt() {
 // of 4 keys stays contiguous).
 __device__ inline int perm16(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
+// Exact x / d and x % d for 0 <= x < 2^31 and a divisor d >= 1 fixed per
+// launch: one high multiply, one add and one shift (the magic-number method
+// for dividends one bit narrower than the word: mul = floor(2^32 (2^s - d) / d)
+// + 1 with 2^s >= d), where a division by a run-time value expands to a long
+// instruction sequence.
+struct FastDiv {
+  uint32_t d = 1, mul = 1, shift = 0;
+  FastDiv() = default;
+  explicit FastDiv(uint32_t divisor) : d(divisor) {
+    while (shift < 31 && (1u << shift) < d) ++shift;
+    mul = (uint32_t)(((uint64_t)1 << 32) * (((uint64_t)1 << shift) - d) / d + 1);
+  }
+  __device__ inline uint32_t div(uint32_t x) const { return (__umulhi(x, mul) + x) >> shift; }
+  __device__ inline uint32_t mod(uint32_t x) const { return x - div(x) * d; }
+};
+
 // 3D-RoPE description: per complex pair p its axis (t, h, w by index ranges)
 // and angular frequency.  Token (frame f, position s in the frame) has
-// coordinates (f, s / grid_w, s % grid_w).
+// coordinates (f, s / grid_w, s % grid_w).  The row and column angles take only
+// grid_h and grid_w values: `tab` (when set) holds their cosine and sine,
+// tab[2 (p * tab_stride + pos) + {0, 1}] for pair p of the h or w axis,
+// computed once per ctx by rope_table with the same sincosf of the same
+// argument, so a lookup returns the values the direct evaluation would.
 struct Rope {
   int pairs_t, pairs_h;     // pairs [0, t) turn with f, [t, t+h) with row, rest with column
   int grid_w, tokens_per_frame;
   float freq[64];
+  const float* tab = nullptr;
+  int tab_stride = 0;
+  FastDiv gw, tpf;          // divisions by grid_w and by tokens_per_frame
+  // host: every field (n frequencies, the rest of freq zero)
+  void set(int pt, int ph, int grid_w_, int tokens, const float* f, int n, const float* table, int stride) {
+    pairs_t = pt;
+    pairs_h = ph;
+    grid_w = grid_w_;
+    tokens_per_frame = tokens;
+    for (int i = 0; i < 64; ++i) freq[i] = i < n ? f[i] : 0.f;
+    tab = table;
+    tab_stride = stride;
+    gw = FastDiv((uint32_t)grid_w_);
+    tpf = FastDiv((uint32_t)tokens);
+  }
   __device__ inline void rotate2(int pair, int64_t frame, int s, float& a, float& b) const {
-    float pos = pair < pairs_t ? (float)frame
-              : (pair < pairs_t + pairs_h ? (float)(s / grid_w) : (float)(s % grid_w));
     float sn, cs;
-    sincosf(pos * freq[pair], &sn, &cs);
+    if (pair >= pairs_t && tab) {
+      const int pos = pair < pairs_t + pairs_h ? (int)gw.div(s) : (int)gw.mod(s);
+      const float2 v = reinterpret_cast<const float2*>(tab)[pair * tab_stride + pos];
+      cs = v.x;
+      sn = v.y;
+    } else {
+      float pos = pair < pairs_t ? (float)frame
+                : (pair < pairs_t + pairs_h ? (float)gw.div(s) : (float)gw.mod(s));
+      sincosf(pos * freq[pair], &sn, &cs);
+    }
     float x = a * cs - b * sn;
     float y = a * sn + b * cs;
     a = x;

@@ -25,11 +25,7 @@ namespace vmla {
 
 static Rope latent_rope(const Plan& p) {
   Rope r;
-  r.pairs_t = p.pairs_t;
-  r.pairs_h = p.pairs_h;
-  r.grid_w = p.grid_w;
-  r.tokens_per_frame = p.Tpf;
-  for (int i = 0; i < kMaxRopePairs; ++i) r.freq[i] = p.freq[i];
+  r.set(p.pairs_t, p.pairs_h, p.grid_w, p.Tpf, p.freq, kMaxRopePairs, p.rope_tab, rope_tab_stride(p.Tpf, p.grid_w));
   return r;
 }
 
@@ -63,11 +59,11 @@ struct EpiExpandKey {
   __device__ void operator()(int z, int m, int n, const float* v) const {
     float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
     if (rot && n >= d_nope) {
-      const int T = rope.tokens_per_frame;
-      const int64_t tau = local_frame(m / T, n_frames, S, W);
+      const int slot = (int)rope.tpf.div(m), s = m - slot * rope.tokens_per_frame;
+      const int64_t tau = local_frame(slot, n_frames, S, W);
       const int pair = (n - d_nope) >> 1;
-      rope.rotate2(pair, tau, m % T, a0, a1);
-      rope.rotate2(pair + 1, tau, m % T, a2, a3);
+      rope.rotate2(pair, tau, s, a0, a1);
+      rope.rotate2(pair + 1, tau, s, a2, a3);
     }
     store4(k + (((long)b * nh + z) * P + m) * dh + n, a0, a1, a2, a3, flag);
   }

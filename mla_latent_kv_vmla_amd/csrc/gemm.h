@@ -200,6 +200,11 @@ template <class E> struct HasRows<E, std::void_t<decltype(E::kRows)>> : std::int
 template <typename O> __device__ inline u32x2 pack4(float a, float b, float c, float d, bool& over) {
   static_assert(sizeof(O) == 2, "16-bit output");
   if constexpr (std::is_same<O, f16>::value) {
+    // one range test for the four values; the saturating path only when it fails
+    const float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)),
+                                     __builtin_fmaxf(__builtin_fabsf(c), __builtin_fabsf(d)));
+    if (!(mx > kF16Max))
+      return u32x2{__builtin_bit_cast(uint32_t, f16x2{(f16)a, (f16)b}), __builtin_bit_cast(uint32_t, f16x2{(f16)c, (f16)d})};
     return u32x2{__builtin_bit_cast(uint32_t, f16x2{to_f16_sat(a, over), to_f16_sat(b, over)}),
                  __builtin_bit_cast(uint32_t, f16x2{to_f16_sat(c, over), to_f16_sat(d, over)})};
   } else {

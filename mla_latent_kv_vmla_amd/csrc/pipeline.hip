@@ -28,11 +28,7 @@ namespace vmla {
 
 static Rope make_rope(const Plan& p) {
   Rope r;
-  r.pairs_t = p.pairs_t;
-  r.pairs_h = p.pairs_h;
-  r.grid_w = p.grid_w;
-  r.tokens_per_frame = p.Tpf;
-  for (int i = 0; i < kMaxRopePairs; ++i) r.freq[i] = p.freq[i];
+  r.set(p.pairs_t, p.pairs_h, p.grid_w, p.Tpf, p.freq, kMaxRopePairs, p.rope_tab, rope_tab_stride(p.Tpf, p.grid_w));
   return r;
 }
 
@@ -44,27 +40,35 @@ template <typename T> struct EpiLatent {
   T* dst;
   long bstride;   // elements per stream in dst
   int64_t frame0;
-  int Nq, W, S, dc, D;
+  int W, S, dc, D;
   int ring, rotate;
+  // ring slot of chunk frame i: i + wrel < 0 -> sink slot frame0 + i, else
+  // S + ((i + wrel) mod W); wrel = (frame0 - S) mod W when frame0 >= S, else
+  // frame0 - S (negative), so i + wrel < W + C <= 2W (no 64-bit modulo per token)
+  int wrel;
+  FastDiv nq;     // chunk tokens per stream
   Rope rope;
   // features n..n+3 of token m after the rotation of the decoupled key channels
   __device__ void values(int m, int n, const float* v, float* a) const {
     a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (n >= dc && rotate) {
-      const int t = m % Nq;
-      const int64_t frame = frame0 + t / rope.tokens_per_frame;
-      const int s = t % rope.tokens_per_frame;
+      const int t = (int)nq.mod(m);
+      const int64_t frame = frame0 + (int)rope.tpf.div(t);
+      const int s = (int)rope.tpf.mod(t);
       const int pair = (n - dc) >> 1;
       rope.rotate2(pair, frame, s, a[0], a[1]);
       rope.rotate2(pair + 1, frame, s, a[2], a[3]);
     }
   }
   __device__ T* row(int, int m, int n) const {
-    const int b = m / Nq, t = m % Nq;
-    const int64_t frame = frame0 + t / rope.tokens_per_frame;
-    const int s = t % rope.tokens_per_frame;
-    const int64_t slot = frame < S ? frame : S + (frame - S) % W;
-    const long r = ring ? (long)slot * rope.tokens_per_frame + s : (long)t;
+    const int b = (int)nq.div(m), t = m - b * (int)nq.d;
+    long r = t;
+    if (ring) {
+      const int i = (int)rope.tpf.div(t), s = t - i * rope.tokens_per_frame;
+      const int rel = i + wrel;
+      const long slot = rel < 0 ? (long)(frame0 + i) : (long)S + (rel >= W ? rel - W : rel);
+      r = slot * rope.tokens_per_frame + s;
+    }
     return dst + b * bstride + r * D + n;
   }
   __device__ void operator()(int z, int m, int n, const float* v) const {
@@ -89,17 +93,18 @@ template <typename T> struct EpiLatent {
 // turned here at the token's (frame, row, column).
 template <typename A> struct EpiQueryAbs {
   A* qt;  // [M][nh*D]
-  int Nq, N, dc, D;
+  int N, dc;
+  FastDiv nq, dd;  // chunk tokens per stream; D = dc + dr features per head
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
   __device__ void values(int m, int n, const float* v, float* a) const {
-    const int j = n % D;
+    const int j = (int)dd.mod(n);
     a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (j >= dc) {
-      const int t = m % Nq;
-      const int64_t frame = frame0 + t / rope.tokens_per_frame;
-      const int s = t % rope.tokens_per_frame;
+      const int t = (int)nq.mod(m);
+      const int64_t frame = frame0 + (int)rope.tpf.div(t);
+      const int s = (int)rope.tpf.mod(t);
       const int pair = (j - dc) >> 1;
       rope.rotate2(pair, frame, s, a[0], a[1]);
       rope.rotate2(pair + 1, frame, s, a[2], a[3]);
@@ -127,24 +132,25 @@ template <typename A> struct EpiQueryAbs {
 // query layout [B][nh][Nq][dh].
 struct EpiQueryHead {
   f16* q;
-  int Nq, nh, dh, d_nope;
+  int nh, dh, d_nope;
+  FastDiv nq, hd;  // chunk tokens per stream; dh features per head
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
   __device__ void values(int m, int n, const float* v, float* a) const {
-    const int t = m % Nq, j = n % dh;
+    const int t = (int)nq.mod(m), j = (int)hd.mod(n);
     a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (j >= d_nope) {
-      const int64_t frame = frame0 + t / rope.tokens_per_frame;
-      const int s = t % rope.tokens_per_frame;
+      const int64_t frame = frame0 + (int)rope.tpf.div(t);
+      const int s = (int)rope.tpf.mod(t);
       const int pair = (j - d_nope) >> 1;
       rope.rotate2(pair, frame, s, a[0], a[1]);
       rope.rotate2(pair + 1, frame, s, a[2], a[3]);
     }
   }
   __device__ f16* row(int, int m, int n) const {
-    const int b = m / Nq, t = m % Nq, h = n / dh, j = n % dh;
-    return q + (((long)b * nh + h) * Nq + t) * dh + j;
+    const int b = (int)nq.div(m), t = m - b * (int)nq.d, h = (int)hd.div(n), j = n - h * dh;
+    return q + (((long)b * nh + h) * (int)nq.d + t) * dh + j;
   }
   __device__ void operator()(int z, int m, int n, const float* v) const {
     float a[4];
@@ -282,6 +288,31 @@ __global__ __launch_bounds__(256) void copy_rows(T* dst, const T* src, long n) {
 
 __global__ void clear_flags(uint32_t* flags) { *flags = 0u; }
 
+// Rotary table: cos and sin of pos * freq[p] for every pair p of the row
+// (pos < grid_h) and column (pos < grid_w) axes, the same sincosf of the same
+// float argument as Rope::rotate2's direct evaluation.
+__global__ __launch_bounds__(256) void rope_table(float* tab, int pairs, int pairs_t, int pairs_h, int grid_h,
+                                                  int grid_w, int stride, Rope r) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < pairs * stride; i += gridDim.x * 256) {
+    const int p = i / stride, pos = i % stride;
+    if (p < pairs_t) continue;
+    const int lim = p < pairs_t + pairs_h ? grid_h : grid_w;
+    float sn = 0.f, cs = 1.f;
+    if (pos < lim) sincosf((float)pos * r.freq[p], &sn, &cs);
+    tab[2 * i] = cs;
+    tab[2 * i + 1] = sn;
+  }
+}
+
+hipError_t run_rope_table(float* tab, int pairs, int pairs_t, int pairs_h, int Tpf, int grid_w, const float* freq,
+                          hipStream_t s) {
+  Rope r;
+  r.set(pairs_t, pairs_h, grid_w, Tpf, freq, kMaxRopePairs, nullptr, 0);
+  const int stride = rope_tab_stride(Tpf, grid_w), n = pairs * stride;
+  rope_table<<<(n + 255) / 256, 256, 0, s>>>(tab, pairs, pairs_t, pairs_h, Tpf / grid_w, grid_w, stride, r);
+  return hipGetLastError();
+}
+
 hipError_t run_clear_flags(uint32_t* flags, hipStream_t s) {
   clear_flags<<<1, 1, 0, s>>>(flags);
   return hipGetLastError();
@@ -297,6 +328,7 @@ static void fold(O* out, const TA* a, const TB* b, int R, int L, int K, float sc
 template <typename T, typename A>
 static void prepare_t(const Plan& p, hipStream_t s) {
   clear_flags<<<1, 1, 0, s>>>(p.flags);
+  (void)run_rope_table(p.rope_tab, p.dr / 2, p.pairs_t, p.pairs_h, p.Tpf, p.grid_w, p.freq, s);  // errors: hipGetLastError below
   {  // [W_DKV; W_KR], rows of `hidden`
     A* wl = static_cast<A*>(p.wlat);
     const long a = (long)p.dc * p.d, b = (long)p.dr * p.d;
@@ -348,9 +380,10 @@ static EpiLatent<T> latent_epilogue(const Plan& p, int64_t frame0, void* dst, bo
   e.dst = static_cast<T*>(dst);
   e.bstride = ring ? (long)(p.S + p.W) * p.Tpf * p.D : (long)p.Nq * p.D;
   e.frame0 = frame0;
-  e.Nq = p.Nq;
+  e.nq = FastDiv((uint32_t)p.Nq);
   e.W = p.W;
   e.S = p.S;
+  e.wrel = frame0 >= p.S ? (int)((frame0 - p.S) % p.W) : (int)(frame0 - p.S);
   e.dc = p.dc;
   e.D = p.D;
   e.ring = ring ? 1 : 0;
@@ -412,10 +445,10 @@ static void chunk_rows_and_queries_t(const Plan& p, const void* x, int64_t frame
   if (form == QueryForm::Absorbed) {
     EpiQueryAbs<A> e;
     e.qt = static_cast<A*>(qdst);
-    e.Nq = p.Nq;
+    e.nq = FastDiv((uint32_t)p.Nq);
+    e.dd = FastDiv((uint32_t)p.D);
     e.N = p.nh * p.D;
     e.dc = p.dc;
-    e.D = p.D;
     e.frame0 = frame0;
     e.rope = make_rope(p);
     e.flag = p.flags;
@@ -423,7 +456,8 @@ static void chunk_rows_and_queries_t(const Plan& p, const void* x, int64_t frame
   } else if constexpr (sizeof(T) == 2) {
     EpiQueryHead e;
     e.q = static_cast<f16*>(qdst);
-    e.Nq = p.Nq;
+    e.nq = FastDiv((uint32_t)p.Nq);
+    e.hd = FastDiv((uint32_t)p.dh);
     e.nh = p.nh;
     e.dh = p.dh;
     e.d_nope = p.d_nope;
@@ -523,6 +557,7 @@ static hipError_t attend_t(const Plan& p, int64_t n, const void* x, void* out, h
     a.grid_w = p.grid_w;
     a.tokens_per_frame = p.Tpf;
     for (int i = 0; i < kMaxRopePairs; ++i) a.freq[i] = p.freq[i];
+    a.rope_tab = p.rope_tab;
     a.stage = p.stage;
     a.out = p.olat;
     a.part_o = p.part_o;

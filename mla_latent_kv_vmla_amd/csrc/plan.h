@@ -45,6 +45,7 @@ struct Plan {
   void* cache;   // [B][(S+W)*Tpf][D]
   // persistent workspace (written by run_prepare)
   uint32_t* flags;  // bit 0: an fp16 operand copy saturated (see kF16Max)
+  float* rope_tab;  // [pairs][rope_tab_stride][2] cos and sin of the row and column angles
   void *wlat;    // [D][d]        [W_DKV; W_KR]
   void *wqa;     // [nh][D][d]    absorbed query weight: per head qscale*[W_UK^h^T W_UQ^h,nope ; W_UQ^h,rope] W_DQ
   void *wuq;     // [nh*dh][d]    qscale * W_UQ W_DQ (per-head queries of the expanded path)
@@ -74,13 +75,21 @@ inline int64_t cached_frames(const Plan& p, int64_t n) {
 // prepared weights) sits at the start of a ctx's workspace; the per-call part
 // follows it there, or fills a clip workspace of its own.
 struct WorkspaceLayout {
-  size_t flags, wlat, wqa, wuq, wuv, wo, persistent;                  // from the workspace start
+  size_t flags, rope_tab, wlat, wqa, wuq, wuv, wo, persistent;        // from the workspace start
   size_t stage, xa, qt, olat, o, part_o, part_ml, vtiles, assembled, per_call;  // from the per-call start
   size_t prep;  // run_prepare's scratch: the first prep_bytes of the per-call part (per_call >= it)
   size_t total;  // persistent + per_call
 };
 
 WorkspaceLayout workspace_layout(const Plan& p);
+// Positions per pair of the rotary table (grid_h or grid_w, whichever is larger).
+inline int rope_tab_stride(int Tpf, int grid_w) { return Tpf / grid_w > grid_w ? Tpf / grid_w : grid_w; }
+inline size_t rope_tab_bytes(int pairs, int Tpf, int grid_w) {
+  return (size_t)pairs * rope_tab_stride(Tpf, grid_w) * 2 * sizeof(float);
+}
+// Fill a rotary table (pairs p >= pairs_t; the t-axis entries stay unused).
+hipError_t run_rope_table(float* tab, int pairs, int pairs_t, int pairs_h, int Tpf, int grid_w, const float* freq,
+                          hipStream_t s);
 // Bytes of one element of the activation type (fp16 for bf16 storage).
 inline size_t act_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
 
@@ -141,6 +150,7 @@ struct AttnCall {
   int64_t rot_n;
   int pairs_t, pairs_h, grid_w, tokens_per_frame;
   float freq[kMaxRopePairs];
+  const float* rope_tab;
 };
 hipError_t run_latent_attention(const AttnCall& a, hipStream_t s);
 bool latent_attention_supported(DType dt, int dc, int dr);
@@ -169,6 +179,7 @@ struct DensePlan {
   void *kring, *vring;  // cache
   // persistent workspace (run_dense_prepare)
   uint32_t* flags;  // bit 0: an fp16 operand copy saturated
+  float* rope_tab;  // rotary table of the row and column axes (see Rope)
   void* wo;         // [d][nh*dv] fp16 W_O
   // per-call workspace
   void *q;       // [B][nh][Nq][dh]  rotated, scaled queries (fp16)
@@ -180,7 +191,7 @@ struct DensePlan {
 
 struct DenseLayout {
   size_t kring, vring, cache_total;                                  // cache
-  size_t flags, wo, q, kstage, vstage, o, part_o, part_ml, ws_total;  // workspace
+  size_t flags, rope_tab, wo, q, kstage, vstage, o, part_o, part_ml, ws_total;  // workspace
 };
 // with_persistent = false (the expanded path's buffer, which takes the flag
 // and W_O of its latent ctx): flags and wo are left out (offsets 0, size 0).

@@ -171,6 +171,7 @@ WorkspaceLayout workspace_layout(const Plan& p) {
     return o;
   };
   L.flags = take(sizeof(uint32_t));
+  L.rope_tab = take(rope_tab_bytes(p.dr / 2, p.Tpf, p.grid_w));
   L.wlat = take((size_t)p.D * p.d * as);
   L.wqa = take((size_t)p.nh * p.D * p.d * as);
   L.wuq = take((size_t)p.nh * p.dh * p.d * as);
@@ -209,6 +210,7 @@ DenseLayout dense_layout(const DensePlan& p, bool with_persistent) {
   L.cache_total = off;
   off = 0;
   L.flags = with_persistent ? take(sizeof(uint32_t)) : 0;
+  L.rope_tab = with_persistent ? take(rope_tab_bytes(p.dh / 2, p.Tpf, p.grid_w)) : 0;
   L.wo = with_persistent ? take((size_t)p.d * p.nh * p.dv * 2) : 0;
   L.q = take(heads * p.Nq * p.dh * 2);
   L.kstage = take(heads * p.stage_stride * p.dh * 2);
@@ -236,6 +238,7 @@ ExpandedLayout expanded_layout(const Plan& p, DensePlan& ex) {
   ex.pairs_h = p.pairs_h;
   ex.pairs_w = p.pairs_w;
   for (int i = 0; i < kMaxRopePairs; ++i) ex.freq[i] = p.freq[i];
+  ex.rope_tab = p.rope_tab;
   ex.qscale = p.qscale;
   ex.G = p.G;
   ex.ring_stride = (int)(((long)(p.S + p.W) * p.Tpf + kDenseKeyTile - 1) / kDenseKeyTile * kDenseKeyTile);
@@ -353,6 +356,7 @@ static void set_ctx_pointers(Plan& p, const vmla_ctx* c) {
   const vmla::WorkspaceLayout L = vmla::workspace_layout(geometry(&c->cfg));
   char* ws = static_cast<char*>(c->workspace);
   p.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  p.rope_tab = reinterpret_cast<float*>(ws + L.rope_tab);
   p.wlat = ws + L.wlat;
   p.wqa = ws + L.wqa;
   p.wuq = ws + L.wuq;
@@ -666,6 +670,7 @@ static DensePlan make_dense_plan(const vmla_dense_ctx* c) {
   p.kring = cache + L.kring;
   p.vring = cache + L.vring;
   p.flags = reinterpret_cast<uint32_t*>(ws + L.flags);
+  p.rope_tab = reinterpret_cast<float*>(ws + L.rope_tab);
   p.wo = ws + L.wo;
   p.q = ws + L.q;
   p.kstage = ws + L.kstage;
