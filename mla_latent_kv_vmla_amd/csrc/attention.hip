@@ -19,10 +19,11 @@
 //                                                      the B operand of this product)
 // so softmax statistics live per lane (one query row per lane pair) and P never
 // leaves registers.  Two kernels share this layout: flash_attn_kernel (8 waves
-// x 32 rows, two waves per SIMD hiding each other's softmax; every width and
-// the dense layer) and flash_attn_pipe_kernel (4 waves x 64 rows, one wave per
-// SIMD that pipelines its own softmax under its MFMAs; latent d_c = 192 with
-// bf16 storage).
+// x 32 rows, two waves per SIMD hiding each other's softmax, or 4 waves at the
+// widest score width; the dense layer, d_c = 448, fp32 storage and the tiny
+// layer) and flash_attn_pipe_kernel (4 waves x 64 rows, one wave per SIMD that
+// pipelines its own softmax under its MFMAs; latent d_c = 96 and 192 with bf16
+// storage).
 //
 // Staging.  Tiles are copied into LDS with LDS-DMA loads through a buffer
 // resource (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at M0 + 16 L),
@@ -160,6 +161,19 @@ __device__ inline float pair_max(float v) {
 __device__ inline float pair_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 32x32x16 f16 MFMAs with VGPR accumulators, issued from asm (the compiler keeps
+// every MFMA of a kernel that needs AGPRs in the AGPR form).  The compiler does
+// not see these as MFMAs: a VALU read of their result must come at least one
+// MFMA issue plus a few wait states later (callers place one).
+__device__ inline f32x16 mfma_vgpr(f16x8 a, f16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+__device__ inline void mfma_vgpr_acc(f32x16& acc, f16x8 a, f16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 // acc *= alpha for an accumulator held in AGPRs.  Each element passes through
@@ -762,28 +776,35 @@ struct PipeSlotPlan {
   bool ok;
 };
 constexpr int pipe_item_cost(int i) { return i < 48 ? 2 : i < 80 ? 1 : 4; }
-// issue order: exponentials of each half interleaved with the packs they complete
-constexpr int pipe_item_order(int j) {
+// Items in issue order: exponentials of each half interleaved with the packs
+// they complete, then (COPIES) the copies, then maxes and tests.  Without
+// copies (scores accumulated in VGPRs, which the maxes read directly) the
+// order has 54 entries and skips items 48..79.
+constexpr int pipe_nitems(bool copies) { return copies ? 86 : 54; }
+constexpr int pipe_item_order(int j, bool copies) {
   if (j < 48) {
     const int h = j / 24, r = j % 24, grp = r / 3, pos = r % 3;  // per pair q: E[2q], E[2q+1], P[q]
     return pos < 2 ? 24 * h + 2 * grp + pos : 24 * h + 16 + grp;
   }
-  return j;
+  return copies ? j : j + 32;
 }
-constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget) {
+constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies) {
   PipeSlotPlan p{};
   p.budget = budget;
   p.ok = true;
   const int NS = NQ + 2 * NV;
+  const int NI = pipe_nitems(copies);
   int load[128] = {};
   int cur = 0;
-  for (int j = 0; j < PipeSlotPlan::NITEM; ++j) {
-    const int i = pipe_item_order(j);
+  for (int i = 0; i < PipeSlotPlan::NITEM; ++i) p.slot_of[i] = -1;
+  for (int j = 0; j < NI; ++j) {
+    const int i = pipe_item_order(j, copies);
     int earliest = cur;
     if (i >= 16 && i < 24) earliest = p.slot_of[2 * (i - 16) + 1] + 1;
     if (i >= 40 && i < 48) earliest = p.slot_of[24 + 2 * (i - 40) + 1] + 1;
     if (i >= 48 && i < 80) earliest = NQ + 1;
-    if (i >= 80 && i < 84) earliest = p.slot_of[48 + 16 * ((i - 80) >> 1) + 8 * ((i - 80) & 1) + 7] + 1;
+    if (i >= 80 && i < 84)
+      earliest = copies ? p.slot_of[48 + 16 * ((i - 80) >> 1) + 8 * ((i - 80) & 1) + 7] + 1 : NQ + 1;
     if (i >= 84) earliest = p.slot_of[80 + 2 * (i - 84) + 1] + 1;
     int s = earliest > cur ? earliest : cur;
     while (s < NS && load[s] > 0 && load[s] + pipe_item_cost(i) > budget) ++s;
@@ -801,22 +822,23 @@ constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget) {
   }
   // items go to slots in issue order, so each slot holds a run of it
   for (int s = 0; s < PipeSlotPlan::MAXS; ++s) p.lo[s] = p.hi[s] = PipeSlotPlan::NITEM;
-  for (int j = PipeSlotPlan::NITEM - 1; j >= 0; --j) p.lo[p.slot_of[pipe_item_order(j)]] = j;
-  for (int j = 0; j < PipeSlotPlan::NITEM; ++j) p.hi[p.slot_of[pipe_item_order(j)]] = j + 1;
+  for (int j = NI - 1; j >= 0; --j) p.lo[p.slot_of[pipe_item_order(j, copies)]] = j;
+  for (int j = 0; j < NI; ++j) p.hi[p.slot_of[pipe_item_order(j, copies)]] = j + 1;
   for (int s = 0; s < NS; ++s) {
     if (p.lo[s] == PipeSlotPlan::NITEM) p.lo[s] = p.hi[s] = 0;
     if (p.hi[s] - p.lo[s] > PipeSlotPlan::MAXPER) p.ok = false;
   }
   return p;
 }
-constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV) {
+constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV, bool copies) {
   for (int b = 3; b <= 12; ++b) {
-    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b);
+    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b, copies);
     if (p.ok) return p;
   }
-  return pipe_slot_plan_b(NQ, NV, 0);
+  return pipe_slot_plan_b(NQ, NV, 0, copies);
 }
-template <int NQ, int NV> inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV);
+template <int NQ, int NV, bool COPIES>
+inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES);
 
 // Software-pipelined latent attention, bf16 storage.  One workgroup = 4 waves
 // (one per SIMD) x 64 query rows (two 32-row blocks), so every K and V fragment
@@ -831,7 +853,11 @@ template <int NQ, int NV> inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slo
 // (score product) and the tile two ahead (DMA in flight); one barrier per
 // tile.  Same staging (fp16 key tiles, V^T by transposing reads), scheduling
 // and numerics as flash_attn_kernel, whose comments cover them.
-template <int D, int DV, int KTILE>
+// VSC (score widths up to 128): the score accumulators live in VGPRs, two sets
+// whose roles alternate every step (the current block's, on which its softmax
+// runs, and the next block's, which the score MFMAs -- issued from asm in the
+// VGPR form -- accumulate), so the softmax needs no AGPR copies.
+template <int D, int DV, int KTILE, bool VSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   using T = bf16;
@@ -950,9 +976,9 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         asm volatile("" : "+a"(o[nb][fb]));
       }
     }
-    f32x16 sc[NB];    // score accumulators of the next block (AGPRs)
+    f32x16 sc[NB];    // score accumulators of the next block (AGPRs; VSC: one of the two VGPR sets)
     f32x16 negm[NB];  // -m_run splat: the score MFMAs start from it, so they produce s - m_run
-    f32x16 d[NB];     // scores (minus m_run) of the current block, copied out of sc (VGPRs)
+    f32x16 d[NB];     // scores (minus m_run) of the current block, copied out of sc (VGPRs; VSC: the other set)
     f16x8 kq[KA];     // K fragments of the next score product, read ahead
     f16x8 pf[NB][2];
 
@@ -1005,10 +1031,16 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       for (int ks = 0; ks < NKS; ++ks) {
         const f16x8 a = kfrag(buf, kb, ks);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[nb][ks], sc[nb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) {
+          if constexpr (VSC) mfma_vgpr_acc(sc[nb], a, qf[nb][ks]);
+          else sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[nb][ks], sc[nb], 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(sc[nb]));
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (VSC) asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sc[nb]));  // results before VALU reads
+        else asm volatile("" : "+a"(sc[nb]));
+      }
     };
     // Softmax work items of one block (d: VGPR copy of its scores), in the
     // order they are issued between MFMAs.  Elements of the block are taken in
@@ -1033,12 +1065,13 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) negm[nb][rr] = -m_run[nb];
-        asm volatile("" : "+a"(negm[nb]));
+        if constexpr (VSC) asm volatile("s_nop 3" : "+v"(negm[nb]));  // VALU writes before an MFMA reads them
+        else asm volatile("" : "+a"(negm[nb]));
       }
     };
     // Rows whose block max exceeds m_run by more than the slack move m_run
     // up; o and l follow.  Rare: a real (uniform) branch.
-    auto rescale = [&]() __attribute__((always_inline)) {
+    auto rescale = [&](f32x16 (&d)[NB]) __attribute__((always_inline)) {
       if (__any(need[0] || need[1])) {
         asm volatile("");
         asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");  // value MFMAs still writing o
@@ -1102,7 +1135,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     // last slots.  has_next = false (last block of a job): no score product.
     auto step = [&](const T* qbuf, int qkb, int t, int kb, const T* pbuf, bool has_next, bool kq_ready,
                     const T* nqbuf, int nqkb, bool prefetch, bool dma, __amdgpu_buffer_rsrc_t krs,
-                    T* dbuf) __attribute__((always_inline)) {
+                    T* dbuf, f32x16 (&d)[NB], f32x16 (&sc)[NB]) __attribute__((always_inline)) {
       if (needs_mask(t, kb)) {
         asm volatile("");
         mask(d, t, kb);
@@ -1111,7 +1144,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         cmp_item(0);
         cmp_item(1);
       }
-      rescale();
+      rescale(d);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) lsum[nb] = 0.f;
       if (!has_next) {
@@ -1136,14 +1169,20 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         }
         f16x8 vq[KA];
         constexpr int NQ = 2 * NKS, NS = NQ + 2 * NV;
-        static_assert(kPipeSlotPlan<NQ, NV>.ok, "no issue-slot plan meets the deadlines");
+        constexpr PipeSlotPlan plan = kPipeSlotPlan<NQ, NV, !VSC>;
+        static_assert(plan.ok, "no issue-slot plan meets the deadlines");
         auto slot_work = [&](int slot) __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
           const int nb = slot & 1;
           if (slot < NQ) {  // score MFMA (k-step slot/2, row block nb); next K fragment after the last use
             const int ks = slot >> 1;
-            sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq[ks % KA], qf[nb][ks], ks == 0 ? negm[nb] : sc[nb], 0, 0,
-                                                            0);
+            if constexpr (VSC) {
+              if (ks == 0) sc[nb] = mfma_vgpr(kq[ks % KA], qf[nb][ks], negm[nb]);
+              else mfma_vgpr_acc(sc[nb], kq[ks % KA], qf[nb][ks]);
+            } else {
+              sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq[ks % KA], qf[nb][ks], ks == 0 ? negm[nb] : sc[nb], 0,
+                                                              0, 0);
+            }
             if (nb == 1 && ks + KA < NKS) kq[ks % KA] = kfrag(qbuf, qkb, ks + KA);
             if (slot >= NQ - 2 * KA && nb == 0)
               vq[(slot - (NQ - 2 * KA)) / 2] = vfrag_n(pbuf, kb, (slot - (NQ - 2 * KA)) / 2);
@@ -1153,18 +1192,25 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
                 __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[n % KA], pf[nb][n / NFB], o[nb][n % NFB], 0, 0, 0);
             if (nb == 1 && n + KA < NV) vq[n % KA] = vfrag_n(pbuf, kb, n + KA);
           }
+          // VSC: the maxes read the accumulators of MFMAs the compiler does not
+          // track; wait states ahead of the first
+          if constexpr (VSC)
+            if (slot == plan.slot_of[80]) asm volatile("s_nop 7\n\ts_nop 3" ::: "memory");
 #pragma unroll
           for (int k = 0; k < PipeSlotPlan::MAXPER; ++k) {
-            const int j = kPipeSlotPlan<NQ, NV>.lo[slot] + k;
-            if (j >= kPipeSlotPlan<NQ, NV>.hi[slot]) continue;
-            const int i = pipe_item_order(j);
+            const int j = plan.lo[slot] + k;
+            if (j >= plan.hi[slot]) continue;
+            const int i = pipe_item_order(j, !VSC);
             if (i < 16) exp_item(d, 0, i);
             else if (i < 24) pack_item(d, 0, i - 16);
             else if (i < 40) exp_item(d, 1, i - 24);
             else if (i < 48) pack_item(d, 1, i - 40);
-            else if (i < 80) copy_item(i - 48);
-            else if (i < 84) max_item(d, i - 80);
-            else cmp_item(i - 84);
+            else if (i < 80) {
+              if constexpr (!VSC) copy_item(i - 48);
+            } else if (i < 84) {
+              if constexpr (VSC) max_item(sc, i - 80);  // the next block's scores, in the accumulators
+              else max_item(d, i - 80);
+            } else cmp_item(i - 84);
           }
           // After the step's last transposing read: the compiler cannot tell the
           // DMA's stage from the stages being read and waits for the DMA before
@@ -1196,7 +1242,10 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         for (int slot = 7 * NS8; slot < NS; ++slot) slot_work(slot);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(sc[nb]));
+        for (int nb = 0; nb < NB; ++nb) {
+          if constexpr (VSC) asm volatile("" : "+v"(sc[nb]));
+          else asm volatile("" : "+a"(sc[nb]));
+        }
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -1211,11 +1260,13 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     // Prologue: block 0's plain scores; their row max starts m_run (every
     // job's first block holds a valid key for every row, so it is finite).
     // K fragments of block 1 read ahead.
-    qk_only(sc, lds + st_cur, 0);
+    qk_only(VSC ? d : sc, lds + st_cur, 0);
 #pragma unroll
     for (int i = 0; i < KA; ++i) kq[i] = kfrag(lds + st_cur, 1, i);
+    if constexpr (!VSC) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) copy_item(e);
+      for (int e = 0; e < 32; ++e) copy_item(e);
+    }
     mask(d, kt0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) max_item(d, q);
@@ -1241,10 +1292,11 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       // (no tile t+2: an empty resource, whose loads write zeros into the free
       // stage, keeps the slots free of branches)
       const auto krs = i + 2 < ntiles ? tile_rsrc(s, t + 2) : raw_rsrc(p.val0, 0u);
-      step(cur, 1, t, 0, cur, true, true, lds + st_nxt, 0, true, true, krs, lds + st_nn);
+      step(cur, 1, t, 0, cur, true, true, lds + st_nxt, 0, true, true, krs, lds + st_nn, d, sc);
       // block 1 of tile t under the scores of block 0 of tile t+1; reads ahead
       // the K fragments of block 1 of tile t+1
-      step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, lds + st_nn);
+      if constexpr (VSC) step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, lds + st_nn, sc, d);
+      else step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, lds + st_nn, d, sc);
       const uint32_t st_old = st_cur;
       st_cur = st_nxt;
       st_nxt = st_nn;
@@ -1254,8 +1306,9 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       const int t = kt1 - 1;
       const T* cur = lds + st_cur;
       const auto krs = tile_rsrc(s, t);
-      step(cur, 1, t, 0, cur, true, true, cur, 0, false, false, krs, lds + st_nn);
-      step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, lds + st_nn);
+      step(cur, 1, t, 0, cur, true, true, cur, 0, false, false, krs, lds + st_nn, d, sc);
+      if constexpr (VSC) step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, lds + st_nn, sc, d);
+      else step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, lds + st_nn, d, sc);
     }
 
     const bool full = causal || (kt0 == 0 && kt1 == p.KT);
@@ -1378,7 +1431,7 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   void* kernel;
   if constexpr (PIPE) {
     static_assert(NW == 4 && NB == 2 && !VROWS && sizeof(T) == 2, "pipelined kernel shape");
-    kernel = reinterpret_cast<void*>(&flash_attn_pipe_kernel<D, DV, KTILE>);
+    kernel = reinterpret_cast<void*>(&flash_attn_pipe_kernel<D, DV, KTILE, (D <= 128)>);
   } else {
     kernel = reinterpret_cast<void*>(&flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS>);
   }
@@ -1402,7 +1455,7 @@ static bool latent_shape(DType dt, int dc, int dr, LatentShape& sh) {
     return false;
   }
   if (dc == 24 && dr == 8) return sh = {64, 4, 1}, true;
-  if (dr == 32 && dc == 96) return sh = {128, 8, 1}, true;
+  if (dr == 32 && dc == 96) return sh = {64, 4, 2}, true;
   if (dr == 32 && dc == 192) return sh = {64, 4, 2}, true;
   if (dr == 32 && dc == 448) return sh = {64, 4, 1}, true;
   return false;
@@ -1460,7 +1513,7 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
   } else {
     if (c.dc == 24 && c.dr == 8) return launch_flash<T, 32, 24, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     if (c.dr == 32) {
-      if (c.dc == 96) return launch_flash<T, 128, 96, 128, 8, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+      if (c.dc == 96) return launch_flash<T, 128, 96, 64, 4, 2, false, true>(a, c.G, c.ev_start, c.ev_stop, s);
       if (c.dc == 192) return launch_flash<T, 224, 192, 64, 4, 2, false, true>(a, c.G, c.ev_start, c.ev_stop, s);
       if (c.dc == 448) return launch_flash<T, 480, 448, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
     }
