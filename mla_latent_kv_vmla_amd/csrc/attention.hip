@@ -775,7 +775,9 @@ struct PipeSlotPlan {
   int budget;
   bool ok;
 };
-constexpr int pipe_item_cost(int i) { return i < 48 ? 2 : i < 80 ? 1 : 4; }
+constexpr int pipe_item_cost(int i, int pack_cost) {
+  return (i >= 16 && i < 24) || (i >= 40 && i < 48) ? pack_cost : i < 48 ? 2 : i < 80 ? 1 : 4;
+}
 // Items in issue order: exponentials of each half interleaved with the packs
 // they complete, then (COPIES) the copies, then maxes and tests.  Without
 // copies (scores accumulated in VGPRs, which the maxes read directly) the
@@ -788,7 +790,7 @@ constexpr int pipe_item_order(int j, bool copies) {
   }
   return copies ? j : j + 32;
 }
-constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies) {
+constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies, int pack_cost) {
   PipeSlotPlan p{};
   p.budget = budget;
   p.ok = true;
@@ -807,13 +809,13 @@ constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies)
       earliest = copies ? p.slot_of[48 + 16 * ((i - 80) >> 1) + 8 * ((i - 80) & 1) + 7] + 1 : NQ + 1;
     if (i >= 84) earliest = p.slot_of[80 + 2 * (i - 84) + 1] + 1;
     int s = earliest > cur ? earliest : cur;
-    while (s < NS && load[s] > 0 && load[s] + pipe_item_cost(i) > budget) ++s;
+    while (s < NS && load[s] > 0 && load[s] + pipe_item_cost(i, pack_cost) > budget) ++s;
     if (s >= NS) {
       p.ok = false;
       return p;
     }
     p.slot_of[i] = s;
-    load[s] += pipe_item_cost(i);
+    load[s] += pipe_item_cost(i, pack_cost);
     cur = s;
     int deadline = NS - 1;
     if (i >= 16 && i < 24) deadline = NQ - 1 + ((i - 16) >= 4 ? 1 : 0);
@@ -830,15 +832,15 @@ constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies)
   }
   return p;
 }
-constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV, bool copies) {
+constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV, bool copies, int pack_cost) {
   for (int b = 3; b <= 12; ++b) {
-    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b, copies);
+    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b, copies, pack_cost);
     if (p.ok) return p;
   }
-  return pipe_slot_plan_b(NQ, NV, 0, copies);
+  return pipe_slot_plan_b(NQ, NV, 0, copies, pack_cost);
 }
-template <int NQ, int NV, bool COPIES>
-inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES);
+template <int NQ, int NV, bool COPIES, int PACKC>
+inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC);
 
 // Software-pipelined latent attention, bf16 storage.  One workgroup = 4 waves
 // (one per SIMD) x 64 query rows (two 32-row blocks), so every K and V fragment
@@ -876,7 +878,11 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   constexpr int KI = KTILE * CH / 64;  // 1-KB loads per tile
   constexpr int NKS = D / 16;    // score k-steps of 16 channels
   constexpr int NFB = G::DVP / 32;
-  constexpr int NV = 2 * NFB;    // value fragments per block
+  // VSC: one more value block whose A operand is a constant 1.0 fragment, so
+  // its accumulator holds the row sums of P, rescaled with O (no v_dot2 sums)
+  constexpr bool ONES = VSC;
+  constexpr int NFV = NFB + (ONES ? 1 : 0);  // value accumulator blocks
+  constexpr int NV = 2 * NFV;    // value MFMAs per block and row block
   constexpr int NST = 3;
   constexpr int KA = 2;          // fragment reads in flight ahead of their MFMA
   constexpr int NI_W = KI / NW;
@@ -965,13 +971,13 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       for (int ks = 0; ks < NKS; ++ks)
         qf[nb][ks] = qrow < p.R ? *reinterpret_cast<const f16x8*>(qsrc + 16 * ks) : f16x8{};
     }
-    f32x16 o[NB][NFB];
+    f32x16 o[NB][NFV];
     float m_run[NB], l_run[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       l_run[nb] = 0.f;
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) {
+      for (int fb = 0; fb < NFV; ++fb) {
         o[nb][fb] = f32x16{};
         asm volatile("" : "+a"(o[nb][fb]));
       }
@@ -1082,7 +1088,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           m_run[nb] += dm;
           l_run[nb] *= alpha;
 #pragma unroll
-          for (int fb = 0; fb < NFB; ++fb) scale_acc_agpr(o[nb][fb], alpha);
+          for (int fb = 0; fb < NFV; ++fb) scale_acc_agpr(o[nb][fb], alpha);
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) d[nb][rr] -= dm;  // re-base this block's scores
         }
@@ -1100,11 +1106,19 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       const f16x2 one2 = {(f16)1.f, (f16)1.f};
       pf[nb][u][j] = (f16)d[nb][8 * u + j];
       pf[nb][u][j + 1] = (f16)d[nb][8 * u + j + 1];
-      lsum[nb] = __builtin_amdgcn_fdot2(f16x2{pf[nb][u][j], pf[nb][u][j + 1]}, one2, lsum[nb], false);
+      if constexpr (!ONES)
+        lsum[nb] = __builtin_amdgcn_fdot2(f16x2{pf[nb][u][j], pf[nb][u][j + 1]}, one2, lsum[nb], false);
     };
-    // value fragment n in issue order: half n/NFB, 32-channel block n%NFB
-    auto vfrag_n = [&](const T* buf, int kb, int n) __attribute__((always_inline)) {
-      return vfrag(buf, kb, 2 * (n % NFB) + n / NFB);
+    // value fragment n in issue order: half n/NFV, 32-channel block n%NFV (the
+    // ones block: a constant 1.0 fragment, no LDS read)
+    auto vfrag_n = [&](const T* buf, int kb, int n) __attribute__((always_inline)) -> f16x8 {
+      if (ONES && n % NFV == NFB) {
+        f16x8 one;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) one[e] = (f16)1.f;
+        return one;
+      }
+      return vfrag(buf, kb, 2 * (n % NFV) + n / NFV);
     };
 
     auto copy_item = [&](int e) __attribute__((always_inline)) {  // element e (0..31) of sc -> d
@@ -1160,7 +1174,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           const f16x8 a = vfrag_n(pbuf, kb, n);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            o[nb][n % NFB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][n / NFB], o[nb][n % NFB], 0, 0, 0);
+            o[nb][n % NFV] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[nb][n / NFV], o[nb][n % NFV], 0, 0, 0);
         }
       } else {
         if (!kq_ready) {
@@ -1169,7 +1183,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         }
         f16x8 vq[KA];
         constexpr int NQ = 2 * NKS, NS = NQ + 2 * NV;
-        constexpr PipeSlotPlan plan = kPipeSlotPlan<NQ, NV, !VSC>;
+        constexpr PipeSlotPlan plan = kPipeSlotPlan<NQ, NV, !VSC, ONES ? 1 : 2>;
         static_assert(plan.ok, "no issue-slot plan meets the deadlines");
         auto slot_work = [&](int slot) __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
@@ -1188,8 +1202,8 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
               vq[(slot - (NQ - 2 * KA)) / 2] = vfrag_n(pbuf, kb, (slot - (NQ - 2 * KA)) / 2);
           } else {  // value MFMA (fragment n, row block nb)
             const int n = (slot - NQ) >> 1;
-            o[nb][n % NFB] =
-                __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[n % KA], pf[nb][n / NFB], o[nb][n % NFB], 0, 0, 0);
+            o[nb][n % NFV] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[n % KA], pf[nb][n / NFV], o[nb][n % NFV], 0, 0, 0);
             if (nb == 1 && n + KA < NV) vq[n % KA] = vfrag_n(pbuf, kb, n + KA);
           }
           // VSC: the maxes read the accumulators of MFMAs the compiler does not
@@ -1249,9 +1263,9 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        l_run[nb] += lsum[nb];
+        if constexpr (!ONES) l_run[nb] += lsum[nb];
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) asm volatile("" : "+a"(o[nb][fb]));
+        for (int fb = 0; fb < NFV; ++fb) asm volatile("" : "+a"(o[nb][fb]));
       }
     };
 
@@ -1315,7 +1329,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     VT* out_s = static_cast<VT*>(p.out) + (s / p.heads) * p.out_so + (s % p.heads) * p.out_sh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const float l_tot = pair_sum(l_run[nb]);
+      const float l_tot = ONES ? o[nb][NFB][0] : pair_sum(l_run[nb]);
       const int qrow = row0 + 32 * nb + l32;
       if (full) {
         if (qrow < p.R) {

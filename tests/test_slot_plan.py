@@ -17,7 +17,8 @@ rule here, stated independently of the planner's procedure:
   copies and every max follows the last score MFMA by at least one slot; a
   row's rescale test follows both of its maxes;
 - each slot's work stays within the plan's budget of plain-VALU units (a
-  v_exp_f32 counts two) and within eight items;
+  v_exp_f32 counts two, a pack two with its v_dot2 row sum, one where the
+  row sums come from a ones block of value MFMAs) and within eight items;
 - items issue in order: each half's exponentials interleaved with the packs they
   complete, then copies (if any), maxes and tests.
 """
@@ -29,20 +30,21 @@ import pytest
 
 SRC = pathlib.Path(__file__).resolve().parents[1] / "mla_latent_kv_vmla_amd" / "csrc" / "attention.hip"
 
-# (NQ, NV, copies) per built pipelined width: NQ = 2 row blocks x (d_c + d_r) / 16
-# k-steps, NV = 2 x d_c / 32 value fragments; copies: AGPR score accumulators.
-WIDTHS = {192: (28, 12, True), 96: (16, 6, False)}
-BUDGET = {192: 4, 96: 6}
+# (NQ, NV, copies, pack cost) per built pipelined width: NQ = 2 row blocks x
+# (d_c + d_r) / 16 k-steps, NV = 2 x (d_c / 32 value fragments, plus the ones
+# block at d_c 96); copies: AGPR score accumulators.
+WIDTHS = {192: (28, 12, True, 2), 96: (16, 8, False, 1)}
+BUDGET = {192: 4, 96: 5}
 
 N_ITEMS = 86
 EXP0, PACK0, EXP1, PACK1, COPY, MAX, CMP = 0, 16, 24, 40, 48, 80, 84
 
 
-def _cost(i):
+def _cost(i, pack_cost):
     if EXP0 <= i < PACK0 or EXP1 <= i < PACK1:
         return 2  # v_exp_f32
     if PACK0 <= i < EXP1 or PACK1 <= i < COPY:
-        return 2  # v_cvt_pk_f16_f32 + v_dot2
+        return pack_cost  # v_cvt_pk_f16_f32 (+ v_dot2)
     if COPY <= i < MAX:
         return 1  # v_accvgpr_read
     return 4      # max over 8 scores (v_maximum3 chain) / pair max + test
@@ -63,11 +65,11 @@ def plans(tmp_path_factory):
         pytest.skip("no host C++ compiler")
     s = SRC.read_text()
     a = s.index("struct PipeSlotPlan {")
-    e = s.index("\n", s.index("inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES);")) + 1
-    dumps = "".join(f"  dump<{nq}, {nv}, {'true' if c else 'false'}>();\n" for nq, nv, c in WIDTHS.values())
+    e = s.index("\n", s.index("inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC);")) + 1
+    dumps = "".join(f"  dump<{nq}, {nv}, {'true' if c else 'false'}, {pc}>();\n" for nq, nv, c, pc in WIDTHS.values())
     prog = ("#include <cstdio>\n" + s[a:e] + """
-template <int NQ, int NV, bool C> void dump() {
-  constexpr PipeSlotPlan p = kPipeSlotPlan<NQ, NV, C>;
+template <int NQ, int NV, bool C, int PC> void dump() {
+  constexpr PipeSlotPlan p = kPipeSlotPlan<NQ, NV, C, PC>;
   std::printf("%d %d %d %d\\n", NQ, NV, (int)p.ok, p.budget);
   for (int i = 0; i < PipeSlotPlan::NITEM; ++i) std::printf("%d ", p.slot_of[i]);
   std::printf("\\n");
@@ -87,7 +89,7 @@ int main() {
 
 @pytest.mark.parametrize("dc", sorted(WIDTHS))
 def test_plan_meets_every_rule(plans, dc):
-    nq, nv, copies = WIDTHS[dc]
+    nq, nv, copies, pack_cost = WIDTHS[dc]
     ok, budget, slot = plans[(nq, nv)]
     ns = nq + 2 * nv
     assert ok and len(slot) == N_ITEMS
@@ -113,7 +115,7 @@ def test_plan_meets_every_rule(plans, dc):
         assert slot[CMP + nb] > max(slot[MAX + 2 * nb], slot[MAX + 2 * nb + 1]), nb
     load, count = [0] * ns, [0] * ns
     for i in placed:
-        load[slot[i]] += _cost(i)
+        load[slot[i]] += _cost(i, pack_cost)
         count[slot[i]] += 1
     assert max(load) <= budget and max(count) <= 8
     order = [slot[i] for i in _issue_order(copies)]
