@@ -237,8 +237,11 @@ __global__ __launch_bounds__(NWN * NWM * 64) void gemm_dma_kernel(GemmDmaOps<T> 
   static_assert(FN >= 1 && FM >= 1 && WTN % 32 == 0 && WTM % 32 == 0, "wave tile");
   static_assert(BW % NW == 0 && BX % NW == 0, "DMA split");
   static_assert(NST >= 2 && (NST - 2) * NLD < 64, "stages");
+  // the 16-bit output tile [BM][BN] goes through LDS in rows of BN * 2 + 16 B
+  constexpr int RS = BN * 2 + 16, CPR = BN / 8;
+  constexpr int LDS_BYTES = HasRows<Epi>::value && BM * RS > NST * STAGE ? BM * RS : NST * STAGE;
 
-  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   // XCD-aware tile order: launch index b runs on XCD b % 8; the tiles of one
   // XCD are consecutive in (z, m-tile, n-tile) order, so they share X rows.
@@ -323,10 +326,8 @@ __global__ __launch_bounds__(NWN * NWM * 64) void gemm_dma_kernel(GemmDmaOps<T> 
   wait_vmcnt<0>();
 
   if constexpr (HasRows<Epi>::value) {
-    // output tile [BM][BN] of 16-bit values through LDS (rows of BN * 2 + 16 B),
-    // then whole 16-B chunks of each token's row to the epilogue's destination
-    constexpr int RS = BN * 2 + 16, CPR = BN / 8;
-    static_assert(BM * RS <= NST * STAGE, "output tile fits the stages");
+    // output tile [BM][BN] of 16-bit values through LDS, then whole 16-B
+    // chunks of each token's row to the epilogue's destination
     __syncthreads();  // every wave is done reading the stages
     bool over = false;
 #pragma unroll
@@ -371,18 +372,35 @@ __global__ __launch_bounds__(NWN * NWM * 64) void gemm_dma_kernel(GemmDmaOps<T> 
   }
 }
 
-// Tile shape of the DMA GEMM: 128 x 128, 4 waves (64 x 64 each), two stages
-// (64 KB of LDS: two workgroups per compute unit).  On the projection shapes
-// of the Wan-1.3B layer this was the fastest of the 64..256-row tile shapes,
-// 4 or 8 waves and 2..4 stages measured on MI355X.
+// Tile shapes of the DMA GEMM, two stages each:
+// - 128 x 128, 4 waves (64 x 64 each): 64 KB of LDS, two workgroups per
+//   compute unit;
+// - 256 x 256, 8 waves (64 x 128 each): 128 KB of LDS (135 KB with the output
+//   tile of a row epilogue), one workgroup per compute unit.
+// On MI355X one round of 256 x 256 tiles (one per compute unit) took ~1.7x a
+// round of 128 x 128 tiles (two per compute unit) on the Wan-1.3B projection
+// shapes, the other 64..256-row shapes with 4 or 8 waves and 2..4 stages
+// slower still; the larger tile is taken when it needs fewer rounds by that
+// ratio (7/4), for epilogues that stage the output tile through LDS (the
+// per-element epilogues keep the 128 x 128 tile: their 32 unrolled calls per
+// lane at 256 x 256 do not stay in registers).
 template <typename T, class Epi>
 inline void launch_gemm_dma(GemmDmaOps<T> op, const Epi& epi, hipStream_t s) {
-  constexpr int BN = 128, BM = 128;
+  const long t128 = (long)((op.N + 127) / 128) * ((op.M + 127) / 128) * op.Z;
+  const long t256 = (long)((op.N + 255) / 256) * ((op.M + 255) / 256) * op.Z;
+  const bool big = HasRows<Epi>::value && 7 * ((t256 + 255) / 256) < 4 * ((t128 + 511) / 512);
+  const int BN = big ? 256 : 128, BM = BN;
   op.tn = (op.N + BN - 1) / BN;
   op.tm = (op.M + BM - 1) / BM;
   const int T_all = op.tn * op.tm * op.Z;
   const int grid = (T_all + 7) / 8 * 8;
-  gemm_dma_kernel<T, BN, BM, 2, 2, 2, Epi><<<grid, 256, 0, s>>>(op, epi);
+  if constexpr (HasRows<Epi>::value) {
+    if (big) {
+      gemm_dma_kernel<T, 256, 256, 4, 2, 2, Epi><<<grid, 512, 0, s>>>(op, epi);
+      return;
+    }
+  }
+  gemm_dma_kernel<T, 128, 128, 2, 2, 2, Epi><<<grid, 256, 0, s>>>(op, epi);
 }
 
 // Y[m][n] -> y[z*yz + m*ldy + n] in the output type O (fp16 outputs saturate
