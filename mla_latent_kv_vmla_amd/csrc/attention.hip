@@ -758,7 +758,7 @@ void flash_attn_kernel(FlashArgs<T> p) {
 // half 1).  Work items, in issue order, with their cost in plain-VALU units
 // (a v_exp_f32 counts 2):
 //   [0, 16)   exponential k of half 0 (row block k/8, element 8u + k%8 with u = 0)
-//   [16, 24)  fp16 pack + v_dot2 row sum of half-0 pair q (elements 2q, 2q+1)
+//   [16, 24)  fp16 pack (+ v_dot2 row sum) of half-0 pair q (elements 2q, 2q+1)
 //   [24, 40)  exponentials of half 1;  [40, 48) packs of half 1
 //   [48, 80)  copy of score element e of the next block out of its accumulator
 //   [80, 84)  block max over 8 elements;  [84, 86) pair max and rescale test
@@ -768,6 +768,10 @@ void flash_attn_kernel(FlashArgs<T> p) {
 // copies, a test after its maxes).  Half-u packs must precede the first value
 // MFMA that reads them.  The plan uses the smallest budget that meets every
 // deadline: about four plain VALU instructions fit behind one MFMA on gfx950.
+// Packs cost 2 units with their v_dot2 row sum, 1 without it; then (LAG) each
+// pack issues after the next pair's two exponentials, so a slot takes two
+// exponentials or one with a pack (or two), and packing in issue order does
+// not leave a slot at 2 or 3 units behind every pack.
 struct PipeSlotPlan {
   static constexpr int NITEM = 86, MAXS = 128, MAXPER = 8;
   int slot_of[NITEM];
@@ -783,14 +787,22 @@ constexpr int pipe_item_cost(int i, int pack_cost) {
 // copies (scores accumulated in VGPRs, which the maxes read directly) the
 // order has 54 entries and skips items 48..79.
 constexpr int pipe_nitems(bool copies) { return copies ? 86 : 54; }
-constexpr int pipe_item_order(int j, bool copies) {
+constexpr int pipe_item_order(int j, bool copies, bool lag) {
   if (j < 48) {
-    const int h = j / 24, r = j % 24, grp = r / 3, pos = r % 3;  // per pair q: E[2q], E[2q+1], P[q]
-    return pos < 2 ? 24 * h + 2 * grp + pos : 24 * h + 16 + grp;
+    const int h = j / 24, r = j % 24;
+    if (!lag) {  // per pair q: E[2q], E[2q+1], P[q]
+      const int grp = r / 3, pos = r % 3;
+      return pos < 2 ? 24 * h + 2 * grp + pos : 24 * h + 16 + grp;
+    }
+    // E[0], E[1], then E[2q], E[2q+1], P[q-1] for q = 1..7, then P[7]
+    if (r < 2) return 24 * h + r;
+    if (r == 23) return 24 * h + 23;
+    const int grp = (r - 2) / 3, pos = (r - 2) % 3;
+    return pos < 2 ? 24 * h + 2 * (grp + 1) + pos : 24 * h + 16 + grp;
   }
   return copies ? j : j + 32;
 }
-constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies, int pack_cost) {
+constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies, int pack_cost, bool lag) {
   PipeSlotPlan p{};
   p.budget = budget;
   p.ok = true;
@@ -800,7 +812,7 @@ constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies,
   int cur = 0;
   for (int i = 0; i < PipeSlotPlan::NITEM; ++i) p.slot_of[i] = -1;
   for (int j = 0; j < NI; ++j) {
-    const int i = pipe_item_order(j, copies);
+    const int i = pipe_item_order(j, copies, lag);
     int earliest = cur;
     if (i >= 16 && i < 24) earliest = p.slot_of[2 * (i - 16) + 1] + 1;
     if (i >= 40 && i < 48) earliest = p.slot_of[24 + 2 * (i - 40) + 1] + 1;
@@ -824,23 +836,23 @@ constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies,
   }
   // items go to slots in issue order, so each slot holds a run of it
   for (int s = 0; s < PipeSlotPlan::MAXS; ++s) p.lo[s] = p.hi[s] = PipeSlotPlan::NITEM;
-  for (int j = NI - 1; j >= 0; --j) p.lo[p.slot_of[pipe_item_order(j, copies)]] = j;
-  for (int j = 0; j < NI; ++j) p.hi[p.slot_of[pipe_item_order(j, copies)]] = j + 1;
+  for (int j = NI - 1; j >= 0; --j) p.lo[p.slot_of[pipe_item_order(j, copies, lag)]] = j;
+  for (int j = 0; j < NI; ++j) p.hi[p.slot_of[pipe_item_order(j, copies, lag)]] = j + 1;
   for (int s = 0; s < NS; ++s) {
     if (p.lo[s] == PipeSlotPlan::NITEM) p.lo[s] = p.hi[s] = 0;
     if (p.hi[s] - p.lo[s] > PipeSlotPlan::MAXPER) p.ok = false;
   }
   return p;
 }
-constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV, bool copies, int pack_cost) {
+constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV, bool copies, int pack_cost, bool lag) {
   for (int b = 3; b <= 12; ++b) {
-    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b, copies, pack_cost);
+    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b, copies, pack_cost, lag);
     if (p.ok) return p;
   }
-  return pipe_slot_plan_b(NQ, NV, 0, copies, pack_cost);
+  return pipe_slot_plan_b(NQ, NV, 0, copies, pack_cost, lag);
 }
-template <int NQ, int NV, bool COPIES, int PACKC>
-inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC);
+template <int NQ, int NV, bool COPIES, int PACKC, bool LAG>
+inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC, LAG);
 
 // Software-pipelined latent attention, bf16 storage.  One workgroup = 4 waves
 // (one per SIMD) x 64 query rows (two 32-row blocks), so every K and V fragment
@@ -1183,7 +1195,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
         }
         f16x8 vq[KA];
         constexpr int NQ = 2 * NKS, NS = NQ + 2 * NV;
-        constexpr PipeSlotPlan plan = kPipeSlotPlan<NQ, NV, !VSC, ONES ? 1 : 2>;
+        constexpr PipeSlotPlan plan = kPipeSlotPlan<NQ, NV, !VSC, ONES ? 1 : 2, ONES>;
         static_assert(plan.ok, "no issue-slot plan meets the deadlines");
         auto slot_work = [&](int slot) __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
@@ -1214,7 +1226,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           for (int k = 0; k < PipeSlotPlan::MAXPER; ++k) {
             const int j = plan.lo[slot] + k;
             if (j >= plan.hi[slot]) continue;
-            const int i = pipe_item_order(j, !VSC);
+            const int i = pipe_item_order(j, !VSC, ONES);
             if (i < 16) exp_item(d, 0, i);
             else if (i < 24) pack_item(d, 0, i - 16);
             else if (i < 40) exp_item(d, 1, i - 24);

@@ -20,7 +20,8 @@ rule here, stated independently of the planner's procedure:
   v_exp_f32 counts two, a pack two with its v_dot2 row sum, one where the
   row sums come from a ones block of value MFMAs) and within eight items;
 - items issue in order: each half's exponentials interleaved with the packs they
-  complete, then copies (if any), maxes and tests.
+  complete (a pack right after its pair's second exponential, or, with one-unit
+  packs, after the next pair's), then copies (if any), maxes and tests.
 """
 import pathlib
 import shutil
@@ -30,11 +31,11 @@ import pytest
 
 SRC = pathlib.Path(__file__).resolve().parents[1] / "mla_latent_kv_vmla_amd" / "csrc" / "attention.hip"
 
-# (NQ, NV, copies, pack cost) per built pipelined width: NQ = 2 row blocks x
-# (d_c + d_r) / 16 k-steps, NV = 2 x (d_c / 32 value fragments, plus the ones
-# block at d_c 96); copies: AGPR score accumulators.
-WIDTHS = {192: (28, 12, True, 2), 96: (16, 8, False, 1)}
-BUDGET = {192: 4, 96: 5}
+# (NQ, NV, copies, pack cost, lagged packs) per built pipelined width: NQ = 2
+# row blocks x (d_c + d_r) / 16 k-steps, NV = 2 x (d_c / 32 value fragments,
+# plus the ones block at d_c 96); copies: AGPR score accumulators.
+WIDTHS = {192: (28, 12, True, 2, False), 96: (16, 8, False, 1, True)}
+BUDGET = {192: 4, 96: 4}
 
 N_ITEMS = 86
 EXP0, PACK0, EXP1, PACK1, COPY, MAX, CMP = 0, 16, 24, 40, 48, 80, 84
@@ -50,11 +51,17 @@ def _cost(i, pack_cost):
     return 4      # max over 8 scores (v_maximum3 chain) / pair max + test
 
 
-def _issue_order(copies):
+def _issue_order(copies, lag):
     order = []
     for base_e, base_p in ((EXP0, PACK0), (EXP1, PACK1)):
         for q in range(8):
-            order += [base_e + 2 * q, base_e + 2 * q + 1, base_p + q]
+            order += [base_e + 2 * q, base_e + 2 * q + 1]
+            if not lag:
+                order.append(base_p + q)
+            elif q > 0:
+                order.append(base_p + q - 1)
+        if lag:
+            order.append(base_p + 7)
     return order + list(range(COPY if copies else MAX, N_ITEMS))
 
 
@@ -65,11 +72,12 @@ def plans(tmp_path_factory):
         pytest.skip("no host C++ compiler")
     s = SRC.read_text()
     a = s.index("struct PipeSlotPlan {")
-    e = s.index("\n", s.index("inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC);")) + 1
-    dumps = "".join(f"  dump<{nq}, {nv}, {'true' if c else 'false'}, {pc}>();\n" for nq, nv, c, pc in WIDTHS.values())
+    e = s.index("\n", s.index("inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC, LAG);")) + 1
+    b = lambda v: "true" if v else "false"
+    dumps = "".join(f"  dump<{nq}, {nv}, {b(c)}, {pc}, {b(lag)}>();\n" for nq, nv, c, pc, lag in WIDTHS.values())
     prog = ("#include <cstdio>\n" + s[a:e] + """
-template <int NQ, int NV, bool C, int PC> void dump() {
-  constexpr PipeSlotPlan p = kPipeSlotPlan<NQ, NV, C, PC>;
+template <int NQ, int NV, bool C, int PC, bool L> void dump() {
+  constexpr PipeSlotPlan p = kPipeSlotPlan<NQ, NV, C, PC, L>;
   std::printf("%d %d %d %d\\n", NQ, NV, (int)p.ok, p.budget);
   for (int i = 0; i < PipeSlotPlan::NITEM; ++i) std::printf("%d ", p.slot_of[i]);
   std::printf("\\n");
@@ -89,7 +97,7 @@ int main() {
 
 @pytest.mark.parametrize("dc", sorted(WIDTHS))
 def test_plan_meets_every_rule(plans, dc):
-    nq, nv, copies, pack_cost = WIDTHS[dc]
+    nq, nv, copies, pack_cost, lag = WIDTHS[dc]
     ok, budget, slot = plans[(nq, nv)]
     ns = nq + 2 * nv
     assert ok and len(slot) == N_ITEMS
@@ -118,6 +126,6 @@ def test_plan_meets_every_rule(plans, dc):
         load[slot[i]] += _cost(i, pack_cost)
         count[slot[i]] += 1
     assert max(load) <= budget and max(count) <= 8
-    order = [slot[i] for i in _issue_order(copies)]
+    order = [slot[i] for i in _issue_order(copies, lag)]
     assert order == sorted(order)
 
