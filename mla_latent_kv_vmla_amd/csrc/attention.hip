@@ -753,10 +753,11 @@ void flash_attn_kernel(FlashArgs<T> p) {
 }
 
 // Issue-slot plan of the pipelined kernel's softmax work (see step() in
-// flash_attn_pipe_kernel).  A step has NS = NQ + 2 NV slots, one MFMA each
-// (NQ score MFMAs, then 2 NV value MFMAs: half 0 of the block's keys, then
-// half 1).  Work items, in issue order, with their cost in plain-VALU units
-// (a v_exp_f32 counts 2):
+// flash_attn_pipe_kernel).  With NB 32-row blocks per wave, a step has
+// NS = NQ + NB NV slots, one MFMA each (NQ score MFMAs, then NB NV value
+// MFMAs: half 0 of the block's keys, then half 1).  Work items, with their
+// cost in plain-VALU units (a v_exp_f32 counts 2), for NB = 2 (NB = 1 keeps
+// the items of row block 0 only):
 //   [0, 16)   exponential k of half 0 (row block k/8, element 8u + k%8 with u = 0)
 //   [16, 24)  fp16 pack (+ v_dot2 row sum) of half-0 pair q (elements 2q, 2q+1)
 //   [24, 40)  exponentials of half 1;  [40, 48) packs of half 1
@@ -786,33 +787,41 @@ constexpr int pipe_item_cost(int i, int pack_cost) {
 // they complete, then (COPIES) the copies, then maxes and tests.  Without
 // copies (scores accumulated in VGPRs, which the maxes read directly) the
 // order has 54 entries and skips items 48..79.
-constexpr int pipe_nitems(bool copies) { return copies ? 86 : 54; }
-constexpr int pipe_item_order(int j, bool copies, bool lag) {
-  if (j < 48) {
-    const int h = j / 24, r = j % 24;
+// With NB = 1 the order keeps its shape over the items of row block 0
+// (exponentials 8 per half, packs 4, copies 16, maxes 2, one test).
+constexpr int pipe_nitems(bool copies, int nb) { return 27 * nb + (copies ? 16 * nb : 0); }
+constexpr int pipe_item_order(int j, bool copies, bool lag, int nb) {
+  const int H = 12 * nb, np = 4 * nb;  // entries and exponential pairs per half
+  if (j < 2 * H) {
+    const int h = j / H, r = j % H;
     if (!lag) {  // per pair q: E[2q], E[2q+1], P[q]
       const int grp = r / 3, pos = r % 3;
       return pos < 2 ? 24 * h + 2 * grp + pos : 24 * h + 16 + grp;
     }
-    // E[0], E[1], then E[2q], E[2q+1], P[q-1] for q = 1..7, then P[7]
+    // E[0], E[1], then E[2q], E[2q+1], P[q-1] for q = 1..np-1, then P[np-1]
     if (r < 2) return 24 * h + r;
-    if (r == 23) return 24 * h + 23;
+    if (r == H - 1) return 24 * h + 16 + np - 1;
     const int grp = (r - 2) / 3, pos = (r - 2) % 3;
     return pos < 2 ? 24 * h + 2 * (grp + 1) + pos : 24 * h + 16 + grp;
   }
-  return copies ? j : j + 32;
+  j -= 2 * H;
+  if (copies) {
+    if (j < 16 * nb) return 48 + j;
+    j -= 16 * nb;
+  }
+  return j < 2 * nb ? 80 + j : 84 + (j - 2 * nb);
 }
-constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies, int pack_cost, bool lag) {
+constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies, int pack_cost, bool lag, int nb) {
   PipeSlotPlan p{};
   p.budget = budget;
   p.ok = true;
-  const int NS = NQ + 2 * NV;
-  const int NI = pipe_nitems(copies);
+  const int NS = NQ + nb * NV;
+  const int NI = pipe_nitems(copies, nb);
   int load[128] = {};
   int cur = 0;
   for (int i = 0; i < PipeSlotPlan::NITEM; ++i) p.slot_of[i] = -1;
   for (int j = 0; j < NI; ++j) {
-    const int i = pipe_item_order(j, copies, lag);
+    const int i = pipe_item_order(j, copies, lag, nb);
     int earliest = cur;
     if (i >= 16 && i < 24) earliest = p.slot_of[2 * (i - 16) + 1] + 1;
     if (i >= 40 && i < 48) earliest = p.slot_of[24 + 2 * (i - 40) + 1] + 1;
@@ -829,30 +838,31 @@ constexpr PipeSlotPlan pipe_slot_plan_b(int NQ, int NV, int budget, bool copies,
     p.slot_of[i] = s;
     load[s] += pipe_item_cost(i, pack_cost);
     cur = s;
+    // a half-u pack of row block r precedes value MFMA slot NQ + u nb NV / 2 + r
     int deadline = NS - 1;
-    if (i >= 16 && i < 24) deadline = NQ - 1 + ((i - 16) >= 4 ? 1 : 0);
-    if (i >= 40 && i < 48) deadline = NQ + NV - 1 + ((i - 40) >= 4 ? 1 : 0);
+    if (i >= 16 && i < 24) deadline = NQ - 1 + ((i - 16) >> 2);
+    if (i >= 40 && i < 48) deadline = NQ + nb * NV / 2 - 1 + ((i - 40) >> 2);
     if (s > deadline) p.ok = false;
   }
   // items go to slots in issue order, so each slot holds a run of it
   for (int s = 0; s < PipeSlotPlan::MAXS; ++s) p.lo[s] = p.hi[s] = PipeSlotPlan::NITEM;
-  for (int j = NI - 1; j >= 0; --j) p.lo[p.slot_of[pipe_item_order(j, copies, lag)]] = j;
-  for (int j = 0; j < NI; ++j) p.hi[p.slot_of[pipe_item_order(j, copies, lag)]] = j + 1;
+  for (int j = NI - 1; j >= 0; --j) p.lo[p.slot_of[pipe_item_order(j, copies, lag, nb)]] = j;
+  for (int j = 0; j < NI; ++j) p.hi[p.slot_of[pipe_item_order(j, copies, lag, nb)]] = j + 1;
   for (int s = 0; s < NS; ++s) {
     if (p.lo[s] == PipeSlotPlan::NITEM) p.lo[s] = p.hi[s] = 0;
     if (p.hi[s] - p.lo[s] > PipeSlotPlan::MAXPER) p.ok = false;
   }
   return p;
 }
-constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV, bool copies, int pack_cost, bool lag) {
+constexpr PipeSlotPlan pipe_slot_plan(int NQ, int NV, bool copies, int pack_cost, bool lag, int nb) {
   for (int b = 3; b <= 12; ++b) {
-    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b, copies, pack_cost, lag);
+    const PipeSlotPlan p = pipe_slot_plan_b(NQ, NV, b, copies, pack_cost, lag, nb);
     if (p.ok) return p;
   }
-  return pipe_slot_plan_b(NQ, NV, 0, copies, pack_cost, lag);
+  return pipe_slot_plan_b(NQ, NV, 0, copies, pack_cost, lag, nb);
 }
-template <int NQ, int NV, bool COPIES, int PACKC, bool LAG>
-inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC, LAG);
+template <int NQ, int NV, bool COPIES, int PACKC, bool LAG, int NB>
+inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PACKC, LAG, NB);
 
 // Software-pipelined latent attention, bf16 storage.  One workgroup = 4 waves
 // (one per SIMD) x 64 query rows (two 32-row blocks), so every K and V fragment
@@ -867,17 +877,27 @@ inline constexpr PipeSlotPlan kPipeSlotPlan = pipe_slot_plan(NQ, NV, COPIES, PAC
 // (score product) and the tile two ahead (DMA in flight); one barrier per
 // tile.  Same staging (fp16 key tiles, V^T by transposing reads), scheduling
 // and numerics as flash_attn_kernel, whose comments cover them.
-// VSC (score widths up to 128): the score accumulators live in VGPRs, two sets
-// whose roles alternate every step (the current block's, on which its softmax
-// runs, and the next block's, which the score MFMAs -- issued from asm in the
-// VGPR form -- accumulate), so the softmax needs no AGPR copies.
-template <int D, int DV, int KTILE, bool VSC>
+// VSC (score widths up to 128, or one row block per wave): the score
+// accumulators live in VGPRs, two sets whose roles alternate every step (the
+// current block's, on which its softmax runs, and the next block's, which the
+// score MFMAs -- issued from asm in the VGPR form -- accumulate), so the
+// softmax needs no AGPR copies.
+// NB = 1 (d_c 448: 14 value blocks of 32 channels fill the AGPRs) gives each
+// wave 32 rows, so each fragment read feeds one MFMA.  NST = 2 (a 64-key tile
+// of 480 channels is 60 KB, so three stages exceed the LDS): tile t+1 takes
+// the stage of tile t-1 once every wave is past it, i.e. its loads are issued
+// in the first slots of the step that finishes the scores of tile t and must
+// land by the next; they are issued from asm so that the compiler adds no
+// wait for them before the LDS reads of that step.
+template <int D, int DV, int KTILE, bool VSC, int NB, int NST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   using T = bf16;
   using VT = f16;  // query, value-operand and output type
   using G = TileGeo<T, D, DV, KTILE>;
-  constexpr int NW = 4, NB = 2, RW = 64;
+  constexpr int NW = 4, RW = 32 * NB;
+  static_assert(NB == 1 || NB == 2, "one or two 32-row blocks per wave");
+  static_assert(NST == 2 || NST == 3, "two or three LDS stages");
   // LDS key tile (16-B chunk c of key row r): four regions of 16 rows (wave w
   // loads region w), each of CH/4 blocks of 1 KB holding chunks 4k..4k+3 of
   // its rows; within a block, chunk c sits at 256 (c % 4) + 16 ((r % 16) ^
@@ -890,14 +910,18 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   constexpr int KI = KTILE * CH / 64;  // 1-KB loads per tile
   constexpr int NKS = D / 16;    // score k-steps of 16 channels
   constexpr int NFB = G::DVP / 32;
-  // VSC: one more value block whose A operand is a constant 1.0 fragment, so
-  // its accumulator holds the row sums of P, rescaled with O (no v_dot2 sums)
-  constexpr bool ONES = VSC;
+  // VSC with two row blocks: one more value block whose A operand is a
+  // constant 1.0 fragment, so its accumulator holds the row sums of P,
+  // rescaled with O (no v_dot2 sums; with one row block the AGPRs are full)
+  constexpr bool ONES = VSC && NB == 2;
   constexpr int NFV = NFB + (ONES ? 1 : 0);  // value accumulator blocks
   constexpr int NV = 2 * NFV;    // value MFMAs per block and row block
-  constexpr int NST = 3;
-  constexpr int KA = 2;          // fragment reads in flight ahead of their MFMA
+#ifndef VMLA_KA1
+#define VMLA_KA1 4
+#endif
+  constexpr int KA = NB == 2 ? 2 : VMLA_KA1;  // fragment reads in flight ahead of their first MFMA
   constexpr int NI_W = KI / NW;
+  constexpr int DS = NST == 3 ? 4 : (NI_W + 1) / 2;  // slots carrying a tile's loads, two per slot
   static_assert(CH % 4 == 0 && KI % NW == 0 && KTILE == 16 * NW, "tile layout: one 16-row region per wave");
   static_assert(KTILE == 64, "two 32-key blocks per tile");
   static_assert(NW * RW <= kAttnMaxRows && G::DVP <= D, "bad shape");
@@ -905,7 +929,8 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
 
   __shared__ __attribute__((aligned(16))) T lds[NST * KS_EL];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = NST == 2 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
   const float NEG_INF = -__builtin_huge_valf();
 
@@ -917,14 +942,19 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   // region `wave`; lane L fills slot L: chunk 4k + L/16 of row
   // 16 wave + ((L % 16) ^ 4 (L / 16)).  The pre-pass stores the tile as this
   // LDS image, so the load copies the block's 1 KB of contiguous bytes.
+  // `st`: element offset of the destination stage.
   const uint32_t dma_voff = (uint32_t)((wave * REG_EL + 8 * lane) * 2);
-  auto issue_part = [&](__amdgpu_buffer_rsrc_t krs, T* buf, int k) __attribute__((always_inline)) {
-    lds_dma16(krs, dma_voff + (uint32_t)(1024 * k), buf + wave * REG_EL + k * 512);
+  const uint32_t lds_u32 = (uint32_t)(size_t)(__attribute__((address_space(3))) T*)lds;
+  auto issue_part = [&](__amdgpu_buffer_rsrc_t krs, uint32_t st, int k) __attribute__((always_inline)) {
+    if constexpr (NST == 2)
+      dma16_lds(krs, dma_voff + (uint32_t)(1024 * k), lds_u32 + 2 * (st + (uint32_t)(wave * REG_EL + k * 512)));
+    else
+      lds_dma16(krs, dma_voff + (uint32_t)(1024 * k), lds + st + wave * REG_EL + k * 512);
   };
-  auto issue_tile = [&](int s, int t, T* buf) __attribute__((always_inline)) {
+  auto issue_tile = [&](int s, int t, uint32_t st) __attribute__((always_inline)) {
     const auto krs = tile_rsrc(s, t);
 #pragma unroll
-    for (int k = 0; k < NI_W; ++k) issue_part(krs, buf, k);
+    for (int k = 0; k < NI_W; ++k) issue_part(krs, st, k);
   };
 
   const bool causal = p.causal_tokens > 0;
@@ -966,13 +996,13 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     // element offsets of the stages of tiles i, i+1, i+2 (rotated per tile; no
     // modulo, so LDS addresses stay provably non-negative and fragment offsets
     // fold into the read instructions)
-    uint32_t st_cur = 0, st_nxt = KS_EL, st_nn = 2 * KS_EL;
+    uint32_t st_cur = 0, st_nxt = KS_EL, st_nn = NST == 3 ? 2 * KS_EL : 0;
 
     // every wave is done with the stages of the previous job
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    issue_tile(s, kt0, lds + st_cur);
-    if (ntiles > 1) issue_tile(s, kt0 + 1, lds + st_nxt);
+    issue_tile(s, kt0, st_cur);
+    if (ntiles > 1) issue_tile(s, kt0 + 1, st_nxt);
 
     f16x8 qf[NB][NKS];
 #pragma unroll
@@ -1090,7 +1120,10 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     // Rows whose block max exceeds m_run by more than the slack move m_run
     // up; o and l follow.  Rare: a real (uniform) branch.
     auto rescale = [&](f32x16 (&d)[NB]) __attribute__((always_inline)) {
-      if (__any(need[0] || need[1])) {
+      bool any_need = need[0];
+#pragma unroll
+      for (int nb = 1; nb < NB; ++nb) any_need = any_need || need[nb];
+      if (__any(any_need)) {
         asm volatile("");
         asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15");  // value MFMAs still writing o
 #pragma unroll
@@ -1161,14 +1194,14 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     // last slots.  has_next = false (last block of a job): no score product.
     auto step = [&](const T* qbuf, int qkb, int t, int kb, const T* pbuf, bool has_next, bool kq_ready,
                     const T* nqbuf, int nqkb, bool prefetch, bool dma, __amdgpu_buffer_rsrc_t krs,
-                    T* dbuf, f32x16 (&d)[NB], f32x16 (&sc)[NB]) __attribute__((always_inline)) {
+                    uint32_t dbuf, f32x16 (&d)[NB], f32x16 (&sc)[NB]) __attribute__((always_inline)) {
       if (needs_mask(t, kb)) {
         asm volatile("");
         mask(d, t, kb);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) max_item(d, q);
-        cmp_item(0);
-        cmp_item(1);
+        for (int q = 0; q < 2 * NB; ++q) max_item(d, q);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) cmp_item(nb);
       }
       rescale(d);
 #pragma unroll
@@ -1177,9 +1210,9 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int k = 0; k < 16; ++k) exp_item(d, u, k);
+          for (int k = 0; k < 8 * NB; ++k) exp_item(d, u, k);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) pack_item(d, u, q);
+          for (int q = 0; q < 4 * NB; ++q) pack_item(d, u, q);
         }
 #pragma unroll
         for (int n = 0; n < NV; ++n) {
@@ -1194,14 +1227,14 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           for (int i = 0; i < KA; ++i) kq[i] = kfrag(qbuf, qkb, i);
         }
         f16x8 vq[KA];
-        constexpr int NQ = 2 * NKS, NS = NQ + 2 * NV;
-        constexpr PipeSlotPlan plan = kPipeSlotPlan<NQ, NV, !VSC, ONES ? 1 : 2, ONES>;
+        constexpr int NQ = NB * NKS, NS = NQ + NB * NV;
+        constexpr PipeSlotPlan plan = kPipeSlotPlan<NQ, NV, !VSC, ONES ? 1 : 2, ONES, NB>;
         static_assert(plan.ok, "no issue-slot plan meets the deadlines");
         auto slot_work = [&](int slot) __attribute__((always_inline)) {
           __builtin_amdgcn_sched_barrier(0);
-          const int nb = slot & 1;
-          if (slot < NQ) {  // score MFMA (k-step slot/2, row block nb); next K fragment after the last use
-            const int ks = slot >> 1;
+          const int nb = slot % NB;
+          if (slot < NQ) {  // score MFMA (k-step slot/NB, row block nb); next K fragment after the last use
+            const int ks = slot / NB;
             if constexpr (VSC) {
               if (ks == 0) sc[nb] = mfma_vgpr(kq[ks % KA], qf[nb][ks], negm[nb]);
               else mfma_vgpr_acc(sc[nb], kq[ks % KA], qf[nb][ks]);
@@ -1209,14 +1242,14 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
               sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kq[ks % KA], qf[nb][ks], ks == 0 ? negm[nb] : sc[nb], 0,
                                                               0, 0);
             }
-            if (nb == 1 && ks + KA < NKS) kq[ks % KA] = kfrag(qbuf, qkb, ks + KA);
-            if (slot >= NQ - 2 * KA && nb == 0)
-              vq[(slot - (NQ - 2 * KA)) / 2] = vfrag_n(pbuf, kb, (slot - (NQ - 2 * KA)) / 2);
+            if (nb == NB - 1 && ks + KA < NKS) kq[ks % KA] = kfrag(qbuf, qkb, ks + KA);
+            if (slot >= NQ - NB * KA && nb == 0)
+              vq[(slot - (NQ - NB * KA)) / NB] = vfrag_n(pbuf, kb, (slot - (NQ - NB * KA)) / NB);
           } else {  // value MFMA (fragment n, row block nb)
-            const int n = (slot - NQ) >> 1;
+            const int n = (slot - NQ) / NB;
             o[nb][n % NFV] =
                 __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[n % KA], pf[nb][n / NFV], o[nb][n % NFV], 0, 0, 0);
-            if (nb == 1 && n + KA < NV) vq[n % KA] = vfrag_n(pbuf, kb, n + KA);
+            if (nb == NB - 1 && n + KA < NV) vq[n % KA] = vfrag_n(pbuf, kb, n + KA);
           }
           // VSC: the maxes read the accumulators of MFMAs the compiler does not
           // track; wait states ahead of the first
@@ -1226,7 +1259,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
           for (int k = 0; k < PipeSlotPlan::MAXPER; ++k) {
             const int j = plan.lo[slot] + k;
             if (j >= plan.hi[slot]) continue;
-            const int i = pipe_item_order(j, !VSC, ONES);
+            const int i = pipe_item_order(j, !VSC, ONES, NB);
             if (i < 16) exp_item(d, 0, i);
             else if (i < 24) pack_item(d, 0, i - 16);
             else if (i < 40) exp_item(d, 1, i - 24);
@@ -1238,15 +1271,19 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
               else max_item(d, i - 80);
             } else cmp_item(i - 84);
           }
-          // After the step's last transposing read: the compiler cannot tell the
-          // DMA's stage from the stages being read and waits for the DMA before
-          // any later transposing read (the next step's first, ~25 slots on).
-          if (dma && slot >= NS - 4) {
+          // NST = 3: after the step's last transposing read: the compiler cannot
+          // tell the DMA's stage from the stages being read and waits for the
+          // DMA before any later transposing read (the next step's first, ~25
+          // slots on).  NST = 2: in the first slots (asm loads, no such wait).
+          if (dma) {
+            const int ds = NST == 3 ? slot - (NS - DS) : slot;
+            if (ds >= 0 && ds < DS) {
 #pragma unroll
-            for (int k = 2 * (slot - (NS - 4)); k < 2 * (slot - (NS - 4)) + 2 && k < NI_W; ++k) issue_part(krs, dbuf, k);
+              for (int k = 2 * ds; k < 2 * ds + 2 && k < NI_W; ++k) issue_part(krs, dbuf, k);
+            }
           }
-          if (prefetch && slot >= NS - 2 * KA && slot % 2 == 1)
-            kq[(slot - (NS - 2 * KA)) / 2] = kfrag(nqbuf, nqkb, (slot - (NS - 2 * KA)) / 2);
+          if (prefetch && slot >= NS - NB * KA && slot % NB == NB - 1)
+            kq[(slot - (NS - NB * KA)) / NB] = kfrag(nqbuf, nqkb, (slot - (NS - NB * KA)) / NB);
         };
         // eight loops, so each stays within the compiler's full-unroll size limit
         constexpr int NS8 = (NS + 7) / 8;
@@ -1295,7 +1332,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
     }
     mask(d, kt0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) max_item(d, q);
+    for (int q = 0; q < 2 * NB; ++q) max_item(d, q);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       m_run[nb] = pair_max(mloc[nb]);
@@ -1304,37 +1341,61 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
       need[nb] = false;
     }
     set_negm();
-    for (int i = 0; i + 1 < ntiles; ++i) {
-      const int t = kt0 + i;
-      const T* cur = lds + st_cur;
-      // Tile t+1 has landed and every wave is past tile t-1 (its last reads
-      // were the value product of the previous step), whose stage takes tile
-      // t+2.
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      // block 0 of tile t under the scores of its block 1, with the loads of
-      // tile t+2 issued in its first slots; reads ahead the K fragments of
-      // block 0 of tile t+1
-      // (no tile t+2: an empty resource, whose loads write zeros into the free
-      // stage, keeps the slots free of branches)
-      const auto krs = i + 2 < ntiles ? tile_rsrc(s, t + 2) : raw_rsrc(p.val0, 0u);
-      step(cur, 1, t, 0, cur, true, true, lds + st_nxt, 0, true, true, krs, lds + st_nn, d, sc);
-      // block 1 of tile t under the scores of block 0 of tile t+1; reads ahead
-      // the K fragments of block 1 of tile t+1
-      if constexpr (VSC) step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, lds + st_nn, sc, d);
-      else step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, lds + st_nn, d, sc);
-      const uint32_t st_old = st_cur;
-      st_cur = st_nxt;
-      st_nxt = st_nn;
-      st_nn = st_old;
+    if constexpr (NST == 3) {
+      for (int i = 0; i + 1 < ntiles; ++i) {
+        const int t = kt0 + i;
+        const T* cur = lds + st_cur;
+        // Tile t+1 has landed and every wave is past tile t-1 (its last reads
+        // were the value product of the previous step), whose stage takes tile
+        // t+2.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // block 0 of tile t under the scores of its block 1, with the loads of
+        // tile t+2 issued in its last slots; reads ahead the K fragments of
+        // block 0 of tile t+1
+        // (no tile t+2: an empty resource, whose loads write zeros into the free
+        // stage, keeps the slots free of branches)
+        const auto krs = i + 2 < ntiles ? tile_rsrc(s, t + 2) : raw_rsrc(p.val0, 0u);
+        step(cur, 1, t, 0, cur, true, true, lds + st_nxt, 0, true, true, krs, st_nn, d, sc);
+        // block 1 of tile t under the scores of block 0 of tile t+1; reads ahead
+        // the K fragments of block 1 of tile t+1
+        if constexpr (VSC) step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, st_nn, sc, d);
+        else step(lds + st_nxt, 0, t, 1, cur, true, true, lds + st_nxt, 1, true, false, krs, st_nn, d, sc);
+        const uint32_t st_old = st_cur;
+        st_cur = st_nxt;
+        st_nxt = st_nn;
+        st_nn = st_old;
+      }
+    } else {
+      for (int i = 0; i + 1 < ntiles; ++i) {
+        const int t = kt0 + i;
+        const T* cur = lds + st_cur;
+        // Tile t+1: loaded by the prologue for i = 0; otherwise into the stage
+        // of tile t-1 once every wave is past it (its last reads were the value
+        // product of the previous step), issued in the first slots of block 0
+        // of tile t, waited for before block 1.
+        const bool load = i > 0;
+        if (load) __syncthreads();
+        const auto krs = load ? tile_rsrc(s, t + 1) : raw_rsrc(p.val0, 0u);
+        step(cur, 1, t, 0, cur, true, true, lds + st_nxt, 0, !load, load, krs, st_nxt, d, sc);
+        if (load) {
+          wait_vmcnt<0>();
+          __syncthreads();
+        }
+        if constexpr (VSC) step(lds + st_nxt, 0, t, 1, cur, true, !load, lds + st_nxt, 1, true, false, krs, st_nxt, sc, d);
+        else step(lds + st_nxt, 0, t, 1, cur, true, !load, lds + st_nxt, 1, true, false, krs, st_nxt, d, sc);
+        const uint32_t st_old = st_cur;
+        st_cur = st_nxt;
+        st_nxt = st_old;
+      }
     }
     {  // last tile (landed: waited for at the previous tile's barrier, or in the prologue)
       const int t = kt1 - 1;
       const T* cur = lds + st_cur;
       const auto krs = tile_rsrc(s, t);
-      step(cur, 1, t, 0, cur, true, true, cur, 0, false, false, krs, lds + st_nn, d, sc);
-      if constexpr (VSC) step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, lds + st_nn, sc, d);
-      else step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, lds + st_nn, d, sc);
+      step(cur, 1, t, 0, cur, true, true, cur, 0, false, false, krs, st_nn, d, sc);
+      if constexpr (VSC) step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, st_nn, sc, d);
+      else step(cur, 0, t, 1, cur, false, true, cur, 0, false, false, krs, st_nn, d, sc);
     }
 
     const bool full = causal || (kt0 == 0 && kt1 == p.KT);
@@ -1456,8 +1517,11 @@ static hipError_t launch_flash(FlashArgs<T> a, int G, hipEvent_t ev0, hipEvent_t
   // after the kernel leaves a gap of several microseconds on each side).
   void* kernel;
   if constexpr (PIPE) {
-    static_assert(NW == 4 && NB == 2 && !VROWS && sizeof(T) == 2, "pipelined kernel shape");
-    kernel = reinterpret_cast<void*>(&flash_attn_pipe_kernel<D, DV, KTILE, (D <= 128)>);
+    static_assert(NW == 4 && !VROWS && sizeof(T) == 2, "pipelined kernel shape");
+    // three LDS stages where they fit; VGPR score accumulators where the
+    // registers allow (score widths up to 128, or one row block per wave)
+    constexpr int NST = 3 * KTILE * D * 2 <= 160 * 1024 ? 3 : 2;
+    kernel = reinterpret_cast<void*>(&flash_attn_pipe_kernel<D, DV, KTILE, (D <= 128 || NB == 1), NB, NST>);
   } else {
     kernel = reinterpret_cast<void*>(&flash_attn_kernel<T, D, DV, KTILE, NW, NB, VROWS>);
   }
@@ -1541,7 +1605,7 @@ static hipError_t latent_t(const AttnCall& c, hipStream_t s) {
     if (c.dr == 32) {
       if (c.dc == 96) return launch_flash<T, 128, 96, 64, 4, 2, false, true>(a, c.G, c.ev_start, c.ev_stop, s);
       if (c.dc == 192) return launch_flash<T, 224, 192, 64, 4, 2, false, true>(a, c.G, c.ev_start, c.ev_stop, s);
-      if (c.dc == 448) return launch_flash<T, 480, 448, 64, 4, 1, false>(a, c.G, c.ev_start, c.ev_stop, s);
+      if (c.dc == 448) return launch_flash<T, 480, 448, 64, 4, 1, false, true>(a, c.G, c.ev_start, c.ev_stop, s);
     }
     return hipErrorInvalidValue;
   }
