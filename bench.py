@@ -286,8 +286,8 @@ def main():
                                                  wl.latent_weights(g, layer=l, mode="literal").as_dict().items()})
                         for l in range(1, g.layers if args.path == "absorbed" else 1)]
         attend_profiled, append = vmla.vmla_attend_profiled, vmla.vmla_compress_append
-        # bf16 at d_c = 192 runs the software-pipelined 64-row kernel
-        lat = "flash_attn_pipe_kernel" if (g.d_c == 192 and g.dtype == "bf16") else "flash_attn_kernel"
+        # bf16 at d_c = 96, 192 and 448 runs the software-pipelined kernel
+        lat = "flash_attn_pipe_kernel" if (g.d_c in (96, 192, 448) and g.dtype == "bf16") else "flash_attn_kernel"
         kernel = f"{lat} (latent, absorbed)"
         if args.path == "clip":
             clip_ws = torch.empty(vmla.vmla_clip_workspace_bytes(layer.cfg), dtype=torch.uint8, device=dev)
