@@ -166,7 +166,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
 //
 // Staging: each 64-wide k stage of the W and X tiles is copied global -> LDS
 // by buffer_load_dwordx4 ... lds (no registers, no VALU), NST stages in
-// flight.  The loads are issued from inline asm, so the compiler sees no LDS
+// flight; a stage's loads are spread over the k sub-steps of the step before
+// it, between its MFMAs.  The loads are issued from inline asm, so the compiler sees no LDS
 // write it cannot order and does not wait for them before every LDS read; the
 // kernel waits itself (vmcnt) before the barrier that publishes a stage.  Each
 // tile's buffer resources start at its first row and end after its last valid
@@ -277,9 +278,11 @@ __global__ __launch_bounds__(NWN * NWM * 64) void gemm_dma_kernel(GemmDmaOps<T> 
     voff[i] = (uint32_t)(((long)(2 * R + (q >> 3)) * ld + 8 * (q & 7)) * 2);
   }
   const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds;
-  auto issue = [&](int st, int kt, bool live) __attribute__((always_inline)) {
+  // loads i0 <= i < i1 of this wave for stage kt into LDS stage st
+  auto issue = [&](int st, int kt, bool live, int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
+      if (i < i0 || i >= i1) continue;
       const bool isw = i < BW / NW;
       const auto r = live ? (isw ? rw : rx) : rnone;
       dma16_lds(r, voff[i] + (uint32_t)(kt * BK * 2), lds0 + (uint32_t)(st * STAGE + (wave + NW * i) * 1024));
@@ -294,18 +297,22 @@ __global__ __launch_bounds__(NWN * NWM * 64) void gemm_dma_kernel(GemmDmaOps<T> 
 
   const int KT = op.K / BK;
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s, s, s < KT);
+  for (int s = 0; s < NST - 1; ++s) issue(s, s, s < KT, 0, NLD);
   int st = 0;
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's loads of stage kt have landed; the barrier publishes every
     // wave's and frees the stage read in the previous step for the next loads
     wait_vmcnt<(NST - 2) * NLD>();
     __syncthreads();
-    issue(st == 0 ? NST - 1 : st - 1, kt + NST - 1, kt + NST - 1 < KT);
+    const int nst = st == 0 ? NST - 1 : st - 1, nkt = kt + NST - 1;
+    const bool nlive = nkt < KT;
     const char* Wst = lds + st * STAGE;
     const char* Xst = Wst + BN * BK * 2;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
+      // the next stage's loads spread over the k sub-steps, between the MFMAs
+      // (issued all at once after the barrier they delayed the first MFMAs)
+      issue(nst, nkt, nlive, ks * NLD / (BK / 16), (ks + 1) * NLD / (BK / 16));
       // row r = 32 f + l32 of a fragment: pair r / 2, chunk 2 ks + h32
       const int lp = 256 * (l32 >> 1) + 16 * ((8 * (l32 & 1) + 2 * ks + h32) ^ (l32 >> 1));
       typename MF::Frag a[FN], b[FM];
