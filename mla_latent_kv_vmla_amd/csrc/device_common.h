@@ -192,6 +192,10 @@ struct FastDiv {
 // tab[2 (p * tab_stride + pos) + {0, 1}] for pair p of the h or w axis,
 // computed once per ctx by rope_table with the same sincosf of the same
 // argument, so a lookup returns the values the direct evaluation would.
+// sin and cos of a rotary angle: one out-of-line copy, so that epilogues with
+// many rotation sites do not each inline the argument reduction of sincosf
+__device__ __attribute__((noinline)) inline void rope_sincos(float ang, float& sn, float& cs) { sincosf(ang, &sn, &cs); }
+
 struct Rope {
   int pairs_t, pairs_h;     // pairs [0, t) turn with f, [t, t+h) with row, rest with column
   int grid_w, tokens_per_frame;
@@ -221,7 +225,7 @@ struct Rope {
     } else {
       float pos = pair < pairs_t ? (float)frame
                 : (pair < pairs_t + pairs_h ? (float)gw.div(s) : (float)gw.mod(s));
-      sincosf(pos * freq[pair], &sn, &cs);
+      rope_sincos(pos * freq[pair], sn, cs);
     }
     float x = a * cs - b * sn;
     float y = a * sn + b * cs;
