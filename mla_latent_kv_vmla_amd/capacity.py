@@ -51,6 +51,7 @@ def latent_workspace_bytes(g, batch: int = 1, es: int = 2, key_tile: int = 64,
     persistent = [4, rope_table_bytes(g, g.d_rope // 2), D * g.hidden * es, nh * D * g.hidden * es, nh * dh * g.hidden * es, nh * g.d_v * g.d_c * es,
                   g.hidden * nh * g.d_v * es]
     per_call = [M * D * es, M * g.hidden * es if es == 2 else 0,  # chunk rows; fp16 copy of x (16-bit storage)
+                g.n_q * (g.d_rope // 2) * 8 if es == 2 else 0,  # the chunk tokens' rotary cos/sin (16-bit storage)
                 M * nh * max(D, g.d_v) * es,  # absorbed queries, then per-head outputs
                 M * nh * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * g.d_c * es, 2 * workgroups * ATTN_MAX_ROWS * 2 * 4,
                 # pre-pass tiles: fp16 key tiles (16-bit storage), transposed value images (fp32)

@@ -215,8 +215,8 @@ struct Rope {
     gw = FastDiv((uint32_t)grid_w_);
     tpf = FastDiv((uint32_t)tokens);
   }
-  __device__ inline void rotate2(int pair, int64_t frame, int s, float& a, float& b) const {
-    float sn, cs;
+  // cos and sin of the angle of pair `pair` for token s of frame `frame`
+  __device__ inline void angle(int pair, int64_t frame, int s, float& cs, float& sn) const {
     if (pair >= pairs_t && tab) {
       const int pos = pair < pairs_t + pairs_h ? (int)gw.div(s) : (int)gw.mod(s);
       const float2 v = reinterpret_cast<const float2*>(tab)[pair * tab_stride + pos];
@@ -227,10 +227,18 @@ struct Rope {
                 : (pair < pairs_t + pairs_h ? (float)gw.div(s) : (float)gw.mod(s));
       rope_sincos(pos * freq[pair], sn, cs);
     }
+  }
+  // (a, b) turned by the angle with cosine cs and sine sn
+  __device__ static inline void turn(float cs, float sn, float& a, float& b) {
     float x = a * cs - b * sn;
     float y = a * sn + b * cs;
     a = x;
     b = y;
+  }
+  __device__ inline void rotate2(int pair, int64_t frame, int s, float& a, float& b) const {
+    float sn, cs;
+    angle(pair, frame, s, cs, sn);
+    turn(cs, sn, a, b);
   }
 };
 

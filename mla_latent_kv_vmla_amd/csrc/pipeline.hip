@@ -48,16 +48,26 @@ template <typename T> struct EpiLatent {
   int wrel;
   FastDiv nq;     // chunk tokens per stream
   Rope rope;
+  // the chunk tokens' cos and sin per pair of pairs ([t][pair / 2], chunk_rope
+  // layout), or null: then computed here
+  const float4* ctab = nullptr;
+  int hp = 0;     // pairs of pairs per token in ctab
   // features n..n+3 of token m after the rotation of the decoupled key channels
   __device__ void values(int m, int n, const float* v, float* a) const {
     a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (n >= dc && rotate) {
       const int t = (int)nq.mod(m);
-      const int64_t frame = frame0 + (int)rope.tpf.div(t);
-      const int s = (int)rope.tpf.mod(t);
       const int pair = (n - dc) >> 1;
-      rope.rotate2(pair, frame, s, a[0], a[1]);
-      rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+      if (ctab) {
+        const float4 c = ctab[t * hp + (pair >> 1)];
+        Rope::turn(c.x, c.y, a[0], a[1]);
+        Rope::turn(c.z, c.w, a[2], a[3]);
+      } else {
+        const int64_t frame = frame0 + (int)rope.tpf.div(t);
+        const int s = (int)rope.tpf.mod(t);
+        rope.rotate2(pair, frame, s, a[0], a[1]);
+        rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+      }
     }
   }
   __device__ T* row(int, int m, int n) const {
@@ -98,16 +108,24 @@ template <typename A> struct EpiQueryAbs {
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
+  const float4* ctab = nullptr;  // as in EpiLatent
+  int hp = 0;
   __device__ void values(int m, int n, const float* v, float* a) const {
     const int j = (int)dd.mod(n);
     a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (j >= dc) {
       const int t = (int)nq.mod(m);
-      const int64_t frame = frame0 + (int)rope.tpf.div(t);
-      const int s = (int)rope.tpf.mod(t);
       const int pair = (j - dc) >> 1;
-      rope.rotate2(pair, frame, s, a[0], a[1]);
-      rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+      if (ctab) {
+        const float4 c = ctab[t * hp + (pair >> 1)];
+        Rope::turn(c.x, c.y, a[0], a[1]);
+        Rope::turn(c.z, c.w, a[2], a[3]);
+      } else {
+        const int64_t frame = frame0 + (int)rope.tpf.div(t);
+        const int s = (int)rope.tpf.mod(t);
+        rope.rotate2(pair, frame, s, a[0], a[1]);
+        rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+      }
     }
   }
   __device__ A* row(int, int m, int n) const { return qt + (long)m * N + n; }
@@ -137,15 +155,23 @@ struct EpiQueryHead {
   int64_t frame0;
   Rope rope;
   uint32_t* flag;
+  const float4* ctab = nullptr;  // as in EpiLatent
+  int hp = 0;
   __device__ void values(int m, int n, const float* v, float* a) const {
     const int t = (int)nq.mod(m), j = (int)hd.mod(n);
     a[0] = v[0], a[1] = v[1], a[2] = v[2], a[3] = v[3];
     if (j >= d_nope) {
-      const int64_t frame = frame0 + (int)rope.tpf.div(t);
-      const int s = (int)rope.tpf.mod(t);
       const int pair = (j - d_nope) >> 1;
-      rope.rotate2(pair, frame, s, a[0], a[1]);
-      rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+      if (ctab) {
+        const float4 c = ctab[t * hp + (pair >> 1)];
+        Rope::turn(c.x, c.y, a[0], a[1]);
+        Rope::turn(c.z, c.w, a[2], a[3]);
+      } else {
+        const int64_t frame = frame0 + (int)rope.tpf.div(t);
+        const int s = (int)rope.tpf.mod(t);
+        rope.rotate2(pair, frame, s, a[0], a[1]);
+        rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+      }
     }
   }
   __device__ f16* row(int, int m, int n) const {
@@ -406,12 +432,25 @@ template <typename T> using Act = typename std::conditional<sizeof(T) == 2, f16,
 
 // x (bf16) to the activation type, 8 elements per thread and step
 // (bf16x8_to_f16x8: exact in fp16's normal range, saturating and flagging
-// beyond it); n8 = elements / 8.
-__global__ __launch_bounds__(256) void convert_x(u32x4* dst, const u32x4* src, long n8, uint32_t* flag) {
+// beyond it); n8 = elements / 8.  Then the chunk's rotary table: for chunk
+// token t (frame frame0 + t / T) and pairs 2k, 2k+1, ctab[t][k] = (cos, sin,
+// cos, sin) as Rope::angle gives them, so that the GEMM epilogues turn with the
+// same values they would compute themselves (nq tokens, hp pairs of pairs).
+__global__ __launch_bounds__(256) void convert_x(u32x4* dst, const u32x4* src, long n8, uint32_t* flag, float4* ctab,
+                                                 int nq, int hp, int64_t frame0, Rope rope) {
   bool over = false;
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256)
     dst[i] = bf16x8_to_f16x8(src[i], over);
   raise_range_flag(over, flag);
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < (long)nq * hp; i += (long)gridDim.x * 256) {
+    const int t = (int)(i / hp), k = (int)(i % hp);
+    const int64_t frame = frame0 + (int)rope.tpf.div(t);
+    const int s = (int)rope.tpf.mod(t);
+    float4 c;
+    rope.angle(2 * k, frame, s, c.x, c.y);
+    rope.angle(2 * k + 1, frame, s, c.z, c.w);
+    ctab[i] = c;
+  }
 }
 
 // The chunk's cache rows (rotated at frames frame0.., into p.stage) and its
@@ -426,15 +465,23 @@ static void rows_and_queries_t(const Plan& p, const void* x, int64_t frame0, con
   using A = Act<T>;
   const int M = p.B * p.Nq;
   const void* xa = x;
+  EpiRowsAndQuery<T, Q> e{latent_epilogue<T>(p, frame0, p.stage, false), q};
   if constexpr (!std::is_same<T, A>::value) {
     const long n8 = (long)M * p.d / 8;  // hidden is a multiple of 8 (config check)
-    convert_x<<<grid_for(n8), 256, 0, s>>>(static_cast<u32x4*>(p.xa), static_cast<const u32x4*>(x), n8, p.flags);
+    // the rotary table when each 4-feature group holds two whole pairs
+    const bool tab = p.dc % 4 == 0 && p.dr % 4 == 0 && p.d_nope % 4 == 0;
+    const int hp = tab ? p.dr / 4 : 0;
+    convert_x<<<grid_for(n8), 256, 0, s>>>(static_cast<u32x4*>(p.xa), static_cast<const u32x4*>(x), n8, p.flags,
+                                           static_cast<float4*>(p.ctab), p.Nq, hp, frame0, make_rope(p));
     xa = p.xa;
+    if (tab) {
+      e.lat.ctab = e.q.ctab = static_cast<const float4*>(p.ctab);
+      e.lat.hp = e.q.hp = hp;
+    }
   }
   GemmOps<A> op = ops<A>(p.wlat, p.d, 0, xa, p.d, 0, p.D + nq, M, p.d);
   op.w2 = static_cast<const A*>(wq);
   op.n_split = p.D;
-  EpiRowsAndQuery<T, Q> e{latent_epilogue<T>(p, frame0, p.stage, false), q};
   gemm<A, false>(op, 1, e, s);
 }
 

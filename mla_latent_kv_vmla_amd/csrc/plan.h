@@ -54,6 +54,7 @@ struct Plan {
   // per-call workspace
   void *stage;   // [B][Nq][D]            chunk latents (rotated), storage type
   void *xa;      // [B][Nq][d]            x in the activation type (bf16 storage; fp32 reads x itself)
+  void *ctab;    // [Nq][dr/2][2]         cos and sin of the chunk tokens' rotary angles (bf16 storage)
   void *qt;      // [B][Nq][nh][D]        absorbed query [W_UK^T q_nope | q_rope] * qscale
   void *olat;    // [B][Nq][nh][dc]       attention output in latent space
   void *o;       // [B][Nq][nh*dv]        per-head outputs after W_UV (same bytes as qt)
@@ -76,7 +77,7 @@ inline int64_t cached_frames(const Plan& p, int64_t n) {
 // follows it there, or fills a clip workspace of its own.
 struct WorkspaceLayout {
   size_t flags, rope_tab, wlat, wqa, wuq, wuv, wo, persistent;        // from the workspace start
-  size_t stage, xa, qt, olat, o, part_o, part_ml, vtiles, assembled, per_call;  // from the per-call start
+  size_t stage, xa, ctab, qt, olat, o, part_o, part_ml, vtiles, assembled, per_call;  // from the per-call start
   size_t prep;  // run_prepare's scratch: the first prep_bytes of the per-call part (per_call >= it)
   size_t total;  // persistent + per_call
 };

@@ -181,6 +181,7 @@ WorkspaceLayout workspace_layout(const Plan& p) {
   off = 0;
   L.stage = take(M * p.D * es);
   L.xa = take(p.dtype == DType::F32 ? 0 : M * p.d * as);
+  L.ctab = take(p.dtype == DType::F32 ? 0 : (size_t)p.Nq * (p.dr / 2) * 2 * sizeof(float));
   // the per-head outputs reuse the absorbed queries' bytes: the queries are dead
   // once the attention kernel has run, before W_UV writes them
   L.qt = take(M * p.nh * (size_t)(p.D > p.dv ? p.D : p.dv) * as);
@@ -331,6 +332,7 @@ static void set_per_call(Plan& p, const vmla::WorkspaceLayout& L, void* base) {
   char* ws = static_cast<char*>(base);
   p.stage = ws + L.stage;
   p.xa = ws + L.xa;
+  p.ctab = ws + L.ctab;
   p.qt = ws + L.qt;
   p.olat = ws + L.olat;
   p.o = ws + L.o;
