@@ -138,7 +138,8 @@ VMLA_API size_t vmla_cache_bytes(const vmla_config* cfg);
  * written by vmla_prepare (the range flag, the cosine and sine of the 3D-RoPE
  * row and column angles -- d_rope/2 x max(grid_h, grid_w) pairs of fp32 --
  * and the weights in the activation type, below) and the per-call buffers of vmla_attend (chunk latents,
- * absorbed queries, latent outputs, per-head outputs, partial softmax states,
+ * the activation-type copy of x and the cosine and sine of the chunk tokens' rotary angles (16-bit
+ * storage), absorbed queries, latent outputs, per-head outputs, partial softmax states,
  * key tiles; vmla_prepare also uses them as scratch).  Returns 0 for an
  * invalid config.
  *
