@@ -40,8 +40,8 @@ struct EpiDenseQ {
     const int64_t frame = frame0 + (int)rope.tpf.div(t);
     const int s = (int)rope.tpf.mod(t);
     float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-    rope.rotate2(j >> 1, frame, s, a0, a1);
-    rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
+    rope.template rotate2<true>(j >> 1, frame, s, a0, a1);
+    rope.template rotate2<true>((j >> 1) + 1, frame, s, a2, a3);
     store4(q + (((long)b * nh + h) * Nq + t) * dh + j, a0 * qscale, a1 * qscale, a2 * qscale, a3 * qscale, flag);
   }
 };
@@ -68,8 +68,8 @@ struct EpiDenseKV {
     if (n < nh * dh) {
       const int h = (int)hd.div(n), j = n - h * dh;
       float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
-      rope.rotate2(j >> 1, frame, s, a0, a1);
-      rope.rotate2((j >> 1) + 1, frame, s, a2, a3);
+      rope.template rotate2<true>(j >> 1, frame, s, a0, a1);
+      rope.template rotate2<true>((j >> 1) + 1, frame, s, a2, a3);
       store4(k + (((long)b * nh + h) * P + row) * dh + j, a0, a1, a2, a3, flag);
     } else {
       const int n2 = n - nh * dh, h = (int)vd.div(n2), f = n2 - h * dv;

@@ -215,7 +215,10 @@ struct Rope {
     gw = FastDiv((uint32_t)grid_w_);
     tpf = FastDiv((uint32_t)tokens);
   }
-  // cos and sin of the angle of pair `pair` for token s of frame `frame`
+  // cos and sin of the angle of pair `pair` for token s of frame `frame`;
+  // OUTLINE: sincosf through the one out-of-line copy (for code with many
+  // rotation sites, such as unrolled GEMM epilogues)
+  template <bool OUTLINE = false>
   __device__ inline void angle(int pair, int64_t frame, int s, float& cs, float& sn) const {
     if (pair >= pairs_t && tab) {
       const int pos = pair < pairs_t + pairs_h ? (int)gw.div(s) : (int)gw.mod(s);
@@ -225,7 +228,8 @@ struct Rope {
     } else {
       float pos = pair < pairs_t ? (float)frame
                 : (pair < pairs_t + pairs_h ? (float)gw.div(s) : (float)gw.mod(s));
-      rope_sincos(pos * freq[pair], sn, cs);
+      if constexpr (OUTLINE) rope_sincos(pos * freq[pair], sn, cs);
+      else sincosf(pos * freq[pair], &sn, &cs);
     }
   }
   // (a, b) turned by the angle with cosine cs and sine sn
@@ -235,9 +239,10 @@ struct Rope {
     a = x;
     b = y;
   }
+  template <bool OUTLINE = false>
   __device__ inline void rotate2(int pair, int64_t frame, int s, float& a, float& b) const {
     float sn, cs;
-    angle(pair, frame, s, cs, sn);
+    angle<OUTLINE>(pair, frame, s, cs, sn);
     turn(cs, sn, a, b);
   }
 };

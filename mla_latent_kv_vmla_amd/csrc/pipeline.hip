@@ -65,8 +65,8 @@ template <typename T> struct EpiLatent {
       } else {
         const int64_t frame = frame0 + (int)rope.tpf.div(t);
         const int s = (int)rope.tpf.mod(t);
-        rope.rotate2(pair, frame, s, a[0], a[1]);
-        rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+        rope.template rotate2<true>(pair, frame, s, a[0], a[1]);
+        rope.template rotate2<true>(pair + 1, frame, s, a[2], a[3]);
       }
     }
   }
@@ -123,8 +123,8 @@ template <typename A> struct EpiQueryAbs {
       } else {
         const int64_t frame = frame0 + (int)rope.tpf.div(t);
         const int s = (int)rope.tpf.mod(t);
-        rope.rotate2(pair, frame, s, a[0], a[1]);
-        rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+        rope.template rotate2<true>(pair, frame, s, a[0], a[1]);
+        rope.template rotate2<true>(pair + 1, frame, s, a[2], a[3]);
       }
     }
   }
@@ -169,8 +169,8 @@ struct EpiQueryHead {
       } else {
         const int64_t frame = frame0 + (int)rope.tpf.div(t);
         const int s = (int)rope.tpf.mod(t);
-        rope.rotate2(pair, frame, s, a[0], a[1]);
-        rope.rotate2(pair + 1, frame, s, a[2], a[3]);
+        rope.template rotate2<true>(pair, frame, s, a[0], a[1]);
+        rope.template rotate2<true>(pair + 1, frame, s, a[2], a[3]);
       }
     }
   }
