@@ -120,10 +120,7 @@ template <typename T> struct FlashArgs {
 };
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
-#ifndef VMLA_FRAG_AHEAD
-#define VMLA_FRAG_AHEAD 4
-#endif
-constexpr int kAhead = VMLA_FRAG_AHEAD;  // LDS fragment reads in flight ahead of their MFMA
+constexpr int kAhead = 4;  // LDS fragment reads in flight ahead of their MFMA
 
 // Maximum of two scores in the IEEE 754-2019 sense (a NaN operand gives NaN).
 // fmaxf must first quiet a signalling NaN, so for operands the compiler cannot
@@ -916,10 +913,7 @@ void flash_attn_pipe_kernel(FlashArgs<bf16> p) {
   constexpr bool ONES = VSC && NB == 2;
   constexpr int NFV = NFB + (ONES ? 1 : 0);  // value accumulator blocks
   constexpr int NV = 2 * NFV;    // value MFMAs per block and row block
-#ifndef VMLA_KA1
-#define VMLA_KA1 4
-#endif
-  constexpr int KA = NB == 2 ? 2 : VMLA_KA1;  // fragment reads in flight ahead of their first MFMA
+  constexpr int KA = NB == 2 ? 2 : 4;  // fragment reads in flight ahead of their first MFMA
   constexpr int NI_W = KI / NW;
   constexpr int DS = NST == 3 ? 4 : (NI_W + 1) / 2;  // slots carrying a tile's loads, two per slot
   static_assert(CH % 4 == 0 && KI % NW == 0 && KTILE == 16 * NW, "tile layout: one 16-row region per wave");

@@ -23,13 +23,8 @@ template <typename T> struct GemmOps {
   int N, M, K, n_split;
 };
 
-#ifndef VMLA_GEMM_BK
-#define VMLA_GEMM_BK 64
-#endif
-#ifndef VMLA_GEMM_BK_SMALL
-#define VMLA_GEMM_BK_SMALL 128
-#endif
-constexpr int GEMM_BK = VMLA_GEMM_BK;  // k-values per pipeline stage (16-bit storage)
+constexpr int GEMM_BK = 64;         // k-values per pipeline stage (16-bit storage)
+constexpr int GEMM_BK_SMALL = 128;  // the same for 64 x 64 tiles
 
 template <typename T, int BN, int BM, bool W_KN, class Epi>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
@@ -37,7 +32,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmOps<T> op, Epi epi) {
   // k-values per stage: deeper stages halve the global-load round trips of
   // these latency-bound GEMMs; 64x64 tiles afford 128 (~70 KB of LDS), larger
   // tiles 64 (two workgroups per CU); fp32 tiles keep 32 (LDS)
-  constexpr int BK = sizeof(T) != 2 ? 32 : (BN == 64 && BM == 64 ? VMLA_GEMM_BK_SMALL : GEMM_BK);
+  constexpr int BK = sizeof(T) != 2 ? 32 : (BN == 64 && BM == 64 ? GEMM_BK_SMALL : GEMM_BK);
   constexpr int KPL = MF::KPL;
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int STRIDE = BK + VEC;          // LDS row: BK k-values + 16 B pad
